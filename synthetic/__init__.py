@@ -1,0 +1,11 @@
+"""Seeded synthetic inputs for the activation-sparse FFN step.
+
+This package produces weights, biases, tokens and per-layer thresholds with the
+structure the PowerInfer and KAIROX pages measure (power-law activation, temporal
+locality of successive tokens, co-activated groups of 32 neurons).  It holds none
+of the step's own arithmetic: no predictor, no gate, no sparse product, no TAM.
+Both the HIP path and the fp64 oracle consume what it produces.
+"""
+from .configs import CONFIGS, FFNConfig, scaled  # noqa: F401
+from .gen import (Layer, make_layer, make_tokens, seed_for, storage_numpy,  # noqa: F401
+                  threshold_for, zipf_profile, quantize_q4)
