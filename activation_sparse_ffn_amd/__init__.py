@@ -1,0 +1,11 @@
+"""MI355X-native predictor-gated activation-sparse FFN step (libsfx).
+
+The compute lives in libsfx.so (HIP kernels for gfx950 behind the C ABI in
+include/sfx.h); this package is its ctypes binding plus buffer orchestration.
+Build with `python -m activation_sparse_ffn_amd.build`.
+"""
+from ._abi import (SFX_BF16, SFX_F16, SFX_F32, SFX_MAX_B, SFX_MAX_GROUPS, SFX_Q4G32,  # noqa: F401
+                   SFX_REGLU, SFX_RELU, SfxError, abi_version, load, sfx_compact, sfx_compact_ws,
+                   sfx_predict, sfx_predict_ws, sfx_sparse_down, sfx_sparse_down_ws, sfx_sparse_up,
+                   sfx_tam_update, sfx_tam_ws, status_str, workspace)
+from .step import StepBuffers, TamState, run_layer  # noqa: F401

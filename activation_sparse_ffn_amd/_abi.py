@@ -1,0 +1,210 @@
+"""ctypes binding of libsfx (include/sfx.h).
+
+Argument marshalling only: each function takes torch tensors, checks dtype /
+contiguity / device, passes raw pointers and the current HIP stream to the C entry
+point of the same name, and raises SfxError on a negative status.  Every step of
+the computation runs in the library's kernels; there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsfx.so")
+
+SFX_F32, SFX_F16, SFX_BF16, SFX_Q4G32 = 0, 1, 2, 3
+SFX_RELU, SFX_REGLU = 0, 1
+SFX_MAX_B = 64
+SFX_MAX_GROUPS = 1024
+ACTS = {"relu": SFX_RELU, "reglu": SFX_REGLU}
+WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
+
+EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
+           "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
+           "sfx_tam_update")
+
+
+class SfxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsfx (once).  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libsfx is not built ({path} missing): run "
+                           "`python -m activation_sparse_ffn_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.sfx_status_str.restype = ctypes.c_char_p
+    lib.sfx_status_str.argtypes = [I]
+    lib.sfx_abi_version.restype = I
+    lib.sfx_abi_version.argtypes = []
+    lib.sfx_predict_ws.restype = Z
+    lib.sfx_predict_ws.argtypes = [I, I, I, I, I]
+    lib.sfx_predict.restype = I
+    lib.sfx_predict.argtypes = [P, I, I, I, I, I, P, P, P, P, P, Z]
+    lib.sfx_compact_ws.restype = Z
+    lib.sfx_compact_ws.argtypes = [I, I]
+    lib.sfx_compact.restype = I
+    lib.sfx_compact.argtypes = [P, I, I, P, F, P, P, P, I, P, P, Z]
+    lib.sfx_sparse_up.restype = I
+    lib.sfx_sparse_up.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P]
+    lib.sfx_sparse_down_ws.restype = Z
+    lib.sfx_sparse_down_ws.argtypes = [I, I, I, I]
+    lib.sfx_sparse_down.restype = I
+    lib.sfx_sparse_down.argtypes = [P, I, I, I, I, P, P, P, P, I, P, P, P, Z]
+    lib.sfx_tam_ws.restype = Z
+    lib.sfx_tam_ws.argtypes = [I, I]
+    lib.sfx_tam_update.restype = I
+    lib.sfx_tam_update.argtypes = [P, I, I, P, F, F, I, P, P, P, P, P, P, P, Z]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().sfx_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load().sfx_abi_version()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise SfxError(status, where)
+
+
+def _wdt_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.uint8:
+        return SFX_Q4G32
+    if t.dtype not in WDT:
+        raise TypeError(f"unsupported weight dtype {t.dtype}")
+    return WDT[t.dtype]
+
+
+def _need(t, dtype, where):
+    if t.dtype != dtype:
+        raise TypeError(f"{where}: expected {dtype}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------------- workspaces
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """Zero-filled device workspace of at least `nbytes` (the library keeps its
+    control words at zero between calls)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def sfx_predict_ws(wdt: int, B: int, d: int, h: int, f: int) -> int:
+    return load().sfx_predict_ws(wdt, B, d, h, f)
+
+
+def sfx_compact_ws(B: int, f: int) -> int:
+    return load().sfx_compact_ws(B, f)
+
+
+def sfx_sparse_down_ws(wdt: int, B: int, d: int, kmax: int) -> int:
+    return load().sfx_sparse_down_ws(wdt, B, d, kmax)
+
+
+def sfx_tam_ws(G: int, K: int) -> int:
+    return load().sfx_tam_ws(G, K)
+
+
+# ------------------------------------------------------------------------- entry points
+
+def sfx_predict(x, W1, W2, scores, ws, stream=None):
+    """scores[B][f] = W2 relu(W1 x_b).  x [B][d], W1 [h][d], W2 [f][h] (same dtype)."""
+    B, d = x.shape
+    h, f = W1.shape[0], W2.shape[0]
+    if W1.shape[1] != d or W2.shape[1] != h or tuple(scores.shape) != (B, f):
+        raise ValueError("sfx_predict: shape mismatch")
+    if W1.dtype != x.dtype or W2.dtype != x.dtype:
+        raise TypeError("sfx_predict: x, W1, W2 must share a dtype")
+    _need(scores, torch.float32, "scores")
+    ptrs = (_ptr(x), _ptr(W1), _ptr(W2), _ptr(scores), _ptr(ws))
+    st = load().sfx_predict(_stream(stream), _wdt_of(x), B, d, h, f, *ptrs, ws.numel() if ws is not None else 0)
+    _check(st, "sfx_predict")
+
+
+def sfx_compact(scores, threshold, union_bits, idx, count, ws, tok_bits=None, stream=None):
+    """Union of {score >= threshold} over tokens -> ascending idx, device count."""
+    B, f = scores.shape
+    _need(scores, torch.float32, "scores")
+    for t, n in ((union_bits, "union_bits"), (count, "count"), (idx, "idx")):
+        if t.dtype not in (torch.int32, torch.uint32):
+            raise TypeError(f"{n} must be int32/uint32")
+    p = (_ptr(scores), _ptr(tok_bits), _ptr(union_bits), _ptr(idx), _ptr(count), _ptr(ws))
+    st = load().sfx_compact(_stream(stream), B, f, p[0], float(threshold), p[1], p[2], p[3], idx.numel(), p[4],
+                            p[5], ws.numel() if ws is not None else 0)
+    _check(st, "sfx_compact")
+
+
+def sfx_sparse_up(x, Wa, ba, idx, count, hact, act="relu", Wa_scales=None, Wl=None, Wl_scales=None,
+                  stream=None):
+    """hact[kmax][B] for the listed neurons (rows < count written)."""
+    B, d = x.shape
+    f = Wa.shape[0]
+    wdt = _wdt_of(Wa)
+    kmax = idx.numel()
+    if hact.numel() < kmax * B:
+        raise ValueError("hact too small")
+    _need(hact, torch.float32, "hact")
+    if ba is not None:
+        _need(ba, torch.float32, "ba")
+    p = (_ptr(x), _ptr(Wa), _ptr(Wa_scales), _ptr(ba), _ptr(Wl), _ptr(Wl_scales), _ptr(idx), _ptr(count))
+    st = load().sfx_sparse_up(_stream(stream), wdt, ACTS[act], B, d, f, *p, kmax, _ptr(hact))
+    _check(st, "sfx_sparse_up")
+
+
+def sfx_sparse_down(Wd, idx, count, hact, y, ws, Wd_scales=None, stream=None):
+    """y[B][d] = sum_j hact[j][b] Wd[idx_j] (overwritten)."""
+    B, d = y.shape
+    f = Wd.shape[0]
+    wdt = _wdt_of(Wd)
+    kmax = idx.numel()
+    _need(y, torch.float32, "y")
+    _need(hact, torch.float32, "hact")
+    p = (_ptr(Wd), _ptr(Wd_scales), _ptr(idx), _ptr(count))
+    q = (_ptr(hact), _ptr(y), _ptr(ws))
+    st = load().sfx_sparse_down(_stream(stream), wdt, B, d, f, *p, kmax, *q, ws.numel() if ws is not None else 0)
+    _check(st, "sfx_sparse_down")
+
+
+def sfx_tam_update(union_bits, lam, eps, K, score, hot_bits, entered_bits, left_bits, topk, topk_count,
+                   ws=None, stream=None):
+    """One TAM step for L layers.  union_bits [L][G], score [L][G] fp32, bit sets [L][ceil(G/32)]."""
+    L, G = union_bits.shape
+    _need(score, torch.float32, "score")
+    p = (_ptr(score), _ptr(hot_bits), _ptr(entered_bits), _ptr(left_bits), _ptr(topk) if K > 0 else None,
+         _ptr(topk_count), _ptr(ws))
+    st = load().sfx_tam_update(_stream(stream), L, G, _ptr(union_bits), float(lam), float(eps), int(K), *p,
+                               ws.numel() if ws is not None else 0)
+    _check(st, "sfx_tam_update")

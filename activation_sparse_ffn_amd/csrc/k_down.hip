@@ -1,0 +1,269 @@
+// Gathered neuron-major down rows (PowerInfer page, Method: hybrid-execution
+// pseudocode, y is the sum of the active neurons' contributions; neuron-aware
+// operators of §5.4, each block owns a disjoint set of neurons).
+//
+//   y[b][:] = sum_{j < count} hact[j][b] * Wd[idx_j][:]
+//
+// Grid = S neuron slices x T column tiles.  Workgroup (s, t) reads the tile-t
+// segment (64 lanes x LW bytes, contiguous) of every row in slice s, accumulates
+// B x CPL fp32 sums per lane, adds its four waves in LDS in a fixed order and
+// writes one partial tile.  The last workgroup of a tile to finish (ticket in the
+// workspace) adds the S partials in slice order and writes y: no atomics on data,
+// and y is the same bit for bit on every run.
+#include "sfx_common.hpp"
+#include "sfx_launch.hpp"
+
+namespace sfx {
+namespace {
+
+constexpr int kRowsInFlight = 8;   // rows per wave whose segments are loaded together
+constexpr int kTargetBlocks = 256;
+constexpr int kMaxSlices = 64;
+
+// Decoded columns of one lane's segment.
+template <class T, int LW>
+struct Seg {
+  static constexpr int cpl = LW / T::bytes;
+  __device__ static void decode(const Raw<LW>& r, const uint16_t*, int, float* o) { unpack<T, LW / 4>(r.w, o); }
+};
+struct TQ4 { static constexpr int bytes = 0; };
+template <int LW>
+struct Seg<TQ4, LW> {
+  static constexpr int cpl = LW * 2;
+  // `scale` already holds the group's fp16 scale as float bits in o[-]: decode codes only.
+  __device__ static void decode(const Raw<LW>& r, const uint16_t*, int, float* o) {
+#pragma unroll
+    for (int q = 0; q < LW / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q * 8 + e] = (float)((int32_t)(r.w[q] << (28 - 4 * e)) >> 28);
+  }
+};
+
+template <class T>
+struct RowGeom {
+  __device__ static size_t row_bytes(int d) { return (size_t)d * T::bytes; }
+  __device__ static size_t col_byte(int col) { return (size_t)col * T::bytes; }
+};
+template <>
+struct RowGeom<TQ4> {
+  __device__ static size_t row_bytes(int d) { return (size_t)d >> 1; }
+  __device__ static size_t col_byte(int col) { return (size_t)col >> 1; }
+};
+
+template <class T, int NB, int LW>
+__global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd, const uint16_t* __restrict__ Wd_s,
+                                                 const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+                                                 int kmax, const float* __restrict__ hact, int B, int d, int f,
+                                                 float* __restrict__ y, float* __restrict__ part,
+                                                 uint32_t* __restrict__ tickets, int S, int ntiles) {
+  constexpr int CPL = Seg<T, LW>::cpl;
+  constexpr int TW = kWave * CPL;
+  constexpr bool Q4 = T::bytes == 0;
+  __shared__ float s_red[kWavesPerBlock - 1][NB][TW];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x % ntiles;
+  const int slice = blockIdx.x / ntiles;
+  const int k = min(*count, kmax);
+  const int j0 = (int)(((long long)k * slice) / S);
+  const int j1 = (int)(((long long)k * (slice + 1)) / S);
+  const int col0 = tile * TW + lane * CPL;
+  const bool valid = col0 < d;
+  const size_t rb = RowGeom<T>::row_bytes(d);
+  const size_t cb = RowGeom<T>::col_byte(col0);
+  const int ngroup = d >> 5;
+
+  float acc[NB][CPL];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[b][c] = 0.f;
+
+  for (int jb = j0 + wave; jb < j1; jb += kWavesPerBlock * kRowsInFlight) {
+    Raw<LW> w[kRowsInFlight];
+    float sc[kRowsInFlight];
+    int rows[kRowsInFlight];
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      int i = (j < j1) ? idx[j] : -1;
+      if ((unsigned)i >= (unsigned)f) i = -1;
+      rows[u] = i;
+      if (i >= 0 && valid) {
+        w[u] = load_raw<LW>(Wd + (size_t)i * rb + cb);
+        if (Q4) sc[u] = (float)__builtin_bit_cast(_Float16, Wd_s[(size_t)i * ngroup + (col0 >> 5)]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < LW / 4; ++q) w[u].w[q] = 0u;
+        sc[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      if (rows[u] >= 0) {
+        float wf[CPL];
+        Seg<T, LW>::decode(w[u], nullptr, 0, wf);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            float hv = hact[(size_t)j * B + b];
+            if (Q4) hv *= sc[u];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[b][c] = fmaf(hv, wf[c], acc[b][c]);
+          }
+        }
+      }
+    }
+  }
+
+  // Combine the four waves in LDS: wave 0 + wave 1 + wave 2 + wave 3, in that order.
+  if (wave > 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) s_red[wave - 1][b][lane * CPL + c] = acc[b][c];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < kWavesPerBlock - 1; ++v)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[b][c] += s_red[v][b][lane * CPL + c];
+    if (valid) {
+      if (S == 1) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < B)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              if (col0 + c < d) y[(size_t)b * d + col0 + c] = acc[b][c];
+      } else {
+        float* p = part + ((size_t)(slice * ntiles + tile) * B) * TW;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < B)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) p[(size_t)b * TW + lane * CPL + c] = acc[b][c];
+      }
+    }
+  }
+  if (S == 1) return;
+
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(tickets + tile, 1u) == (uint32_t)(S - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // Last workgroup of this tile: y = sum of the S partials in slice order.
+  for (int e = threadIdx.x; e < B * TW; e += kBlock) {
+    const int b = e / TW;
+    const int cc = e - b * TW;
+    const int col = tile * TW + cc;
+    if (col >= d) continue;
+    float sum = 0.f;
+    for (int s2 = 0; s2 < S; ++s2)
+      sum += part[((size_t)(s2 * ntiles + tile) * B + b) * TW + cc];
+    y[(size_t)b * d + col] = sum;
+  }
+  if (threadIdx.x == 0) tickets[tile] = 0u;
+}
+
+// Load width (bytes per lane per row) for a storage type and token class: keep
+// NB x CPL accumulators per lane at <= 64 (<= 128 for int4 at B = 16).
+template <class T>
+constexpr int lw_for(int nb) {
+  return T::bytes == 0 ? (nb <= 2 ? 16 : nb <= 4 ? 8 : 4)
+                       : (nb * (16 / T::bytes) <= 64 ? 16 : nb * (8 / T::bytes) <= 64 ? 8 : 4);
+}
+
+struct Plan { int lw, cpl, tw, ntiles, S; };
+
+Plan plan_for(int wdt, int B, int d, int kmax) {
+  const int nb = nb_class(B);
+  int lw = 16, cpl = 4;
+  switch (wdt) {
+    case DT_F32: lw = lw_for<TF32>(nb); cpl = lw / 4; break;
+    case DT_F16: lw = lw_for<TF16>(nb); cpl = lw / 2; break;
+    case DT_BF16: lw = lw_for<TBF16>(nb); cpl = lw / 2; break;
+    default: lw = lw_for<TQ4>(nb); cpl = lw * 2; break;
+  }
+  Plan p;
+  p.lw = lw;
+  p.cpl = cpl;
+  p.tw = kWave * cpl;
+  p.ntiles = (d + p.tw - 1) / p.tw;
+  int S = kTargetBlocks / p.ntiles;
+  if (S > kMaxSlices) S = kMaxSlices;
+  const int rows_cap = (kmax + kWavesPerBlock - 1) / kWavesPerBlock;  // >= 4 rows per slice
+  if (S > rows_cap) S = rows_cap;
+  if (S < 1) S = 1;
+  p.S = S;
+  return p;
+}
+
+template <class T, int NB>
+hipError_t run(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd, const void* Wd_s,
+               const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y, void* ws) {
+  constexpr int LW = lw_for<T>(NB);
+  uint32_t* tickets = (uint32_t*)ws;
+  const size_t tick_bytes = ((size_t)p.ntiles * 4 + 255) & ~(size_t)255;
+  float* part = (float*)((uint8_t*)ws + tick_bytes);
+  k_down<T, NB, LW><<<dim3(p.S * p.ntiles), dim3(kBlock), 0, s>>>(
+      (const uint8_t*)Wd, (const uint16_t*)Wd_s, idx, count, kmax, hact, B, d, f, y, part, tickets, p.S,
+      p.ntiles);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dispatch(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd, const void* Wd_s,
+                    const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y, void* ws) {
+  switch (nb_class(B)) {
+    case 1: return run<T, 1>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case 2: return run<T, 2>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case 4: return run<T, 4>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case 8: return run<T, 8>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case 16: return run<T, 16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case 32: return run<T, 32>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    default: return run<T, 64>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+  }
+}
+
+}  // namespace
+
+bool down_supported(int wdt, int B) { return wdt != DT_Q4 || B <= 16; }
+
+size_t down_ws_bytes(int wdt, int B, int d, int kmax) {
+  const Plan p = plan_for(wdt, B, d, kmax);
+  const size_t tick_bytes = ((size_t)p.ntiles * 4 + 255) & ~(size_t)255;
+  const size_t part = p.S > 1 ? (size_t)p.S * p.ntiles * B * p.tw * sizeof(float) : 0;
+  return tick_bytes + ((part + 255) & ~(size_t)255);
+}
+
+hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* Wd, const void* Wd_s,
+                       const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y,
+                       void* ws) {
+  const Plan p = plan_for(wdt, B, d, kmax);
+  switch (wdt) {
+    case DT_F32: return dispatch<TF32>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case DT_F16: return dispatch<TF16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case DT_BF16: return dispatch<TBF16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+    case DT_Q4:
+      switch (nb_class(B)) {
+        case 1: return run<TQ4, 1>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+        case 2: return run<TQ4, 2>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+        case 4: return run<TQ4, 4>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+        case 8: return run<TQ4, 8>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+        default: return run<TQ4, 16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
+      }
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sfx

@@ -1,0 +1,185 @@
+// Per-layer MLP predictor: scores_b = W2 max(W1 x_b, 0)
+// (PowerInfer page, Method, per-layer predictor of §5.1: one hidden layer with ReLU,
+// one score per FFN neuron).
+//
+// At small batch both layers are HBM streams of the weights: every weight byte is
+// read once and feeds B multiply-adds.  Layer 1 gives one wave per hidden row;
+// layer 2 gives each wave R rows of W2, so a lane keeps R 16-byte loads in flight
+// per chunk.  The hidden vector is kept in fp32 (workspace), never rounded to the
+// weight type.  From B = 16 on, layer 2 is a dense contraction and runs on the
+// matrix cores (k_predict_mfma.hip).
+#include "sfx_common.hpp"
+#include "sfx_launch.hpp"
+
+namespace sfx {
+
+hipError_t launch_pred_scores_mfma(hipStream_t s, int wdt, int B, int h, int f, const void* W2,
+                                   const float* hid, float* scores);
+bool pred_mfma_eligible(int wdt, int B, int h, int f);
+
+namespace {
+
+constexpr int kU = 8;  // 16-byte chunks per lane issued together
+
+// hidden[b][row] = max(W1[row] . x_b, 0); one wave per row.
+template <class T, int NB>
+__global__ __launch_bounds__(kBlock) void k_pred_hidden(const uint8_t* __restrict__ x,
+                                                        const uint8_t* __restrict__ W1,
+                                                        float* __restrict__ hid, int B, int d, int h) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= h) return;
+  const int nchunk = d / T::vec;
+  const size_t row_bytes = (size_t)d * T::bytes;
+  const uint8_t* wrow = W1 + (size_t)row * row_bytes;
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+
+  for (int c0 = 0; c0 < nchunk; c0 += kU * kWave) {
+    Raw<16> w[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < nchunk) w[u] = load_raw<16>(wrow + (size_t)c * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < nchunk) {
+        float wf[T::vec];
+        unpack<T, 4>(w[u].w, wf);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            Raw<16> xv = load_raw<16>(x + (size_t)b * row_bytes + (size_t)c * 16);
+            float xf[T::vec];
+            unpack<T, 4>(xv.w, xf);
+#pragma unroll
+            for (int e = 0; e < T::vec; ++e) acc[b] = fmaf(wf[e], xf[e], acc[b]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = wave_sum(acc[b]);
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < B) hid[(size_t)b * h + row] = fmaxf(acc[b], 0.f);
+  }
+}
+
+// scores[b][i] = W2[i] . hidden_b; each wave owns R consecutive rows.
+template <class T, int NB, int R>
+__global__ __launch_bounds__(kBlock) void k_pred_scores(const uint8_t* __restrict__ W2,
+                                                        const float* __restrict__ hid,
+                                                        float* __restrict__ scores, int B, int h, int f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row0 = (blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)) * R;
+  if (row0 >= f) return;
+  const int nchunk = h / T::vec;
+  const size_t row_bytes = (size_t)h * T::bytes;
+  float acc[R][NB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  for (int c = lane; c < nchunk; c += kWave) {
+    Raw<16> w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (row0 + r < f) w[r] = load_raw<16>(W2 + (size_t)(row0 + r) * row_bytes + (size_t)c * 16);
+    float wf[R][T::vec];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (row0 + r < f) unpack<T, 4>(w[r].w, wf[r]);
+      else {
+#pragma unroll
+        for (int e = 0; e < T::vec; ++e) wf[r][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < B) {
+        const float* hb = hid + (size_t)b * h + (size_t)c * T::vec;
+        float hv[T::vec];
+#pragma unroll
+        for (int e = 0; e < T::vec; e += 4) {
+          Raw<16> q = load_raw<16>(hb + e);
+          hv[e] = __uint_as_float(q.w[0]);
+          hv[e + 1] = __uint_as_float(q.w[1]);
+          hv[e + 2] = __uint_as_float(q.w[2]);
+          hv[e + 3] = __uint_as_float(q.w[3]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < T::vec; ++e) acc[r][b] = fmaf(wf[r][e], hv[e], acc[r][b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < B && row0 + r < f) scores[(size_t)b * f + row0 + r] = acc[r][b];
+  }
+}
+
+template <class T, int NB>
+hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
+               const void* W2, float* scores, float* hid, bool mfma, int wdt) {
+  dim3 blk(kBlock);
+  k_pred_hidden<T, NB><<<dim3((h + kWavesPerBlock - 1) / kWavesPerBlock), blk, 0, s>>>(
+      (const uint8_t*)x, (const uint8_t*)W1, hid, B, d, h);
+  if (mfma) return launch_pred_scores_mfma(s, wdt, B, h, f, W2, hid, scores);
+  constexpr int R = NB == 1 ? 4 : NB == 2 ? 2 : 1;
+  const int rows_per_block = kWavesPerBlock * R;
+  k_pred_scores<T, NB, R><<<dim3((f + rows_per_block - 1) / rows_per_block), blk, 0, s>>>(
+      (const uint8_t*)W2, hid, scores, B, h, f);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dispatch_nb(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
+                       const void* W2, float* scores, float* hid, bool mfma, int wdt) {
+  switch (nb_class(B)) {
+    case 1: return run<T, 1>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 2: return run<T, 2>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 4: return run<T, 4>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 8: return run<T, 8>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 16: return run<T, 16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 32: return run<T, 32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    default: return run<T, 64>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+  }
+}
+
+}  // namespace
+
+size_t predict_ws_bytes(int wdt, int B, int d, int h, int f) {
+  (void)wdt; (void)d; (void)f;
+  const size_t hid = (size_t)B * h * sizeof(float);
+  return (hid + 255) & ~(size_t)255;
+}
+
+hipError_t launch_predict(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x,
+                          const void* W1, const void* W2, float* scores, void* ws) {
+  float* hid = (float*)ws;
+  const bool mfma = pred_mfma_eligible(wdt, B, h, f);
+  switch (wdt) {
+    case DT_F32: return dispatch_nb<TF32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case DT_F16: return dispatch_nb<TF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case DT_BF16: return dispatch_nb<TBF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sfx

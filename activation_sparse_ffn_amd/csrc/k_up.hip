@@ -1,0 +1,268 @@
+// Gathered up / gate rows of the active neurons (PowerInfer page, Method, neuron-
+// aware operators of §5.4: the operator reads only the rows of neurons marked
+// active; Paper vs code, activation functions: ReLU and ReGLU).
+//
+//   hact[j][b] = act(Wa[idx_j] . x_b + ba[idx_j])        ReLU
+//   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0) * (Wl[idx_j] . x_b)   ReGLU
+//
+// A persistent grid of waves strides over the device-resident count; each wave
+// reads whole rows with coalesced 16-byte loads (a row is contiguous), keeps the
+// B dot products in registers, reduces them across the wave and applies the bias
+// and the activation in registers.  int4 rows are decoded in the kernel: a lane's
+// 16-byte load is exactly one group of 32 codes with its one fp16 scale.
+#include "sfx_common.hpp"
+#include "sfx_launch.hpp"
+
+namespace sfx {
+namespace {
+
+constexpr int kU = 8;         // 16-byte chunks per lane issued together
+constexpr int kBlocksPerCU = 2;
+
+template <class T, int NB, bool REGLU>
+__global__ __launch_bounds__(kBlock) void k_up(const uint8_t* __restrict__ x, const uint8_t* __restrict__ Wa,
+                                               const float* __restrict__ ba, const uint8_t* __restrict__ Wl,
+                                               const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+                                               int kmax, int B, int d, int f, float* __restrict__ hact) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * kWavesPerBlock;
+  const int k = min(*count, kmax);
+  const int nchunk = d / T::vec;
+  const size_t row_bytes = (size_t)d * T::bytes;
+
+  for (int j = wave; j < k; j += nwaves) {
+    const int i = idx[j];
+    const bool ok = (unsigned)i < (unsigned)f;
+    float za[NB], zl[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
+    if (ok) {
+      const uint8_t* ra = Wa + (size_t)i * row_bytes;
+      const uint8_t* rl = REGLU ? Wl + (size_t)i * row_bytes : nullptr;
+      for (int c0 = 0; c0 < nchunk; c0 += kU * kWave) {
+        Raw<16> wa[kU], wl[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = c0 + u * kWave + lane;
+          if (c < nchunk) {
+            wa[u] = load_raw<16>(ra + (size_t)c * 16);
+            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = c0 + u * kWave + lane;
+          if (c < nchunk) {
+            float af[T::vec], lf[T::vec];
+            unpack<T, 4>(wa[u].w, af);
+            if (REGLU) unpack<T, 4>(wl[u].w, lf);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              if (b < B) {
+                Raw<16> xv = load_raw<16>(x + (size_t)b * row_bytes + (size_t)c * 16);
+                float xf[T::vec];
+                unpack<T, 4>(xv.w, xf);
+#pragma unroll
+                for (int e = 0; e < T::vec; ++e) {
+                  za[b] = fmaf(af[e], xf[e], za[b]);
+                  if (REGLU) zl[b] = fmaf(lf[e], xf[e], zl[b]);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      za[b] = wave_sum(za[b]);
+      if (REGLU) zl[b] = wave_sum(zl[b]);
+    }
+    if (lane == 0) {
+      const float bias = (ok && ba != nullptr) ? ba[i] : 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b < B) {
+          float a = ok ? fmaxf(za[b] + bias, 0.f) : 0.f;
+          if (REGLU) a *= zl[b];
+          hact[(size_t)j * B + b] = a;
+        }
+      }
+    }
+  }
+}
+
+// int4 rows: codes [f][d/2] bytes, scales [f][d/32] fp16; x is fp16.
+template <int NB, bool REGLU>
+__global__ __launch_bounds__(kBlock) void k_up_q4(const uint8_t* __restrict__ x, const uint8_t* __restrict__ Wa,
+                                                  const uint16_t* __restrict__ Wa_s, const float* __restrict__ ba,
+                                                  const uint8_t* __restrict__ Wl, const uint16_t* __restrict__ Wl_s,
+                                                  const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+                                                  int kmax, int B, int d, int f, float* __restrict__ hact) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * kWavesPerBlock;
+  const int k = min(*count, kmax);
+  const int ngroup = d >> 5;                  // 32 columns per group = 16 bytes of codes
+  const size_t row_bytes = (size_t)d >> 1;
+  const size_t x_bytes = (size_t)d * 2;
+
+  for (int j = wave; j < k; j += nwaves) {
+    const int i = idx[j];
+    const bool ok = (unsigned)i < (unsigned)f;
+    float za[NB], zl[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
+    if (ok) {
+      for (int g0 = 0; g0 < ngroup; g0 += 4 * kWave) {
+        Raw<16> qa[4], ql[4];
+        float sa[4], sl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int g = g0 + u * kWave + lane;
+          if (g < ngroup) {
+            qa[u] = load_raw<16>(Wa + (size_t)i * row_bytes + (size_t)g * 16);
+            sa[u] = (float)__builtin_bit_cast(_Float16, Wa_s[(size_t)i * ngroup + g]);
+            if (REGLU) {
+              ql[u] = load_raw<16>(Wl + (size_t)i * row_bytes + (size_t)g * 16);
+              sl[u] = (float)__builtin_bit_cast(_Float16, Wl_s[(size_t)i * ngroup + g]);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int g = g0 + u * kWave + lane;
+          if (g < ngroup) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              if (b < B) {
+                const uint8_t* xg = x + (size_t)b * x_bytes + (size_t)g * 64;
+                float pa = 0.f, pl = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {           // 4 words of codes = 32 columns
+                  Raw<16> xv = load_raw<16>(xg + q * 16);  // 8 fp16 = columns 8q..8q+7
+                  float xf[8];
+                  unpack<TF16, 4>(xv.w, xf);
+                  const uint32_t wa = qa[u].w[q];
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) {
+                    const float c = (float)((int32_t)(wa << (28 - 4 * e)) >> 28);
+                    pa = fmaf(c, xf[e], pa);
+                  }
+                  if (REGLU) {
+                    const uint32_t wl = ql[u].w[q];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                      const float c = (float)((int32_t)(wl << (28 - 4 * e)) >> 28);
+                      pl = fmaf(c, xf[e], pl);
+                    }
+                  }
+                }
+                za[b] = fmaf(sa[u], pa, za[b]);
+                if (REGLU) zl[b] = fmaf(sl[u], pl, zl[b]);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      za[b] = wave_sum(za[b]);
+      if (REGLU) zl[b] = wave_sum(zl[b]);
+    }
+    if (lane == 0) {
+      const float bias = (ok && ba != nullptr) ? ba[i] : 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b < B) {
+          float a = ok ? fmaxf(za[b] + bias, 0.f) : 0.f;
+          if (REGLU) a *= zl[b];
+          hact[(size_t)j * B + b] = a;
+        }
+      }
+    }
+  }
+}
+
+int grid_blocks(int kmax) {
+  const int cus = device_cu_count();
+  const int cap = (cus > 0 ? cus : 256) * kBlocksPerCU;
+  const int need = (kmax + kWavesPerBlock - 1) / kWavesPerBlock;
+  return need < cap ? (need > 0 ? need : 1) : cap;
+}
+
+template <class T, int NB>
+hipError_t run(hipStream_t s, int act, int B, int d, int f, const void* x, const void* Wa,
+               const float* ba, const void* Wl, const int32_t* idx, const int32_t* count, int kmax,
+               float* hact) {
+  dim3 g(grid_blocks(kmax)), blk(kBlock);
+  if (act == 1)
+    k_up<T, NB, true><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, (const uint8_t*)Wl, idx,
+                                         count, kmax, B, d, f, hact);
+  else
+    k_up<T, NB, false><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, nullptr, idx, count,
+                                          kmax, B, d, f, hact);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t run_q4(hipStream_t s, int act, int B, int d, int f, const void* x, const void* Wa,
+                  const void* Wa_s, const float* ba, const void* Wl, const void* Wl_s,
+                  const int32_t* idx, const int32_t* count, int kmax, float* hact) {
+  dim3 g(grid_blocks(kmax)), blk(kBlock);
+  if (act == 1)
+    k_up_q4<NB, true><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, (const uint16_t*)Wa_s, ba,
+                                         (const uint8_t*)Wl, (const uint16_t*)Wl_s, idx, count, kmax, B, d,
+                                         f, hact);
+  else
+    k_up_q4<NB, false><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, (const uint16_t*)Wa_s, ba,
+                                          nullptr, nullptr, idx, count, kmax, B, d, f, hact);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dispatch(hipStream_t s, int act, int B, int d, int f, const void* x, const void* Wa,
+                    const float* ba, const void* Wl, const int32_t* idx, const int32_t* count, int kmax,
+                    float* hact) {
+  switch (nb_class(B)) {
+    case 1: return run<T, 1>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case 2: return run<T, 2>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case 4: return run<T, 4>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case 8: return run<T, 8>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case 16: return run<T, 16>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case 32: return run<T, 32>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    default: return run<T, 64>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+  }
+}
+
+}  // namespace
+
+bool up_supported(int wdt, int act, int B) {
+  (void)act;
+  if (wdt == DT_Q4) return B <= 16;
+  return true;
+}
+
+hipError_t launch_up(hipStream_t s, int wdt, int act, int B, int d, int f, const void* x,
+                     const void* Wa, const void* Wa_s, const float* ba, const void* Wl,
+                     const void* Wl_s, const int32_t* idx, const int32_t* count, int kmax,
+                     float* hact) {
+  switch (wdt) {
+    case DT_F32: return dispatch<TF32>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case DT_F16: return dispatch<TF16>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case DT_BF16: return dispatch<TBF16>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
+    case DT_Q4:
+      switch (nb_class(B)) {
+        case 1: return run_q4<1>(s, act, B, d, f, x, Wa, Wa_s, ba, Wl, Wl_s, idx, count, kmax, hact);
+        case 2: return run_q4<2>(s, act, B, d, f, x, Wa, Wa_s, ba, Wl, Wl_s, idx, count, kmax, hact);
+        case 4: return run_q4<4>(s, act, B, d, f, x, Wa, Wa_s, ba, Wl, Wl_s, idx, count, kmax, hact);
+        case 8: return run_q4<8>(s, act, B, d, f, x, Wa, Wa_s, ba, Wl, Wl_s, idx, count, kmax, hact);
+        default: return run_q4<16>(s, act, B, d, f, x, Wa, Wa_s, ba, Wl, Wl_s, idx, count, kmax, hact);
+      }
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sfx

@@ -1,0 +1,177 @@
+// C ABI of libsfx: host-side argument checks, workspace queries, status strings.
+// Every check runs before anything is enqueued, and no check touches the GPU
+// except the CU-count query that sizes persistent grids.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "../../include/sfx.h"
+#include "sfx_launch.hpp"
+
+namespace sfx {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace sfx
+
+namespace {
+
+int elem_bytes(int wdt) {
+  switch (wdt) {
+    case SFX_F32: return 4;
+    case SFX_F16: return 2;
+    case SFX_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SFX_OK;
+  if (ws == nullptr || !aligned256(ws) || ws_bytes < need) return SFX_E_WORKSPACE;
+  return SFX_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SFX_OK : SFX_E_LAUNCH; }
+
+// Row of `n` stored elements of `wdt` (Q4: n codes) spans a multiple of 16 bytes.
+bool row_ok(int wdt, long long n) {
+  if (wdt == SFX_Q4G32) return n % 32 == 0;
+  return (n * elem_bytes(wdt)) % 16 == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sfx_status_str(int status) {
+  switch (status) {
+    case SFX_OK: return "ok";
+    case SFX_E_NULL: return "required pointer is NULL";
+    case SFX_E_SHAPE: return "size out of range or inconsistent";
+    case SFX_E_DTYPE: return "unknown or unsupported dtype / activation for this call";
+    case SFX_E_ALIGN: return "pointer or row not 16-byte aligned";
+    case SFX_E_WORKSPACE: return "workspace NULL, misaligned or too small";
+    case SFX_E_LAUNCH: return "HIP reported a launch error";
+    case SFX_E_UNSUPPORTED: return "combination not built";
+    case SFX_E_DEVICE: return "no current HIP device";
+    default: return "unknown status";
+  }
+}
+
+int sfx_abi_version(void) { return SFX_ABI_VERSION; }
+
+// ------------------------------------------------------------------------------ predict
+
+size_t sfx_predict_ws(int wdt, int B, int d, int h, int f) {
+  if (B < 1 || B > SFX_MAX_B || h < 1) return 0;
+  return sfx::predict_ws_bytes(wdt, B, d, h, f);
+}
+
+int sfx_predict(void* stream, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
+                const void* W2, float* scores, void* ws, size_t ws_bytes) {
+  if (wdt != SFX_F32 && wdt != SFX_F16 && wdt != SFX_BF16) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1) return SFX_E_SHAPE;
+  if (!x || !W1 || !W2 || !scores) return SFX_E_NULL;
+  if (!row_ok(wdt, d) || !row_ok(wdt, h)) return SFX_E_ALIGN;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || !aligned16(scores)) return SFX_E_ALIGN;
+  const int w = check_ws(ws, ws_bytes, sfx::predict_ws_bytes(wdt, B, d, h, f));
+  if (w != SFX_OK) return w;
+  return launch_status(
+      sfx::launch_predict((hipStream_t)stream, wdt, B, d, h, f, x, W1, W2, scores, ws));
+}
+
+// ------------------------------------------------------------------------------ compact
+
+size_t sfx_compact_ws(int B, int f) {
+  if (B < 1 || f < 1) return 0;
+  return sfx::compact_ws_bytes(B, f);
+}
+
+int sfx_compact(void* stream, int B, int f, const float* scores, float threshold, uint32_t* tok_bits,
+                uint32_t* union_bits, int32_t* idx, int kmax, int32_t* count, void* ws, size_t ws_bytes) {
+  if (B < 1 || B > SFX_MAX_B || f < 1) return SFX_E_SHAPE;
+  if (kmax < f) return SFX_E_SHAPE;
+  if (!scores || !union_bits || !idx || !count) return SFX_E_NULL;
+  if (!aligned16(scores) || !aligned4(union_bits) || !aligned4(idx) || (tok_bits && !aligned4(tok_bits)))
+    return SFX_E_ALIGN;
+  const int w = check_ws(ws, ws_bytes, sfx::compact_ws_bytes(B, f));
+  if (w != SFX_OK) return w;
+  return launch_status(sfx::launch_compact((hipStream_t)stream, B, f, scores, threshold, tok_bits, union_bits,
+                                           idx, kmax, count, ws));
+}
+
+// ------------------------------------------------------------------------------ up
+
+int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f, const void* x, const void* Wa,
+                  const void* Wa_scales, const float* ba, const void* Wl, const void* Wl_scales,
+                  const int32_t* idx, const int32_t* count, int kmax, float* hact) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || f < 1 || kmax < 1) return SFX_E_SHAPE;
+  if (!x || !Wa || !idx || !count || !hact) return SFX_E_NULL;
+  if (act == SFX_REGLU && !Wl) return SFX_E_NULL;
+  if (wdt == SFX_Q4G32 && (!Wa_scales || (act == SFX_REGLU && !Wl_scales))) return SFX_E_NULL;
+  if (!row_ok(wdt, d)) return wdt == SFX_Q4G32 ? SFX_E_SHAPE : SFX_E_ALIGN;
+  if (!aligned16(x) || !aligned16(Wa) || !aligned16(hact) || (Wl && !aligned16(Wl))) return SFX_E_ALIGN;
+  if (!sfx::up_supported(wdt, act, B)) return SFX_E_UNSUPPORTED;
+  return launch_status(sfx::launch_up((hipStream_t)stream, wdt, act, B, d, f, x, Wa, Wa_scales, ba,
+                                      act == SFX_REGLU ? Wl : nullptr, Wl_scales, idx, count, kmax, hact));
+}
+
+// ------------------------------------------------------------------------------ down
+
+size_t sfx_sparse_down_ws(int wdt, int B, int d, int kmax) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32 || B < 1 || B > SFX_MAX_B || d < 1 || kmax < 1) return 0;
+  return sfx::down_ws_bytes(wdt, B, d, kmax);
+}
+
+int sfx_sparse_down(void* stream, int wdt, int B, int d, int f, const void* Wd, const void* Wd_scales,
+                    const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y, void* ws,
+                    size_t ws_bytes) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || f < 1 || kmax < 1) return SFX_E_SHAPE;
+  if (!Wd || !idx || !count || !hact || !y) return SFX_E_NULL;
+  if (wdt == SFX_Q4G32 && !Wd_scales) return SFX_E_NULL;
+  if (!row_ok(wdt, d)) return wdt == SFX_Q4G32 ? SFX_E_SHAPE : SFX_E_ALIGN;
+  if (!aligned16(Wd) || !aligned16(hact) || !aligned16(y)) return SFX_E_ALIGN;
+  if (!sfx::down_supported(wdt, B)) return SFX_E_UNSUPPORTED;
+  const int w = check_ws(ws, ws_bytes, sfx::down_ws_bytes(wdt, B, d, kmax));
+  if (w != SFX_OK) return w;
+  return launch_status(sfx::launch_down((hipStream_t)stream, wdt, B, d, f, Wd, Wd_scales, idx, count, kmax,
+                                        hact, y, ws));
+}
+
+// ------------------------------------------------------------------------------ TAM
+
+size_t sfx_tam_ws(int G, int K) { return sfx::tam_ws_bytes(G, K); }
+
+int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits, float lambda, float eps, int K,
+                   float* score, uint32_t* hot_bits, uint32_t* entered_bits, uint32_t* left_bits,
+                   int32_t* topk, int32_t* topk_count, void* ws, size_t ws_bytes) {
+  (void)ws;
+  (void)ws_bytes;
+  if (L < 1 || G < 1 || G > SFX_MAX_GROUPS || K < 0 || K > G) return SFX_E_SHAPE;
+  if (!(lambda > 0.0f && lambda < 1.0f) || !(eps >= 0.0f)) return SFX_E_SHAPE;
+  if (!union_bits || !score || !hot_bits || !entered_bits || !left_bits || !topk_count) return SFX_E_NULL;
+  if (K > 0 && !topk) return SFX_E_NULL;
+  return launch_status(sfx::launch_tam((hipStream_t)stream, L, G, union_bits, lambda, eps, K, score, hot_bits,
+                                       entered_bits, left_bits, topk, topk_count));
+}
+
+}  // extern "C"

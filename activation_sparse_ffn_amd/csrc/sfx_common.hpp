@@ -1,0 +1,64 @@
+// Shared device helpers for the libsfx kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfx {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;          // threads per workgroup for the streaming kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q4 = 3 };
+
+// Storage traits.  `vec` = elements in one 16-byte load.
+struct TF32 { static constexpr int bytes = 4; static constexpr int vec = 4; };
+struct TF16 { static constexpr int bytes = 2; static constexpr int vec = 8; };
+struct TBF16 { static constexpr int bytes = 2; static constexpr int vec = 8; };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Exact conversion of one 32-bit word holding storage elements to floats.
+__device__ __forceinline__ void unpack_word(TF32, uint32_t w, float* o) { o[0] = __uint_as_float(w); }
+__device__ __forceinline__ void unpack_word(TF16, uint32_t w, float* o) {
+  half2_t h = __builtin_bit_cast(half2_t, w);
+  o[0] = (float)h.x;
+  o[1] = (float)h.y;
+}
+__device__ __forceinline__ void unpack_word(TBF16, uint32_t w, float* o) {
+  o[0] = __uint_as_float(w << 16);
+  o[1] = __uint_as_float(w & 0xFFFF0000u);
+}
+
+template <class T>
+struct PerWord { static constexpr int n = 4 / T::bytes; };
+
+// `NW` 32-bit words -> NW * (4 / bytes) floats.
+template <class T, int NW>
+__device__ __forceinline__ void unpack(const uint32_t* w, float* o) {
+#pragma unroll
+  for (int i = 0; i < NW; ++i) unpack_word(T{}, w[i], o + i * PerWord<T>::n);
+}
+
+// A load of N bytes (N = 4, 8 or 16) as one vector instruction.
+template <int N>
+struct alignas(N) Raw { uint32_t w[N / 4]; };
+
+template <int N>
+__device__ __forceinline__ Raw<N> load_raw(const void* p) { return *reinterpret_cast<const Raw<N>*>(p); }
+
+// Butterfly sum over the 64 lanes of a wave; every lane gets the total.  The
+// order of additions is fixed, so the result is reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Token-count classes that kernels are instantiated for.
+__host__ __device__ constexpr int nb_class(int B) {
+  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+}
+
+}  // namespace sfx

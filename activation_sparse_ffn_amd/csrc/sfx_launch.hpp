@@ -1,0 +1,38 @@
+// Internal launchers, one per kernel family.  Arguments are already validated by
+// the C ABI layer; each launcher only picks an instantiation and enqueues it.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfx {
+
+int device_cu_count();  // cached per device; 0 if no device
+
+size_t predict_ws_bytes(int wdt, int B, int d, int h, int f);
+hipError_t launch_predict(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x,
+                          const void* W1, const void* W2, float* scores, void* ws);
+
+size_t compact_ws_bytes(int B, int f);
+hipError_t launch_compact(hipStream_t s, int B, int f, const float* scores, float t,
+                          uint32_t* tok_bits, uint32_t* union_bits, int32_t* idx, int kmax,
+                          int32_t* count, void* ws);
+
+hipError_t launch_up(hipStream_t s, int wdt, int act, int B, int d, int f, const void* x,
+                     const void* Wa, const void* Wa_s, const float* ba, const void* Wl,
+                     const void* Wl_s, const int32_t* idx, const int32_t* count, int kmax,
+                     float* hact);
+bool up_supported(int wdt, int act, int B);
+
+size_t down_ws_bytes(int wdt, int B, int d, int kmax);
+hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* Wd,
+                       const void* Wd_s, const int32_t* idx, const int32_t* count, int kmax,
+                       const float* hact, float* y, void* ws);
+bool down_supported(int wdt, int B);
+
+size_t tam_ws_bytes(int G, int K);
+hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, float lambda,
+                      float eps, int K, float* score, uint32_t* hot_bits, uint32_t* entered,
+                      uint32_t* left, int32_t* topk, int32_t* topk_count);
+
+}  // namespace sfx

@@ -1,0 +1,64 @@
+"""Buffers and call order of one layer-step (predict -> compact -> up -> down) and of
+the per-step TAM update, on top of the libsfx binding.  Orchestration only: every
+number is produced by the library's kernels."""
+import torch
+
+from . import _abi as A
+
+TORCH_WDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+WDT_CODE = {"f32": A.SFX_F32, "f16": A.SFX_F16, "bf16": A.SFX_BF16, "q4": A.SFX_Q4G32}
+
+
+class StepBuffers:
+    """Device buffers for one layer-step at batch B.  `union_bits` may be a row of a
+    caller-owned [L][W] array, so the TAM update can read every layer's union."""
+
+    def __init__(self, d: int, f: int, h: int, B: int, wdtype: str, pdtype: str, device="cuda",
+                 union_bits: torch.Tensor = None, kmax: int = None):
+        self.d, self.f, self.h, self.B = d, f, h, B
+        self.wdtype, self.pdtype = wdtype, pdtype
+        self.kmax = f if kmax is None else kmax
+        W = (f + 31) // 32
+        dev = torch.device(device)
+        self.scores = torch.empty(B, f, dtype=torch.float32, device=dev)
+        self.tok_bits = torch.zeros(B, W, dtype=torch.int32, device=dev)
+        self.union_bits = union_bits if union_bits is not None else torch.zeros(W, dtype=torch.int32, device=dev)
+        self.idx = torch.zeros(self.kmax, dtype=torch.int32, device=dev)
+        self.count = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.hact = torch.zeros(self.kmax, B, dtype=torch.float32, device=dev)
+        self.y = torch.empty(B, d, dtype=torch.float32, device=dev)
+        self.ws_pred = A.workspace(A.sfx_predict_ws(WDT_CODE[pdtype], B, d, h, f), dev)
+        self.ws_comp = A.workspace(A.sfx_compact_ws(B, f), dev)
+        self.ws_down = A.workspace(A.sfx_sparse_down_ws(WDT_CODE[wdtype], B, d, self.kmax), dev)
+
+
+def run_layer(buf: StepBuffers, layer, x: torch.Tensor, threshold: float, act: str,
+              tok_bits: bool = True, stream=None):
+    """predict -> compact -> up -> down for one layer.  `layer` holds the device
+    tensors W1, W2, Wa, ba, Wd (Wl, Wa_s, Wl_s, Wd_s when present)."""
+    g = layer.get if isinstance(layer, dict) else (lambda k: getattr(layer, k, None))
+    A.sfx_predict(x, g("W1"), g("W2"), buf.scores, buf.ws_pred, stream=stream)
+    A.sfx_compact(buf.scores, threshold, buf.union_bits, buf.idx, buf.count, buf.ws_comp,
+                  tok_bits=buf.tok_bits if tok_bits else None, stream=stream)
+    A.sfx_sparse_up(x, g("Wa"), g("ba"), buf.idx, buf.count, buf.hact, act=act, Wa_scales=g("Wa_s"),
+                    Wl=g("Wl"), Wl_scales=g("Wl_s"), stream=stream)
+    A.sfx_sparse_down(g("Wd"), buf.idx, buf.count, buf.hact, buf.y, buf.ws_down, Wd_scales=g("Wd_s"),
+                      stream=stream)
+
+
+class TamState:
+    """TAM state of L layers with G groups each (fp32 scores, hot bits)."""
+
+    def __init__(self, L: int, G: int, K: int, device="cuda"):
+        HW = (G + 31) // 32
+        self.L, self.G, self.K = L, G, K
+        self.score = torch.zeros(L, G, dtype=torch.float32, device=device)
+        self.hot = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.entered = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.left = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.topk = torch.full((L, max(K, 1)), -1, dtype=torch.int32, device=device)
+        self.topk_count = torch.zeros(L, dtype=torch.int32, device=device)
+
+    def update(self, union_bits: torch.Tensor, lam: float, eps: float, stream=None):
+        A.sfx_tam_update(union_bits, lam, eps, self.K, self.score, self.hot, self.entered, self.left,
+                         self.topk, self.topk_count, stream=stream)

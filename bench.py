@@ -1,0 +1,226 @@
+"""Benchmark of the predictor-gated activation-sparse FFN step on one MI355X.
+
+A step is one decode step through the whole stack: for every layer predict ->
+compact -> sparse up -> sparse down, then one TAM update over all layers.  The
+default workload is the OPT-6.7B-shaped ReLU stack (d=4096, f=16384, h=1024, fp16,
+32 layers, batch 1) on seeded synthetic layers generated on the device.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--batch 1]
+
+Prints one JSON line.  `value` = tokens/s per FFN layer = B * layers / step time,
+with every input resident in HBM when the timed region starts; the timed region
+is one replay of a HIP graph holding exactly K steps.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "sparse-FFN tokens/s per layer + effective HBM GB/s (% of peak) at batch 1"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--config", default="C2")
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--layers", type=int, default=0, help="0 = the workload's layer count")
+    p.add_argument("--roofline-steps", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=4)
+    p.add_argument("--cpu-steps", type=int, default=32)
+    p.add_argument("--tam-lambda", type=float, default=0.9)
+    p.add_argument("--tam-eps", type=float, default=0.01)
+    return p.parse_args()
+
+
+def e_bytes(dt):
+    return {"f32": 4, "f16": 2, "bf16": 2}[dt]
+
+
+def row_bytes(cfg):
+    if cfg.wdtype == "q4":
+        return cfg.d // 2 + 2 * (cfg.d // 32)
+    return cfg.d * e_bytes(cfg.wdtype)
+
+
+def kernel_bytes(cfg, B, k):
+    """Algorithmic bytes of one layer-step, per call (what the method must move)."""
+    d, f, h = cfg.d, cfg.f, cfg.h
+    ep = e_bytes(cfg.pdtype)
+    na = 2 if cfg.act == "reglu" else 1
+    er = row_bytes(cfg)
+    return {
+        "predict": (h * d + f * h) * ep + B * d * ep + B * f * 4,
+        "compact": B * f * 4 + (1 + B) * f / 8 + k * 4,
+        "up": B * d * ep + k * 4 + na * k * er + k * 4 + B * k * 4,
+        "down": k * 4 + B * k * 4 + k * er + B * d * 4,
+    }
+
+
+def cpu_baseline(cfg, layers_np, xs_np, B, steps):
+    """The fp64 oracle, unchanged, on a bounded sample of the same workload."""
+    from oracle import sfx_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = 0
+    t0 = time.perf_counter()
+    for li, Lnp in enumerate(layers_np):
+        for s in range(steps):
+            O.ffn_step(xs_np[li][s], Lnp, cfg.wdtype, cfg.pdtype, cfg.act, Lnp["threshold"])
+            n += 1
+    dt = time.perf_counter() - t0
+    return {"value": B * n / dt, "unit": "tokens/s/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(layers_np)} layers x {steps} decode steps of the benchmark workload "
+                      f"(batch {B}), fp64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sharded path is "
+              "described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as S
+    from activation_sparse_ffn_amd import StepBuffers, TamState, run_layer
+    from activation_sparse_ffn_amd import _abi as A
+
+    A.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = S.CONFIGS[args.config]
+    B = args.batch
+    L = args.layers or cfg.layers
+    K, W = args.steps, args.warmup
+    G = (cfg.f + 31) // 32
+    tam_k = max(1, G // 4) if cfg.tam is None else cfg.tam["K"]
+
+    print(f"[bench] generating {L} layers of {cfg.workload}", file=sys.stderr, flush=True)
+    layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
+    xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
+    ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
+    buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
+    tam = TamState(L, G, tam_k, device=dev)
+    tensors = [ly.tensors() for ly in layers]
+
+    def step(s):
+        for l in range(L):
+            buf.union_bits = ubits[l]
+            run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
+        tam.update(ubits, args.tam_lambda, args.tam_eps)
+
+    # eager pass (loads code objects), then capture the warmup and timed steps
+    step(0)
+    torch.cuda.synchronize()
+    print("[bench] capturing graphs", file=sys.stderr, flush=True)
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for s in range(W):
+            step(s)
+    with torch.cuda.graph(g_timed):
+        for s in range(W, W + K):
+            step(s)
+    torch.cuda.synchronize()
+
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    g_timed.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / K
+    print(f"[bench] timed {K} steps: {ms_total:.3f} ms", file=sys.stderr, flush=True)
+
+    # Active counts of the timed steps (deterministic: an eager re-run of the same steps).
+    counts = np.zeros((K, L), dtype=np.int64)
+    for i, s in enumerate(range(W, W + K)):
+        cs = []
+        for l in range(L):
+            buf.union_bits = ubits[l]
+            run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
+            cs.append(buf.count.clone())
+        counts[i] = torch.cat(cs).cpu().numpy()
+    kb = [kernel_bytes(cfg, B, int(k)) for k in counts.reshape(-1)]
+    tam_bytes = L * G * 16
+    step_bytes = sum(sum(v.values()) for v in kb) / K + tam_bytes
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # Dominant kernel: the predictor (largest byte share).  Per-launch durations from
+    # HIP events bracketing each sfx_predict on the launch stream; all launches are
+    # queued behind a spin kernel so the events time the GPU, not the host.
+    R = min(args.roofline_steps, K)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    i = 0
+    for s in range(W, W + R):
+        for l in range(L):
+            t = tensors[l]
+            evs[i][0].record()
+            A.sfx_predict(xs[l][s], t["W1"], t["W2"], buf.scores, buf.ws_pred)
+            evs[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pred_bytes = kernel_bytes(cfg, B, 0)["predict"]
+    pred_gbps = pred_bytes / (dur_ms.mean() * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(B * L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.wdtype,
+        "data": "synthetic (seeded, generated on device)",
+        "config": {"workload": cfg.workload, "batch": B, "layers": L, "d": cfg.d, "f": cfg.f, "h": cfg.h,
+                   "act": cfg.act, "density": cfg.density, "tam": {"lambda": args.tam_lambda,
+                                                                  "eps": args.tam_eps, "K": tam_k, "G": G}},
+        "us_per_layer_step": round(ms_step * 1e3 / L, 3),
+        "effective_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "mean_active": round(float(counts.mean()), 1),
+        "bytes_per_layer_step": round(step_bytes / L, 0),
+        "roofline": {"bound": "hbm", "kernel": "sfx_predict", "achieved": round(pred_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(pred_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
+                     "bytes_per_launch": pred_bytes, "launches": int(dur_ms.size)},
+    }
+
+    if not args.no_cpu_baseline:
+        import synthetic.gen as SG
+        nl = min(args.cpu_layers, L)
+        ns = min(args.cpu_steps, K)
+        lnp, xnp = [], []
+        for l in range(nl):
+            d = {k: SG.storage_numpy(v) for k, v in tensors[l].items()}
+            d["threshold"] = layers[l].threshold
+            lnp.append(d)
+            xnp.append([SG.storage_numpy(xs[l][s]) for s in range(W, W + ns)])
+        result["cpu_baseline"] = cpu_baseline(cfg, lnp, xnp, B, ns)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * sfx.h -- C ABI of libsfx, the predictor-gated activation-sparse FFN step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One layer-step, as the PowerInfer page describes it (Method: per-layer predictor,
+ * hybrid execution, neuron-aware operators) and as KAIROX extends it (Core method:
+ * groups of 32 neurons, temporal activation momentum):
+ *
+ *   sfx_predict      scores = W2 relu(W1 x)                    per token
+ *   sfx_compact      active = scores >= t, union over tokens,   ascending index list
+ *   sfx_sparse_up    hact   = act(Wa[i] x + b_i) (ReLU / ReGLU) active rows only
+ *   sfx_sparse_down  y      = sum_j hact_j Wd[idx_j]            active rows only
+ *   sfx_tam_update   per-group momentum score and hot set       once per step, all layers
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a caller-owned DEVICE pointer unless the comment
+ *     says otherwise.  The library never frees or retains a pointer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call only enqueues kernels on it and returns: it never synchronises, never
+ *     allocates device memory and reads no environment variables.  Calls may be
+ *     captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns a negative sfx_status and enqueues nothing.  SFX_E_LAUNCH
+ *     reports a HIP launch error (hipGetLastError) after enqueueing.
+ *   - Matrices are row-major and densely packed.  Device pointers must be 16-byte
+ *     aligned (bit masks, index lists and counts: 4-byte aligned) and every row
+ *     of a weight matrix must span a multiple of 16 bytes.
+ *   - Workspaces must be 256-byte aligned, at least as large as the matching
+ *     *_ws() query, and zero-filled before their first use; each call leaves the
+ *     control words it uses at zero again.  One workspace must not be used by two
+ *     calls that may run at the same time.
+ *   - Batch B (tokens per step) is 1..SFX_MAX_B.
+ *   - The data passed to one call must not change until that call's kernels end.
+ */
+#ifndef SFX_H
+#define SFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFX_ABI_VERSION 1
+#define SFX_MAX_B 64
+#define SFX_MAX_GROUPS 1024
+
+typedef enum {
+  SFX_OK = 0,
+  SFX_E_NULL = -1,        /* a required pointer is NULL */
+  SFX_E_SHAPE = -2,       /* a size is out of range or inconsistent */
+  SFX_E_DTYPE = -3,       /* unknown dtype / activation, or one the call does not take */
+  SFX_E_ALIGN = -4,       /* a pointer or a row is not 16-byte aligned */
+  SFX_E_WORKSPACE = -5,   /* workspace NULL, misaligned or smaller than the query */
+  SFX_E_LAUNCH = -6,      /* HIP reported an error for an enqueued kernel */
+  SFX_E_UNSUPPORTED = -7, /* the combination is valid but not built */
+  SFX_E_DEVICE = -8       /* no current HIP device could be queried */
+} sfx_status;
+
+typedef enum {
+  SFX_F32 = 0,   /* IEEE binary32 */
+  SFX_F16 = 1,   /* IEEE binary16 */
+  SFX_BF16 = 2,  /* bfloat16 (high half of binary32) */
+  SFX_Q4G32 = 3  /* FFN rows only: symmetric int4, planar.  q [rows][cols/2] uint8,
+                    byte c holds column 2c in its low nibble and 2c+1 in its high
+                    nibble, two's complement in [-8, 7]; scales [rows][cols/32]
+                    binary16, one per 32 consecutive columns; w = q * s. */
+} sfx_dtype;
+
+typedef enum {
+  SFX_RELU = 0,  /* a = max(Wa_i . x + b_i, 0) */
+  SFX_REGLU = 1  /* a = max(Wa_i . x + b_i, 0) * (Wl_i . x)  (gate = Wa, linear = Wl) */
+} sfx_act;
+
+/* Host: static text for a status code. */
+const char* sfx_status_str(int status);
+/* Host: SFX_ABI_VERSION of the built library. */
+int sfx_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_predict -- per-layer MLP predictor (PowerInfer page, Method, the predictor
+ * pseudocode of §5.1: one hidden layer with ReLU, one score per FFN neuron).
+ *
+ *   hidden_b = max(W1 x_b, 0)   (fp32, kept in the workspace, never rounded to wdt)
+ *   scores_b = W2 hidden_b      (fp32 accumulation)
+ *
+ *   wdt     SFX_F32, SFX_F16 or SFX_BF16: storage of x, W1 and W2.
+ *   x       [B][d] wdt, the FFN input of each token.
+ *   W1      [h][d] wdt.   W2 [f][h] wdt.  No biases.
+ *   scores  [B][f] fp32, written.
+ *   ws      >= sfx_predict_ws(wdt, B, d, h, f) bytes.
+ * Rows: d*sizeof(wdt) and h*sizeof(wdt) must be multiples of 16 bytes.
+ * B >= 16 runs the second layer on the matrix cores with the hidden vector split
+ * into two half-precision terms, so scores keep fp32 accuracy.
+ * ------------------------------------------------------------------------------- */
+size_t sfx_predict_ws(int wdt, int B, int d, int h, int f);
+int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
+                const void* x, const void* W1, const void* W2,
+                float* scores, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_compact -- threshold and compaction (PowerInfer page, Method, hybrid-execution
+ * pseudocode: a neuron is computed when its score is >= the threshold; Paper vs code,
+ * predictor threshold).  For B > 1 the active set is the union of the per-token sets.
+ *
+ *   scores     [B][f] fp32.  A NaN score is inactive.
+ *   threshold  fp32 host scalar; compared as score >= threshold in fp32.
+ *   tok_bits   [B][W] uint32 (W = ceil(f/32)) per-token masks, or NULL.
+ *   union_bits [W] uint32 union mask.  Neuron i is bit (i % 32) of word i / 32;
+ *              bits past f are zero.  Word g is group g of 32 neurons.
+ *   idx        [kmax] int32: the union's neurons in ascending order in idx[0..count).
+ *              Entries from count on are left unchanged.
+ *   kmax       capacity of idx; must be >= f, so the list cannot overflow.
+ *   count      device int32 scalar, written.  It stays on the device.
+ *   ws         >= sfx_compact_ws(B, f) bytes.
+ * ------------------------------------------------------------------------------- */
+size_t sfx_compact_ws(int B, int f);
+int sfx_compact(void* stream, int B, int f, const float* scores, float threshold,
+                uint32_t* tok_bits, uint32_t* union_bits, int32_t* idx, int kmax,
+                int32_t* count, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_sparse_up -- gathered up (and gate) rows of the active neurons (PowerInfer page,
+ * Method, neuron-aware operators of §5.4: only active rows are read; Paper vs code,
+ * activation functions ReLU and ReGLU).  Every token computes every listed neuron.
+ *
+ *   hact[j][b] = act(Wa[idx[j]] . x_b + ba[idx[j]])      for j < *count, b < B
+ *
+ *   wdt      storage of the FFN rows: SFX_F32, SFX_F16, SFX_BF16 or SFX_Q4G32.
+ *   act      SFX_RELU or SFX_REGLU.
+ *   x        [B][d] in wdt (binary16 when wdt = SFX_Q4G32).
+ *   Wa       [f][d] activated branch, row = neuron (Q4: packed codes).
+ *   Wa_scales Q4 scales [f][d/32] binary16, else NULL.
+ *   ba       [f] fp32 bias of the activated branch, or NULL for none.
+ *   Wl, Wl_scales  ReGLU linear branch, same layout as Wa; NULL for ReLU.
+ *   idx, count     the list from sfx_compact (or any list of distinct neurons in
+ *                  [0, f)); count is read on the device and clamped to kmax; an
+ *                  index outside [0, f) yields a zero activation.
+ *   hact     [kmax][B] fp32; rows j < count are written, the rest are unchanged.
+ * Q4 requires d % 32 == 0.
+ * ------------------------------------------------------------------------------- */
+int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f,
+                  const void* x, const void* Wa, const void* Wa_scales, const float* ba,
+                  const void* Wl, const void* Wl_scales,
+                  const int32_t* idx, const int32_t* count, int kmax, float* hact);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_sparse_down -- gathered neuron-major down rows (PowerInfer page, Method,
+ * hybrid-execution pseudocode: y is the sum of the active neurons' contributions;
+ * neuron-aware operators: blocks own disjoint neurons).
+ *
+ *   y[b][:] = sum_{j < count} hact[j][b] * Wd[idx[j]][:]
+ *
+ * The neurons are split into slices; each slice's partial sum goes to the
+ * workspace and the last slice to finish a column tile adds the partials in slice
+ * order, so y is bitwise reproducible.  y is overwritten (zero when count = 0).
+ *
+ *   Wd        [f][d] wdt, row = neuron (Q4: packed codes); Wd_scales as for Wa.
+ *   idx, count, kmax, hact   as produced by sfx_compact / sfx_sparse_up.
+ *   y         [B][d] fp32.
+ *   ws        >= sfx_sparse_down_ws(wdt, B, d, kmax) bytes.
+ * ------------------------------------------------------------------------------- */
+size_t sfx_sparse_down_ws(int wdt, int B, int d, int kmax);
+int sfx_sparse_down(void* stream, int wdt, int B, int d, int f,
+                    const void* Wd, const void* Wd_scales,
+                    const int32_t* idx, const int32_t* count, int kmax, const float* hact,
+                    float* y, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_tam_update -- temporal activation momentum over groups of 32 neurons (KAIROX
+ * page, Core method: item 3, decisions per group with at most 1024 groups per layer;
+ * item 4, TAM with tau = (1 - lambda) + eps; item 6, set-difference update).
+ * One call updates L layers (one workgroup each).
+ *
+ *   a_g   = (union_bits[l][g] != 0)                       group g touched this step
+ *   s_g  <- lambda * s_g + (1 - lambda) * a_g              fp32
+ *   cand  = { g : s_g > tau },  tau = (1 - lambda) + eps   in fp32
+ *   topk  = first min(K, |cand|) of cand ranked by s desc, then g asc
+ *   hot'  = topk;  entered = hot' & ~hot;  left = hot & ~hot'
+ *
+ *   L, G        layers, groups per layer (1..SFX_MAX_GROUPS).
+ *   union_bits  [L][G] uint32: word g of layer l's union mask (sfx_compact output).
+ *   lambda      in (0, 1); eps >= 0; K in 0..G.
+ *   score       [L][G] fp32 state, in/out (start at zero).
+ *   hot_bits    [L][ceil(G/32)] uint32 state, in/out (start at zero).
+ *   entered_bits, left_bits  [L][ceil(G/32)] uint32, written.
+ *   topk        [L][K] int32, written (entries past topk_count are -1).
+ *   topk_count  [L] int32, written.
+ *   ws          >= sfx_tam_ws(G, K) bytes (may be NULL when that is 0).
+ * ------------------------------------------------------------------------------- */
+size_t sfx_tam_ws(int G, int K);
+int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
+                   float lambda, float eps, int K,
+                   float* score, uint32_t* hot_bits, uint32_t* entered_bits,
+                   uint32_t* left_bits, int32_t* topk, int32_t* topk_count,
+                   void* ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFX_H */

@@ -1,0 +1,129 @@
+"""Host-side checks of libsfx: the library loads, exports every function that
+include/sfx.h declares, and rejects bad arguments with the documented status
+before anything is enqueued (no call here reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparse_ffn_amd import _abi as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfx.h")
+
+E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED = -1, -2, -3, -4, -5, -7
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(A.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert A.abi_version() == 1
+    for s in range(-8, 1):
+        assert A.status_str(s) and A.status_str(s) != "unknown status"
+    assert A.status_str(-99) == "unknown status"
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)          # 16-byte aligned fake device addresses (never dereferenced)
+ODD = P(0x10004)
+
+
+def test_predict_validation(lib):
+    ws_n = lib.sfx_predict_ws(1, 1, 4096, 1024, 16384)
+    assert ws_n == 4096
+    ws = P(0x20000)
+    call = lambda **k: lib.sfx_predict(None, k.get("wdt", 1), k.get("B", 1), k.get("d", 4096), k.get("h", 1024),
+                                       k.get("f", 16384), k.get("x", GOOD), GOOD, GOOD, k.get("s", GOOD),
+                                       k.get("ws", ws), k.get("wsn", ws_n))
+    assert call(wdt=3) == E_DTYPE               # int4 predictor is not built
+    assert call(wdt=9) == E_DTYPE
+    assert call(B=0) == E_SHAPE and call(B=65) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(d=4100) == E_ALIGN              # row of 8200 bytes
+    assert call(x=ODD) == E_ALIGN
+    assert call(ws=None) == E_WORKSPACE
+    assert call(wsn=ws_n - 1) == E_WORKSPACE
+    assert call(ws=P(0x20010)) == E_WORKSPACE   # workspace must be 256-byte aligned
+
+
+def test_compact_validation(lib):
+    ws = P(0x20000)
+    n = lib.sfx_compact_ws(1, 1000)
+    call = lambda **k: lib.sfx_compact(None, k.get("B", 1), k.get("f", 1000), k.get("s", GOOD), ctypes.c_float(0.0),
+                                       None, k.get("u", GOOD), GOOD, k.get("kmax", 1000), k.get("c", GOOD),
+                                       k.get("ws", ws), k.get("wsn", n))
+    assert call(kmax=999) == E_SHAPE            # kmax must be >= f
+    assert call(u=None) == E_NULL and call(c=None) == E_NULL
+    assert call(s=ODD) == E_ALIGN
+    assert call(wsn=0) == E_WORKSPACE
+
+
+def test_up_validation(lib):
+    call = lambda **k: lib.sfx_sparse_up(None, k.get("wdt", 1), k.get("act", 0), k.get("B", 1), k.get("d", 4096),
+                                         1000, GOOD, GOOD, k.get("sa"), None, k.get("wl"), k.get("sl"),
+                                         GOOD, GOOD, 1000, GOOD)
+    assert call(act=2) == E_DTYPE
+    assert call(wdt=4) == E_DTYPE
+    assert call(act=1) == E_NULL                # ReGLU needs the linear branch
+    assert call(wdt=3) == E_NULL                # int4 needs scales
+    assert call(wdt=3, sa=GOOD, d=4100) == E_SHAPE
+    assert call(wdt=3, sa=GOOD, B=32) == E_UNSUPPORTED
+    assert call(d=4092) == E_ALIGN
+
+
+def test_down_validation(lib):
+    n = lib.sfx_sparse_down_ws(1, 1, 4096, 16384)
+    assert n > 0
+    call = lambda **k: lib.sfx_sparse_down(None, k.get("wdt", 1), k.get("B", 1), 4096, 16384, GOOD,
+                                           k.get("sc"), GOOD, GOOD, 16384, GOOD, k.get("y", GOOD),
+                                           k.get("ws", P(0x20000)), k.get("wsn", n))
+    assert call(y=None) == E_NULL
+    assert call(wdt=3) == E_NULL
+    assert call(wsn=n - 256) == E_WORKSPACE
+    assert call(y=ODD) == E_ALIGN
+    assert call(wdt=3, sc=GOOD, B=17) == E_UNSUPPORTED
+
+
+def test_tam_validation(lib):
+    call = lambda **k: lib.sfx_tam_update(None, k.get("L", 1), k.get("G", 1024), GOOD, ctypes.c_float(k.get("lam", 0.9)),
+                                          ctypes.c_float(0.01), k.get("K", 256), GOOD, GOOD, GOOD, GOOD,
+                                          k.get("topk", GOOD), GOOD, None, 0)
+    assert call(G=1025) == E_SHAPE
+    assert call(K=1025) == E_SHAPE
+    assert call(lam=1.0) == E_SHAPE and call(lam=0.0) == E_SHAPE
+    assert call(topk=None) == E_NULL
+    assert lib.sfx_tam_ws(1024, 256) == 0
+
+
+def test_workspace_queries_are_monotone(lib):
+    a = lib.sfx_sparse_down_ws(1, 1, 4096, 16384)
+    b = lib.sfx_sparse_down_ws(1, 8, 4096, 16384)
+    assert b > a
+    assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == 8 * 1024 * 4
+    assert lib.sfx_predict_ws(1, 0, 4096, 1024, 16384) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        A.sfx_predict(x, torch.zeros(8, 64, dtype=torch.float16), torch.zeros(16, 8, dtype=torch.float16),
+                      torch.zeros(1, 16), torch.zeros(256, dtype=torch.uint8))
