@@ -16,7 +16,7 @@
 namespace sfx {
 namespace {
 
-constexpr int kRowsInFlight = 8;   // rows per wave whose segments are loaded together
+constexpr int kRowsInFlight = 16;  // rows per wave whose segments are loaded together
 constexpr int kTargetBlocks = 256;
 constexpr int kMaxSlices = 64;
 
@@ -30,7 +30,7 @@ struct TQ4 { static constexpr int bytes = 0; };
 template <int LW>
 struct Seg<TQ4, LW> {
   static constexpr int cpl = LW * 2;
-  // `scale` already holds the group's fp16 scale as float bits in o[-]: decode codes only.
+  // Codes only: the group's fp16 scale is applied to hact by the caller.
   __device__ static void decode(const Raw<LW>& r, const uint16_t*, int, float* o) {
 #pragma unroll
     for (int q = 0; q < LW / 4; ++q)
@@ -146,31 +146,51 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
         float* p = part + ((size_t)(slice * ntiles + tile) * B) * TW;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          if (b < B)
+          if (b < B) {
+            if constexpr (CPL % 2 == 0) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) p[(size_t)b * TW + lane * CPL + c] = acc[b][c];
+              for (int c = 0; c < CPL; c += 2)
+                store_through2(p + (size_t)b * TW + lane * CPL + c, acc[b][c], acc[b][c + 1]);
+            } else {
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) store_through(p + (size_t)b * TW + lane * CPL + c, acc[b][c]);
+            }
+          }
       }
     }
   }
   if (S == 1) return;
 
-  __threadfence();
+  wait_memory();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(tickets + tile, 1u) == (uint32_t)(S - 1));
+  if (threadIdx.x == 0) s_last = (take_ticket(tickets + tile) == (uint32_t)(S - 1));
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  acquire_agent();
 
-  // Last workgroup of this tile: y = sum of the S partials in slice order.
-  for (int e = threadIdx.x; e < B * TW; e += kBlock) {
-    const int b = e / TW;
-    const int cc = e - b * TW;
+  // Last workgroup of this tile: y = sum of the S partials in slice order.  Each
+  // thread owns 4 consecutive columns of one token and keeps up to 16 partial
+  // loads in flight.
+  for (int e = threadIdx.x; e < B * (TW / 4); e += kBlock) {
+    const int b = e / (TW / 4);
+    const int cc = (e - b * (TW / 4)) * 4;
     const int col = tile * TW + cc;
     if (col >= d) continue;
-    float sum = 0.f;
-    for (int s2 = 0; s2 < S; ++s2)
-      sum += part[((size_t)(s2 * ntiles + tile) * B + b) * TW + cc];
-    y[(size_t)b * d + col] = sum;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < S) v[u] = *reinterpret_cast<const float4*>(part + ((size_t)((s0 + u) * ntiles + tile) * B + b) * TW + cc);
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < S) { sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w; }
+    }
+    float* yo = y + (size_t)b * d + col;
+    yo[0] = sum.x;
+    if (col + 1 < d) yo[1] = sum.y;
+    if (col + 2 < d) yo[2] = sum.z;
+    if (col + 3 < d) yo[3] = sum.w;
   }
   if (threadIdx.x == 0) tickets[tile] = 0u;
 }

@@ -56,6 +56,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Cross-workgroup hand-off without a device-wide cache write-back.  A producer
+// writes the data it hands over with agent-scope atomic stores (written through to
+// the coherence point), waits for them to complete and then bumps a ticket with a
+// relaxed agent-scope atomic.  The consumer that sees the final ticket invalidates
+// its caches once (agent acquire) and reads the data with ordinary loads.  This
+// avoids an agent release fence in every producer, whose L2 write-back is
+// serialised across the device.
+__device__ __forceinline__ void store_through(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_through(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_through2(float* p, float a, float b) {  // p 8-byte aligned
+  const unsigned long long v = ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's outstanding memory operations have completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Ticket: returns the previous value (relaxed, agent scope).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* t) {
+  return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Consumer side: drop stale cache lines before reading handed-over data.
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 // Token-count classes that kernels are instantiated for.
 __host__ __device__ constexpr int nb_class(int B) {
   return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
