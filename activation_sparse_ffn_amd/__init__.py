@@ -8,4 +8,5 @@ from ._abi import (SFX_BF16, SFX_F16, SFX_F32, SFX_MAX_B, SFX_MAX_GROUPS, SFX_Q4
                    SFX_REGLU, SFX_RELU, SfxError, abi_version, load, sfx_compact, sfx_compact_ws,
                    sfx_predict, sfx_predict_ws, sfx_sparse_down, sfx_sparse_down_ws, sfx_sparse_up,
                    sfx_tam_update, sfx_tam_ws, status_str, workspace)
-from .step import StepBuffers, TamState, run_layer  # noqa: F401
+from ._abi import layer_descriptors, sfx_ffn_step, sfx_ffn_step_ws  # noqa: F401
+from .step import StackStep, StepBuffers, TamState, run_layer  # noqa: F401

@@ -22,7 +22,18 @@ WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
-           "sfx_tam_update")
+           "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step")
+
+
+class SfxLayer(ctypes.Structure):
+    """Mirror of `sfx_layer` in include/sfx.h (one layer of a fused step)."""
+    _fields_ = [("x", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("Wa", ctypes.c_void_p), ("Wa_scales", ctypes.c_void_p), ("ba", ctypes.c_void_p),
+                ("Wl", ctypes.c_void_p), ("Wl_scales", ctypes.c_void_p), ("Wd", ctypes.c_void_p),
+                ("Wd_scales", ctypes.c_void_p), ("threshold", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("scores", ctypes.c_void_p), ("tok_bits", ctypes.c_void_p), ("union_bits", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("hact", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
 
 
 class SfxError(RuntimeError):
@@ -66,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_tam_ws.argtypes = [I, I]
     lib.sfx_tam_update.restype = I
     lib.sfx_tam_update.argtypes = [P, I, I, P, F, F, I, P, P, P, P, P, P, P, Z]
+    lib.sfx_ffn_step_ws.restype = Z
+    lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
+    lib.sfx_ffn_step.restype = I
+    lib.sfx_ffn_step.argtypes = [P, I, I, I, I, I, I, I, P, P, Z]
     _lib = lib
     return lib
 
@@ -208,3 +223,35 @@ def sfx_tam_update(union_bits, lam, eps, K, score, hot_bits, entered_bits, left_
     st = load().sfx_tam_update(_stream(stream), L, G, _ptr(union_bits), float(lam), float(eps), int(K), *p,
                                ws.numel() if ws is not None else 0)
     _check(st, "sfx_tam_update")
+
+
+# ------------------------------------------------------------------------- fused step
+
+def sfx_ffn_step_ws(wdt: int, act: int, B: int, d: int, h: int, f: int) -> int:
+    """Workspace bytes of the fused step, 0 when the shape is not built for it."""
+    return load().sfx_ffn_step_ws(wdt, act, B, d, h, f)
+
+
+def layer_descriptors(layers, device=None) -> torch.Tensor:
+    """Device array of `sfx_layer` descriptors.  `layers` is a list of dicts of
+    tensors (x, W1, W2, Wa, ba, Wl, Wd, scores, tok_bits, union_bits, idx, count,
+    hact, y) plus a float `threshold`; missing optional entries are NULL."""
+    arr = (SfxLayer * len(layers))()
+    for i, e in enumerate(layers):
+        for name, _ in SfxLayer._fields_:
+            if name in ("threshold", "reserved"):
+                continue
+            t = e.get(name)
+            setattr(arr[i], name, _ptr(t).value if t is not None else None)
+        arr[i].threshold = float(e["threshold"])
+    raw = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return raw.to(device or "cuda")
+
+
+def sfx_ffn_step(wdt: int, act, B: int, d: int, h: int, f: int, descs: torch.Tensor, ws, stream=None):
+    """Every layer's predict -> compact -> up -> down in one launch."""
+    L = descs.numel() // ctypes.sizeof(SfxLayer)
+    a = ACTS[act] if isinstance(act, str) else int(act)
+    p = (_ptr(descs), _ptr(ws))
+    st = load().sfx_ffn_step(_stream(stream), wdt, a, B, d, h, f, L, p[0], p[1], ws.numel())
+    _check(st, "sfx_ffn_step")

@@ -1,0 +1,9 @@
+// Fused multi-layer step kernel, fp16 instantiations (see k_step.hpp).
+#include "k_step.hpp"
+
+namespace sfx {
+hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, int DL) {
+  (void)DL;
+  return step::dispatch_step<TF16>(s, p, act, P);
+}
+}  // namespace sfx

@@ -1,0 +1,79 @@
+// Host side of the fused multi-layer step: which shapes it is built for, its
+// workspace and its launch.
+#include <hip/hip_runtime.h>
+
+#include "sfx_common.hpp"
+#include "sfx_launch.hpp"
+#include "sfx_step.hpp"
+
+namespace sfx {
+
+hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, int DL);
+hipError_t launch_step_bf16(hipStream_t s, const StepParams& p, int act, int P, int DL);
+
+namespace {
+constexpr int kNT = 512, kNW = 8, kW2Bytes = 131072, kRedFloats = 1024;
+constexpr int kXBytes = 163840 - kW2Bytes - kRedFloats * 4 - 768;
+constexpr int kMaxWords = 1024;
+}  // namespace
+
+StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
+  StepGeom g{};
+  g.ok = false;
+  g.P = P;
+  if (P < 8 || (wdt != DT_F16 && wdt != DT_BF16) || B < 1 || B > 4 || (act != 0 && act != 1)) return g;
+  if (d < 8 || h < 8 || d % 8 != 0 || h % 8 != 0 || f < 1) return g;
+  const int W = (f + 31) / 32;
+  if (W > kMaxWords) return g;
+  const int nch1 = d / 8, nch2 = h / 8;
+  g.dl = nch1 <= 512 ? 1 : 0;
+  if (g.dl == 0) return g;
+  g.nr1 = (h + P - 1) / P;
+  if (g.nr1 > kNW) return g;
+  const int NB = nb_class(B);
+  const int nw2max = (W + P - 1) / P;
+  if (32 * nw2max * NB > kRedFloats) return g;
+  const long long items = 32LL * nw2max * nch2;
+  g.w2_lds = ((items + 63) / 64) * 64 * 16 <= kW2Bytes ? 1 : 0;
+  const int TB = NB < 4 ? NB : 4;
+  const long long hid_bytes = 4LL * TB * h;
+  if (hid_bytes > (g.w2_lds ? kXBytes : kW2Bytes)) return g;
+  int nct = (d + 8 * P - 1) / (8 * P);
+  int n = 1;
+  while (n < nct) n <<= 1;
+  if (n > kNW) return g;
+  g.cw = 8 * n;
+  g.ok = true;
+  (void)kNT;
+  return g;
+}
+
+size_t step_ws_bytes(int B, int h, int P) {
+  const size_t flags = ((size_t)P * 4 + 255) & ~(size_t)255;
+  const size_t hid = ((size_t)B * h * 4 + 255) & ~(size_t)255;
+  return 256 + flags + hid;
+}
+
+hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,
+                       void* ws, const StepGeom& g) {
+  StepParams p{};
+  p.layers = layers;
+  p.L = L;
+  p.B = B;
+  p.d = d;
+  p.h = h;
+  p.f = f;
+  p.W = (f + 31) / 32;
+  p.nr1 = g.nr1;
+  p.w2_lds = g.w2_lds;
+  p.cw = g.cw;
+  uint8_t* base = (uint8_t*)ws;
+  p.err = (uint32_t*)base;
+  p.go = (uint32_t*)(base + 128);
+  p.flags = (uint32_t*)(base + 256);
+  p.hid = (float*)(base + 256 + (((size_t)g.P * 4 + 255) & ~(size_t)255));
+  if (wdt == DT_F16) return launch_step_f16(s, p, act, g.P, g.dl);
+  return launch_step_bf16(s, p, act, g.P, g.dl);
+}
+
+}  // namespace sfx

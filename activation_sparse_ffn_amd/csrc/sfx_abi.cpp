@@ -7,6 +7,7 @@
 
 #include "../../include/sfx.h"
 #include "sfx_launch.hpp"
+#include "sfx_step.hpp"
 
 namespace sfx {
 
@@ -172,6 +173,31 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits, float
   if (K > 0 && !topk) return SFX_E_NULL;
   return launch_status(sfx::launch_tam((hipStream_t)stream, L, G, union_bits, lambda, eps, K, score, hot_bits,
                                        entered_bits, left_bits, topk, topk_count));
+}
+
+// ------------------------------------------------------------------------------ fused step
+
+size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f) {
+  const int P = sfx::device_cu_count();
+  if (P <= 0) return 0;
+  if (!sfx::step_geometry(wdt, act, B, d, h, f, P).ok) return 0;
+  return sfx::step_ws_bytes(B, h, P);
+}
+
+int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int L, const sfx_layer* layers,
+                 void* ws, size_t ws_bytes) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1 || L < 1) return SFX_E_SHAPE;
+  if (!layers) return SFX_E_NULL;
+  if (!ws) return SFX_E_WORKSPACE;
+  const int P = sfx::device_cu_count();
+  if (P <= 0) return SFX_E_DEVICE;
+  const sfx::StepGeom g = sfx::step_geometry(wdt, act, B, d, h, f, P);
+  if (!g.ok) return SFX_E_UNSUPPORTED;
+  const int w = check_ws(ws, ws_bytes, sfx::step_ws_bytes(B, h, P));
+  if (w != SFX_OK) return w;
+  return launch_status(sfx::launch_step((hipStream_t)stream, wdt, act, B, d, h, f, L, layers, ws, g));
 }
 
 }  // extern "C"

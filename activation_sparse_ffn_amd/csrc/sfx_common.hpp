@@ -56,6 +56,39 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum each of V values (V a power of two, V <= 64) over the 64 lanes of a wave,
+// halving the values held per lane at every exchange (about V + 6 shuffles instead
+// of 6 V).  On return v[0] of lane L holds the total of value index
+// L >> (6 - log2 V).  The pattern is fixed, so results are reproducible.
+template <int V, int O>
+struct WaveReduceStep {
+  __device__ __forceinline__ static void run(float* v, int lane) {
+    constexpr int half = V / 2;
+    const bool up = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = up ? v[i] : v[i + half];
+      const float keep = up ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, O, kWave);
+    }
+    WaveReduceStep<half, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct WaveReduceStep<1, O> {
+  __device__ __forceinline__ static void run(float* v, int) {
+#pragma unroll
+    for (int o = O; o > 0; o >>= 1) v[0] += __shfl_xor(v[0], o, kWave);
+  }
+};
+template <int V>
+__device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+  WaveReduceStep<V, 32>::run(v, threadIdx.x & (kWave - 1));
+  return v[0];
+}
+__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
 // Cross-workgroup hand-off without a device-wide cache write-back.  A producer
 // writes the data it hands over with agent-scope atomic stores (written through to
 // the coherence point), waits for them to complete and then bumps a ticket with a

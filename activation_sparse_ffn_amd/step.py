@@ -62,3 +62,63 @@ class TamState:
     def update(self, union_bits: torch.Tensor, lam: float, eps: float, stream=None):
         A.sfx_tam_update(union_bits, lam, eps, self.K, self.score, self.hot, self.entered, self.left,
                          self.topk, self.topk_count, stream=stream)
+
+
+class StackStep:
+    """All layers of a stack run by the fused multi-layer kernel (one launch per
+    step).  Each layer keeps its own output buffers.  `descriptors(inputs)` builds
+    the device descriptor array for a list of per-layer token tensors [B][d]; a
+    step is `run(descs)`."""
+
+    def __init__(self, layers, d: int, f: int, h: int, B: int, wdtype: str, act: str, device="cuda",
+                 union_bits: torch.Tensor = None):
+        self.d, self.f, self.h, self.B, self.act = d, f, h, B, act
+        self.wdt = WDT_CODE[wdtype]
+        L = len(layers)
+        W = (f + 31) // 32
+        self.device = torch.device(device)
+        dev = self.device
+        self.union_bits = union_bits if union_bits is not None else torch.zeros(L, W, dtype=torch.int32, device=dev)
+        self.bufs = []
+        self.weights = []
+        for l, layer in enumerate(layers):
+            g = layer.get if isinstance(layer, dict) else (lambda k, _ly=layer: getattr(_ly, k, None))
+            self.bufs.append({"scores": torch.empty(B, f, dtype=torch.float32, device=dev),
+                              "tok_bits": torch.zeros(B, W, dtype=torch.int32, device=dev),
+                              "union_bits": self.union_bits[l],
+                              "idx": torch.zeros(f, dtype=torch.int32, device=dev),
+                              "count": torch.zeros(1, dtype=torch.int32, device=dev),
+                              "hact": torch.zeros(f, B, dtype=torch.float32, device=dev),
+                              "y": torch.empty(B, d, dtype=torch.float32, device=dev)})
+            self.weights.append({"W1": g("W1"), "W2": g("W2"), "Wa": g("Wa"), "ba": g("ba"), "Wl": g("Wl"),
+                                 "Wd": g("Wd"), "threshold": float(g("threshold"))})
+        n = A.sfx_ffn_step_ws(self.wdt, A.ACTS[act], B, d, h, f)
+        if n == 0:
+            raise A.SfxError(-7, "sfx_ffn_step_ws")
+        self.ws = A.workspace(n, dev)
+
+    @staticmethod
+    def supported(d: int, f: int, h: int, B: int, wdtype: str, act: str) -> bool:
+        if wdtype not in ("f16", "bf16"):
+            return False
+        return A.sfx_ffn_step_ws(WDT_CODE[wdtype], A.ACTS[act], B, d, h, f) > 0
+
+    def descriptors(self, inputs, tok_bits: bool = True) -> torch.Tensor:
+        entries = []
+        for b, wt, x in zip(self.bufs, self.weights, inputs):
+            e = dict(b)
+            if not tok_bits:
+                e["tok_bits"] = None
+            e.update(wt)
+            e["x"] = x
+            entries.append(e)
+        return A.layer_descriptors(entries, self.device)
+
+    def run(self, descs: torch.Tensor, stream=None):
+        A.sfx_ffn_step(self.wdt, self.act, self.B, self.d, self.h, self.f, descs, self.ws, stream=stream)
+
+    def counts(self) -> torch.Tensor:
+        return torch.cat([b["count"] for b in self.bufs])
+
+    def error_word(self) -> int:
+        return int(self.ws[:4].view(torch.int32).item())

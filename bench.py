@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=32)
     p.add_argument("--tam-lambda", type=float, default=0.9)
     p.add_argument("--tam-eps", type=float, default=0.01)
+    p.add_argument("--separate", action="store_true", help="time the five separate calls per layer")
     return p.parse_args()
 
 
@@ -94,7 +95,7 @@ def main():
 
     import torch
     import synthetic as S
-    from activation_sparse_ffn_amd import StepBuffers, TamState, run_layer
+    from activation_sparse_ffn_amd import StackStep, StepBuffers, TamState, run_layer
     from activation_sparse_ffn_amd import _abi as A
 
     A.load()
@@ -111,20 +112,42 @@ def main():
     layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
     xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
     ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
-    buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
     tam = TamState(L, G, tam_k, device=dev)
     tensors = [ly.tensors() for ly in layers]
+    fused = (not args.separate) and StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
 
-    def step(s):
-        for l in range(L):
-            buf.union_bits = ubits[l]
-            run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
-        tam.update(ubits, args.tam_lambda, args.tam_eps)
+    if fused:
+        st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ubits)
+        descs = [st.descriptors([xs[l][s] for l in range(L)], tok_bits=False) for s in range(W + K)]
+
+        def step(s):
+            st.run(descs[s])
+            tam.update(ubits, args.tam_lambda, args.tam_eps)
+
+        def counts_of(s):
+            st.run(descs[s])
+            return st.counts().cpu().numpy()
+    else:
+        buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
+
+        def step(s):
+            for l in range(L):
+                buf.union_bits = ubits[l]
+                run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
+            tam.update(ubits, args.tam_lambda, args.tam_eps)
+
+        def counts_of(s):
+            cs = []
+            for l in range(L):
+                buf.union_bits = ubits[l]
+                run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
+                cs.append(buf.count.clone())
+            return torch.cat(cs).cpu().numpy()
 
     # eager pass (loads code objects), then capture the warmup and timed steps
     step(0)
     torch.cuda.synchronize()
-    print("[bench] capturing graphs", file=sys.stderr, flush=True)
+    print(f"[bench] {'fused' if fused else 'separate-call'} path; capturing graphs", file=sys.stderr, flush=True)
     g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_warm):
         for s in range(W):
@@ -145,40 +168,52 @@ def main():
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / K
     print(f"[bench] timed {K} steps: {ms_total:.3f} ms", file=sys.stderr, flush=True)
+    if fused:
+        assert st.error_word() == 0, "grid barrier timed out"
 
     # Active counts of the timed steps (deterministic: an eager re-run of the same steps).
     counts = np.zeros((K, L), dtype=np.int64)
     for i, s in enumerate(range(W, W + K)):
-        cs = []
-        for l in range(L):
-            buf.union_bits = ubits[l]
-            run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
-            cs.append(buf.count.clone())
-        counts[i] = torch.cat(cs).cpu().numpy()
+        counts[i] = counts_of(s)
     kb = [kernel_bytes(cfg, B, int(k)) for k in counts.reshape(-1)]
     tam_bytes = L * G * 16
     step_bytes = sum(sum(v.values()) for v in kb) / K + tam_bytes
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # Dominant kernel: the predictor (largest byte share).  Per-launch durations from
-    # HIP events bracketing each sfx_predict on the launch stream; all launches are
-    # queued behind a spin kernel so the events time the GPU, not the host.
+    # Dominant kernel: per-launch durations from HIP events bracketing each launch on
+    # the launch stream; every launch is queued behind a spin kernel so the events
+    # time the GPU, not the host.  Fused path: the whole-stack kernel (all layers'
+    # bytes per launch).  Separate path: sfx_predict (the largest byte share).
     R = min(args.roofline_steps, K)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))
-    i = 0
-    for s in range(W, W + R):
-        for l in range(L):
-            t = tensors[l]
+    if fused:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+        torch.cuda._sleep(int(2e8))
+        for i, s in enumerate(range(W, W + R)):
             evs[i][0].record()
-            A.sfx_predict(xs[l][s], t["W1"], t["W2"], buf.scores, buf.ws_pred)
+            st.run(descs[s])
             evs[i][1].record()
-            i += 1
-    torch.cuda.synchronize()
-    dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    pred_bytes = kernel_bytes(cfg, B, 0)["predict"]
-    pred_gbps = pred_bytes / (dur_ms.mean() * 1e-3) / 1e9
+        torch.cuda.synchronize()
+        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        per_launch = [sum(sum(kernel_bytes(cfg, B, int(k)).values()) for k in counts[i]) for i in range(R)]
+        dom_bytes = float(np.mean(per_launch))
+        dom_name = "sfx_ffn_step (k_step, all layers of one decode step)"
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
+        torch.cuda._sleep(int(2e8))
+        i = 0
+        for s in range(W, W + R):
+            for l in range(L):
+                t = tensors[l]
+                evs[i][0].record()
+                A.sfx_predict(xs[l][s], t["W1"], t["W2"], buf.scores, buf.ws_pred)
+                evs[i][1].record()
+                i += 1
+        torch.cuda.synchronize()
+        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        dom_bytes = float(kernel_bytes(cfg, B, 0)["predict"])
+        dom_name = "sfx_predict (k_pred_hidden + k_pred_scores)"
+    dom_gbps = dom_bytes / (dur_ms.mean() * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -201,10 +236,11 @@ def main():
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "mean_active": round(float(counts.mean()), 1),
         "bytes_per_layer_step": round(step_bytes / L, 0),
-        "roofline": {"bound": "hbm", "kernel": "sfx_predict", "achieved": round(pred_gbps, 1),
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(pred_gbps / PEAK_HBM_GBPS, 4),
+        "path": "fused" if fused else "separate",
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": None, "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
-                     "bytes_per_launch": pred_bytes, "launches": int(dur_ms.size)},
+                     "bytes_per_launch": round(dom_bytes), "launches": int(dur_ms.size)},
     }
 
     if not args.no_cpu_baseline:

@@ -196,6 +196,54 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
                    uint32_t* left_bits, int32_t* topk, int32_t* topk_count,
                    void* ws, size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------------
+ * sfx_ffn_step -- the whole step for L layers in one launch: for each layer in order,
+ * exactly what sfx_predict, sfx_compact, sfx_sparse_up and sfx_sparse_down compute
+ * (same outputs, same layouts), with each layer's y complete before the next
+ * layer's input is read.  Same passages as those four calls.
+ *
+ * One persistent workgroup per compute unit; phases are separated by grid
+ * barriers in the workspace, so the grid must be resident on the device (nothing
+ * else running on it).  A barrier that does not complete within its bound sets
+ * word 0 of the workspace nonzero instead of hanging, and the outputs of that call
+ * are then undefined.
+ *
+ *   wdt      SFX_F16 or SFX_BF16 (x, predictor and FFN rows).  act: ReLU / ReGLU.
+ *   B        1..4.   d <= 4096, d and h multiples of 8, f <= 32768.
+ *   L        number of layers; `layers` is a DEVICE array of L descriptors
+ *            (caller-owned, unchanged until the kernel ends).  Each layer's idx
+ *            holds at least f entries; tok_bits may be NULL; ba may be NULL.
+ *   ws       >= sfx_ffn_step_ws(wdt, act, B, d, h, f) bytes, zero-filled before
+ *            its first use, used on one device only.
+ * Returns SFX_E_UNSUPPORTED for shapes the fused kernel is not built for; the
+ * separate calls cover those.
+ * ------------------------------------------------------------------------------- */
+typedef struct sfx_layer {
+  const void* x;            /* [B][d] */
+  const void* W1;           /* [h][d] */
+  const void* W2;           /* [f][h] */
+  const void* Wa;           /* [f][d] */
+  const void* Wa_scales;    /* reserved, NULL */
+  const float* ba;          /* [f] or NULL */
+  const void* Wl;           /* [f][d] ReGLU linear branch, else NULL */
+  const void* Wl_scales;    /* reserved, NULL */
+  const void* Wd;           /* [f][d] neuron-major */
+  const void* Wd_scales;    /* reserved, NULL */
+  float threshold;
+  int32_t reserved;
+  float* scores;            /* [B][f] */
+  uint32_t* tok_bits;       /* [B][ceil(f/32)] or NULL */
+  uint32_t* union_bits;     /* [ceil(f/32)] */
+  int32_t* idx;             /* [>= f] */
+  int32_t* count;           /* device scalar */
+  float* hact;              /* [>= f][B] */
+  float* y;                 /* [B][d] */
+} sfx_layer;
+
+size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f);
+int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int L,
+                 const sfx_layer* layers, void* ws, size_t ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

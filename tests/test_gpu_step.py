@@ -1,0 +1,125 @@
+"""GPU parity of the fused multi-layer step (sfx_ffn_step): every layer's outputs
+against the fp64 oracle with the same bar as the separate calls, the barrier error
+word stays zero, results are bitwise reproducible, and graph replays match eager
+runs."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from activation_sparse_ffn_amd import StackStep
+from gpu_helpers import check_step, layer_np, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SMALL = {
+    "C2s": S.scaled(S.CONFIGS["C2"], name="C2f", d=1032, f=3000, h=136),
+    "C3s": S.scaled(S.CONFIGS["C3"], name="C3f", d=1032, f=2080, h=136),
+    "C2m": S.scaled(S.CONFIGS["C2"], name="C2m", d=2048, f=8192, h=512),
+}
+
+
+def _outputs(st: StackStep, l: int):
+    b = st.bufs[l]
+    k = int(b["count"].item())
+    return {"scores": b["scores"].cpu().numpy(), "tok_bits": b["tok_bits"].cpu().numpy().view(np.uint32),
+            "union_bits": b["union_bits"].cpu().numpy().view(np.uint32), "idx": b["idx"][:k].cpu().numpy(),
+            "count": k, "hact": b["hact"][:k].cpu().numpy(), "y": b["y"].cpu().numpy()}
+
+
+def _run_and_check(cfg, L, B, steps, layers=None):
+    layers = layers or [S.make_layer(cfg, l, device=DEV) for l in range(L)]
+    lnp = [layer_np(ly) for ly in layers]
+    xs = [S.make_tokens(cfg, l, steps, B, device=DEV) for l in range(L)]
+    assert StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+    st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+    for s in range(steps):
+        descs = st.descriptors([xs[l][s] for l in range(L)], tok_bits=(s % 2 == 0))
+        say(f"fused {cfg.name} L={L} B={B} step {s}")
+        st.run(descs)
+        torch.cuda.synchronize()
+        assert st.error_word() == 0
+        for l in range(L):
+            out = _outputs(st, l)
+            if s % 2 == 1:                     # tok_bits not requested this step: keep the last ones out
+                out["tok_bits"] = None
+            r = check_step(cfg, lnp[l], S.storage_numpy(xs[l][s]), out, layers[l].threshold)
+            if l == 0:
+                say("   ", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in r.items()})
+    return st
+
+
+@pytest.mark.parametrize("name,B", [("C2s", 1), ("C2s", 3), ("C3s", 1), ("C3s", 2), ("C3s", 4), ("C2m", 1)])
+def test_fused_scaled(name, B):
+    _run_and_check(SMALL[name], 3, B, 3)
+
+
+@pytest.mark.parametrize("name,B", [("C2", 1), ("C3", 1), ("C3", 4)])
+def test_fused_full_size(name, B):
+    cfg = S.CONFIGS[name]
+    _run_and_check(cfg, 2, B, 2)
+    torch.cuda.empty_cache()
+
+
+def test_fused_threshold_extremes():
+    """+inf: nothing active in any layer, y = 0; -inf: every neuron active."""
+    cfg = SMALL["C2s"]
+    layers = [S.make_layer(cfg, l, device=DEV) for l in range(2)]
+    x = [S.make_tokens(cfg, l, 1, 1, device=DEV)[0].clone() for l in range(2)]
+    for t in (float("inf"), float("-inf")):
+        for ly in layers:
+            ly.threshold = t
+        st = StackStep(layers, cfg.d, cfg.f, cfg.h, 1, cfg.wdtype, cfg.act)
+        say(f"fused threshold {t}")
+        st.run(st.descriptors(x))
+        torch.cuda.synchronize()
+        assert st.error_word() == 0
+        for l in range(2):
+            out = _outputs(st, l)
+            if t > 0:
+                assert out["count"] == 0 and not out["y"].any()
+            else:
+                assert out["count"] == cfg.f and np.array_equal(out["idx"], np.arange(cfg.f))
+                check_step(cfg, layer_np(layers[l]), S.storage_numpy(x[l]), out, t)
+
+
+def test_fused_determinism_and_graph_replay():
+    cfg = SMALL["C3s"]
+    L, B = 3, 2
+    layers = [S.make_layer(cfg, l, device=DEV) for l in range(L)]
+    xs = [S.make_tokens(cfg, l, 3, B, device=DEV) for l in range(L)]
+    inputs = [xs[l][0].clone() for l in range(L)]
+    st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+    static = st.descriptors(inputs)
+    eager = []
+    for s in range(3):
+        for l in range(L):
+            inputs[l].copy_(xs[l][s])
+        st.run(static)
+        torch.cuda.synchronize()
+        eager.append([_outputs(st, l) for l in range(L)])
+    # same inputs again: bitwise identical
+    for l in range(L):
+        inputs[l].copy_(xs[l][2])
+    st.run(static)
+    torch.cuda.synchronize()
+    for l in range(L):
+        o = _outputs(st, l)
+        for key in ("scores", "union_bits", "idx", "hact", "y"):
+            assert np.array_equal(o[key], eager[2][l][key]), key
+    say("fused graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run(static)
+    for s in range(3):
+        for l in range(L):
+            inputs[l].copy_(xs[l][s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert st.error_word() == 0
+        for l in range(L):
+            o = _outputs(st, l)
+            for key in ("idx", "hact", "y"):
+                assert np.array_equal(o[key], eager[s][l][key]), (s, l, key)
+        _ = torch.randn(1000, device=DEV).sum().item()
