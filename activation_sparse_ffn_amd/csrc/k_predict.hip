@@ -6,15 +6,15 @@
 // read once and feeds B multiply-adds.  Layer 1 gives one wave per hidden row;
 // layer 2 gives each wave R rows of W2, so a lane keeps R 16-byte loads in flight
 // per chunk.  The hidden vector is kept in fp32 (workspace), never rounded to the
-// weight type.  From B = 16 on, layer 2 is a dense contraction and runs on the
-// matrix cores (k_predict_mfma.hip).
+// weight type.  From B = 16 on (fp16 / bf16) both layers are dense contractions
+// and run on the matrix cores (k_predict_mfma.hip).
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 
 namespace sfx {
 
-hipError_t launch_pred_scores_mfma(hipStream_t s, int wdt, int B, int h, int f, const void* W2,
-                                   const float* hid, float* scores);
+hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
+                            const void* W2, float* hid, float* scores);
 bool pred_mfma_eligible(int wdt, int B, int h, int f);
 
 namespace {
@@ -137,10 +137,10 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const uint8_t* __restric
 template <class T, int NB>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
                const void* W2, float* scores, float* hid, bool mfma, int wdt) {
+  if (mfma) return launch_pred_mfma(s, wdt, B, d, h, f, x, W1, W2, hid, scores);
   dim3 blk(kBlock);
   k_pred_hidden<T, NB><<<dim3((h + kWavesPerBlock - 1) / kWavesPerBlock), blk, 0, s>>>(
       (const uint8_t*)x, (const uint8_t*)W1, hid, B, d, h);
-  if (mfma) return launch_pred_scores_mfma(s, wdt, B, h, f, W2, hid, scores);
   constexpr int R = NB == 1 ? 4 : NB == 2 ? 2 : 1;
   const int rows_per_block = kWavesPerBlock * R;
   k_pred_scores<T, NB, R><<<dim3((f + rows_per_block - 1) / rows_per_block), blk, 0, s>>>(

@@ -106,6 +106,22 @@ def test_full_size_layer(name, B):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,B", [("C3s", 16), ("C3s", 32), ("C2s", 17), ("C2s", 64), ("C3s", 64)])
+def test_matrix_core_predictor(name, B):
+    """B >= 16 runs both predictor layers on the matrix cores (hidden split into
+    exact 16-bit pieces): scores must still sit within 1e-5 of fp64."""
+    cfg = SCALED[name]
+    L = S.make_layer(cfg, 0, device=DEV)
+    Lnp = layer_np(L)
+    xs = _tokens(cfg, 0, 2, B)
+    buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype)
+    for step in range(2):
+        say(f"matrix-core predictor {name} B={B} step {step}")
+        out, _ = gpu_layer_step(cfg, L, xs[step], buf=buf)
+        r = check_step(cfg, Lnp, S.storage_numpy(xs[step]), out, L.threshold)
+        say("   ", {k: (round(v, 9) if isinstance(v, float) else v) for k, v in r.items()})
+
+
 def test_threshold_extremes():
     """+inf: nothing active, y = 0.  -inf: every neuron active, y = the dense layer."""
     cfg = SCALED["C2s"]
