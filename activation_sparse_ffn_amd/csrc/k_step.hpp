@@ -3,28 +3,31 @@
 // predictor, hybrid-execution pseudocode, neuron-aware operators; KAIROX page, Core
 // method, item 3: neurons stored in contiguous groups of 32).
 //
-// One workgroup of 512 threads per compute unit, all resident; phases are separated
-// by grid barriers (per-workgroup arrival flags polled by workgroup 0, which then
-// releases a `go` word; every wait is bounded and sets an error word instead of
-// hanging).  Data one workgroup hands to another (hidden, union words, idx, hact)
-// is written with agent-scope atomic stores and read with agent-scope atomic loads,
-// so no barrier needs a cache write-back.  Per layer:
+// One workgroup of 512 threads per compute unit, all resident.  Inside a layer,
+// data one workgroup hands to others (hidden values, union mask words, hact) is
+// written as 64-bit words {layer tag, value} with one agent-scope atomic store each;
+// readers poll those words with agent-scope atomic loads until the tag of the
+// current layer shows up.  So a hand-off costs one store and one poll, with no
+// store-completion wait and no grid barrier.  Between layers a grid barrier
+// (arrival flags polled by workgroup 0, which then releases a `go` word) makes the
+// layer's y complete before the next layer's input is read.  Every wait is bounded
+// and sets an error word instead of hanging.  Per layer:
 //
 //   A  hidden rows owned round-robin (row r -> workgroup r mod P), W1 chunks and x
-//      in registers, fp32 dot products, relu.  Meanwhile the workgroup's W2 rows
-//      (mask words g = w, w + P, ...: 32 rows each) stream straight into LDS with
-//      16-byte global->LDS loads.                                          barrier
-//   B  scores of the owned rows from LDS (or from HBM when the rows do not fit),
-//      threshold, per-token and union mask words.                          barrier
-//   C  every workgroup scans the union popcounts (the list itself lands in LDS);
+//      in registers, fp32 dot products, relu, tagged hidden out.  Then the
+//      workgroup's W2 rows (mask words g = w, w + P, ...: 32 rows each) stream
+//      straight into LDS with 16-byte global->LDS loads.
+//   B  poll the hidden, scores of the owned rows from LDS (or from HBM when the rows
+//      do not fit), threshold, per-token and union mask words (union tagged out).
+//   C  poll the union words, scan their popcounts (the active list lands in LDS);
 //      workgroup w takes active ranks [w k / P, (w+1) k / P) -- an even split of
 //      the work whatever the mask looks like -- writes idx, gathers its up (and
-//      gate) rows, applies bias and ReLU / ReGLU and hands hact over.       barrier
+//      gate) rows, applies bias and ReLU / ReGLU, tagged hact out.
 //   D  down by column tiles: workgroup w owns d/P columns (rounded to 8) of y and
-//      reads that segment of every active row, so y needs no partial sums and no
-//      atomics; the reduction order is fixed, so y is bitwise reproducible.
-//      Tiles are mapped so workgroups sharing a 128-byte line of Wd run on one XCD.
-//                                                                           barrier
+//      reads that segment of every active row (polling each row's hact), so y
+//      needs no partial sums and no atomics; the reduction order is fixed, so y is
+//      bitwise reproducible.  Tiles are mapped so workgroups sharing a 128-byte
+//      line of Wd run on one XCD.                                grid barrier
 #pragma once
 #include "sfx_common.hpp"
 #include "sfx_step.hpp"
@@ -40,30 +43,52 @@ constexpr int kRedFloats = 1024;         // reduction scratch
 constexpr int kXBytes = kLds - kW2Bytes - kRedFloats * 4 - 768;
 constexpr int kMaxWords = 1024;          // f <= 32768
 constexpr int kPrefBytes = (kMaxWords + 8) * 4;
-constexpr int kNidCap = (kXBytes - kPrefBytes) / 4;
+constexpr int kUwBytes = kMaxWords * 4;
+constexpr int kNidCap = (kXBytes - kPrefBytes - kUwBytes) / 4;
 constexpr int kSpin = 1 << 20;
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_agent(const float* p) {
+__device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_tagged(unsigned long long* p, uint32_t tag, uint32_t bits) {
+  __hip_atomic_store(p, ((unsigned long long)tag << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ bool tag_ok(unsigned long long v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
+
+// Poll N tagged words (entries i < n, addresses addr(i)) until all carry `tag`.
+// Loads are issued as one batch, then only stale entries are reloaded.  Bounded:
+// on timeout (or when another workgroup already failed) the error word is set and
+// whatever was read is returned.
+template <int N, class Addr>
+__device__ __forceinline__ void poll_tagged(unsigned long long (&v)[N], int n, Addr addr, uint32_t tag,
+                                            uint32_t* err) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < n) v[i] = ld_agent64(addr(i));
+  for (int spins = 0;; ++spins) {
+    bool stale = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= (i < n) && !tag_ok(v[i], tag);
+    if (!stale) return;
+    if (spins > kSpin || ((spins & 255) == 255 && ld_agent(err) != 0u)) {
+      store_through(err, 3u);
+      return;
+    }
+    // back off: thousands of waves re-reading uncached words would otherwise
+    // crowd out the loads that do the work
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (i < n && !tag_ok(v[i], tag)) v[i] = ld_agent64(addr(i));
+  }
 }
 
-// Grid barrier.  Threads that wrote handed-over data must have waited for those
-// stores (wait_memory) before calling; thread 0 then raises the workgroup's flag
-// to `target`.  Readers fetch handed-over data with agent-scope atomic loads issued
-// in batches (no cache invalidation: a per-workgroup agent acquire is serialised
-// across the device).  Workgroup 0 polls all flags and
-// raises `go`; the others poll `go`.  Bounded: on timeout the error word is set and
-// the workgroup continues, and once the error word is set no later barrier waits
-// (outputs are then undefined; nothing hangs).
+// Grid barrier between layers.  Thread 0 raises the workgroup's flag to `target`;
+// workgroup 0 polls all flags and raises `go`; the others poll `go`.  Bounded:
+// on timeout the error word is set, and once it is set no later wait spins.
 __device__ __forceinline__ void grid_barrier(const StepParams& p, uint32_t target) {
   __syncthreads();
   if (threadIdx.x == 0) store_through(p.flags + blockIdx.x, target);
@@ -84,6 +109,7 @@ __device__ __forceinline__ void grid_barrier(const StepParams& p, uint32_t targe
   } else if (threadIdx.x == 0) {
     int spins = 0;
     while ((int)(ld_agent(p.go) - target) < 0) {
+      __builtin_amdgcn_s_sleep(1);
       if (ld_agent(p.err) != 0u) break;
       if (++spins > kSpin) {
         store_through(p.err, 2u);
@@ -118,22 +144,35 @@ __device__ __forceinline__ bool reduce_owner(int lane) { return (lane & ((kWave 
 template <int V>
 __device__ __forceinline__ int reduce_index(int lane) { return lane >> (6 - ilog2c(V)); }
 
-// T: TF16 or TBF16.  NB: token class.  DL: 1 for d <= 4096, 2 for d <= 8192.
+// Neuron of active rank r from the union words and their prefix (both in LDS).
+__device__ __forceinline__ int rank_to_neuron(int r, const uint32_t* s_pref, const uint32_t* s_uw, int W) {
+  int lo = 0, hi = W;                   // s_pref[lo] <= r < s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int)s_pref[mid] <= r) lo = mid; else hi = mid;
+  }
+  uint32_t wd = s_uw[lo];
+  for (int s = r - (int)s_pref[lo]; s > 0; --s) wd &= wd - 1;
+  return 32 * lo + __builtin_ctz(wd);
+}
+
+// T: TF16 or TBF16.  NB: token class (1, 2, 4).  DL: 1 for d <= 4096.
 template <class T, int NB, bool REGLU, int DL>
 __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int kU = 8 * DL;              // 16-byte chunks per lane of a d-row
   constexpr int TB = NB < 4 ? NB : 4;     // tokens per pass in phase B
   constexpr int kUP = (REGLU || NB >= 4) ? 4 : kU;   // up-row chunks per lane loaded together
-  constexpr int kRD = NB >= 4 ? 8 : 16;   // down rows per lane loaded together
+  constexpr int kRD = 8 / NB;             // down rows per lane loaded together
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
   __shared__ uint32_t s_words[64];
   __shared__ uint32_t s_wt[kNW];
   uint32_t* s_pref = reinterpret_cast<uint32_t*>(s_x);
-  int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes);
+  uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
+  int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
 
-  uint32_t epoch = ld_agent(p.flags + blockIdx.x);
+  const uint32_t e0 = ld_agent(p.flags + blockIdx.x);
   for (int l = 0; l < p.L; ++l) {
     // Re-derived per layer behind opaque copies, so per-thread offsets are not
     // hoisted out of the layer loop (that would keep every phase's values live).
@@ -148,6 +187,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     const int nch1 = d / 8;        // 16-byte chunks per W1 / Wa / Wd row
     const int nch2 = h / 8;        // 16-byte chunks per W2 row
     const size_t rb1 = (size_t)d * 2, rb2 = (size_t)h * 2;
+    const uint32_t tag = e0 + (uint32_t)l + 1u;
 
     // Phase-A geometry: rows w + P s (s < nr1) of W1, wpr waves per row.
     const int nr1 = p.nr1;
@@ -175,16 +215,16 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     const uint8_t* W2 = (const uint8_t*)Ld.W2;
 
     // ---------------------------------------------------------------- phase A
-    Raw<16> w1r[kU];
-    if (a_active) {
-      const uint8_t* row = (const uint8_t*)Ld.W1 + (size_t)a_row * rb1;
-#pragma unroll
-      for (int m = 0; m < kU; ++m) {
-        const int c = a_part * kWave + lane + m * a_stride;
-        if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
-      }
-    }
     {
+      Raw<16> w1r[kU];
+      if (a_active) {
+        const uint8_t* row = (const uint8_t*)Ld.W1 + (size_t)a_row * rb1;
+#pragma unroll
+        for (int m = 0; m < kU; ++m) {
+          const int c = a_part * kWave + lane + m * a_stride;
+          if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
+        }
+      }
       float acc[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] = 0.f;
@@ -211,13 +251,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         if (row < h) {
           float s = 0.f;
           for (int q = 0; q < wpr; ++q) s += s_red[(slot * wpr + q) * NB + b];
-          store_through(p.hid + (size_t)b * h + row, fmaxf(s, 0.f));
+          st_tagged(p.hid + (size_t)b * h + row, tag, __float_as_uint(fmaxf(s, 0.f)));
         }
-        wait_memory();
       }
     }
-    // The W2 rows go to LDS while the grid waits at the barrier (issued after the
-    // hidden stores: memory waits on this GPU count loads and stores in order).
     if (w2_lds) {
       // the owned W2 rows -> LDS, row-major, 16 bytes per lane
       const int items = rows2 * nch2;
@@ -234,30 +271,24 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
     }
-    grid_barrier(p, ++epoch);
 
     // ---------------------------------------------------------------- phase B
-    if (w2_lds) {
-      wait_memory();
-      __syncthreads();
-    }
     {
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
+      if (w2_lds) {
+        wait_memory();                         // this thread's LDS rows have landed
+      }
       for (int b0 = 0; b0 < B; b0 += TB) {
         const int tb = min(TB, B - b0);
+        __syncthreads();                       // previous use of s_hid / s_w2 done
         for (int i0 = tid; i0 < tb * h; i0 += 8 * kNT) {
-          float hvv[8];
+          unsigned long long hw[8];
+          const int n = min(8, (tb * h - i0 + kNT - 1) / kNT);
+          poll_tagged<8>(hw, n, [&](int u) { return p.hid + (size_t)b0 * h + i0 + u * kNT; }, tag, p.err);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kNT;
-            hvv[u] = i < tb * h ? ld_agent(p.hid + (size_t)b0 * h + i) : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kNT;
-            if (i < tb * h) s_hid[i] = hvv[u];
-          }
+          for (int u = 0; u < 8; ++u)
+            if (u < n) s_hid[i0 + u * kNT] = __uint_as_float((uint32_t)hw[u]);
         }
         __syncthreads();
         for (int q0 = wave; q0 < rows2; q0 += kNW * 8) {
@@ -302,39 +333,49 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             if (q < rows2 && b < tb) s_sc[q * NB + b0 + b] = v;
           }
         }
-        __syncthreads();
       }
-      // scores out, mask words
-      for (int i = tid; i < rows2 * B; i += kNT) {
-        const int q = i / B, b = i - q * B;
-        const int row = 32 * (w + P * (q >> 5)) + (q & 31);
-        if (row < f) Ld.scores[(size_t)b * f + row] = s_sc[q * NB + b];
-      }
-      if (tid < nw2 * B) {
-        const int m = tid / B, b = tid - m * B;
+      __syncthreads();
+      // mask words by wave ballots (lane = row of a 64-row pair of words), then the
+      // union goes out tagged, then the scores
+      for (int m0 = 2 * wave; m0 < nw2; m0 += 2 * kNW) {
+        const int m = m0 + (lane >> 5);
         const int g = w + P * m;
-        uint32_t word = 0;
-        for (int i = 0; i < 32; ++i) {
-          const int row = 32 * g + i;
-          if (row < f && s_sc[(32 * m + i) * NB + b] >= Ld.threshold) word |= 1u << i;
+        const int row = 32 * g + (lane & 31);
+        const bool in = m < nw2 && row < f;
+        const float thr = Ld.threshold;
+        for (int b = 0; b < B; ++b) {
+          const uint64_t bal = __ballot(in && s_sc[(32 * m + (lane & 31)) * NB + b] >= thr);
+          if ((lane & 31) == 0 && m < nw2) {
+            const uint32_t word = (uint32_t)(lane == 0 ? bal : (bal >> 32));
+            if (Ld.tok_bits != nullptr) Ld.tok_bits[(size_t)b * W + g] = word;
+            s_words[m * NB + b] = word;
+          }
         }
-        if (Ld.tok_bits != nullptr) Ld.tok_bits[(size_t)b * W + g] = word;
-        s_words[m * NB + b] = word;
       }
       __syncthreads();
       if (tid < nw2) {
         uint32_t u = 0;
         for (int b = 0; b < B; ++b) u |= s_words[tid * NB + b];
-        store_through(Ld.union_bits + w + P * tid, u);
-        wait_memory();
+        const int g = w + P * tid;
+        st_tagged(p.uni + g, tag, u);
+        Ld.union_bits[g] = u;
+      }
+      for (int i = tid; i < rows2 * B; i += kNT) {
+        const int q = i / B, b = i - q * B;
+        const int row = 32 * (w + P * (q >> 5)) + (q & 31);
+        if (row < f) Ld.scores[(size_t)b * f + row] = s_sc[q * NB + b];
       }
     }
-    grid_barrier(p, ++epoch);
 
     // ---------------------------------------------------------------- phase C
-    uint32_t w0 = 0, w1 = 0;
-    if (2 * tid < W) w0 = ld_agent(Ld.union_bits + 2 * tid);
-    if (2 * tid + 1 < W) w1 = ld_agent(Ld.union_bits + 2 * tid + 1);
+    unsigned long long uw[2];
+    {
+      const int base2 = 2 * tid;
+      const int n = base2 + 1 < W ? 2 : (base2 < W ? 1 : 0);
+      poll_tagged<2>(uw, n, [&](int u) { return p.uni + base2 + u; }, tag, p.err);
+    }
+    const uint32_t w0 = 2 * tid < W ? (uint32_t)uw[0] : 0u;
+    const uint32_t w1 = 2 * tid + 1 < W ? (uint32_t)uw[1] : 0u;
     const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
     uint32_t inc = cnt;
 #pragma unroll
@@ -352,8 +393,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       total += t;
     }
     const uint32_t base = before + inc - cnt;
-    if (2 * tid < W) s_pref[2 * tid] = base;
-    if (2 * tid + 1 < W) s_pref[2 * tid + 1] = base + cnt0;
+    if (2 * tid < W) { s_pref[2 * tid] = base; s_uw[2 * tid] = w0; }
+    if (2 * tid + 1 < W) { s_pref[2 * tid + 1] = base + cnt0; s_uw[2 * tid + 1] = w1; }
     if (tid == 0) s_pref[W] = total;
     const int k = (int)total;
     const bool in_lds = k <= kNidCap;
@@ -371,20 +412,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const int r0 = (int)(((long long)k * w) / P);
       const int r1 = (int)(((long long)k * (w + 1)) / P);
       for (int r = r0 + wave; r < r1; r += kNW) {
-        int nid;
-        if (in_lds) {
-          nid = s_nid[r];
-        } else {
-          int lo = 0, hi = W;                 // s_pref[lo] <= r < s_pref[hi]
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((int)s_pref[mid] <= r) lo = mid; else hi = mid;
-          }
-          uint32_t wd = ld_agent(Ld.union_bits + lo);
-          for (int s = r - (int)s_pref[lo]; s > 0; --s) wd &= wd - 1;
-          nid = 32 * lo + __builtin_ctz(wd);
-        }
-        if (lane == 0) st_agent(Ld.idx + r, nid);
+        const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
+        if (lane == 0) Ld.idx[r] = nid;
         const uint8_t* ra = (const uint8_t*)Ld.Wa + (size_t)nid * rb1;
         const uint8_t* rl = REGLU ? (const uint8_t*)Ld.Wl + (size_t)nid * rb1 : nullptr;
         float za[NB], zl[NB];
@@ -421,12 +450,13 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         if (REGLU) v *= wave_reduce_multi<NB>(zl);
         if (reduce_owner<NB>(lane)) {
           const int b = reduce_index<NB>(lane);
-          if (b < B) store_through(Ld.hact + (size_t)r * B + b, v);
+          if (b < B) {
+            st_tagged(p.hact + (size_t)r * B + b, tag, __float_as_uint(v));
+            Ld.hact[(size_t)r * B + b] = v;
+          }
         }
       }
     }
-    wait_memory();
-    grid_barrier(p, ++epoch);
 
     // ---------------------------------------------------------------- phase D
     {
@@ -437,27 +467,31 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const uint8_t* Wd = (const uint8_t*)Ld.Wd;
         for (int rb = d_rr; rb < k; rb += d_rs * kRD) {
           Raw<16> wv[kRD];
-          float hv[kRD][NB];
 #pragma unroll
           for (int u = 0; u < kRD; ++u) {
             const int r = rb + u * d_rs;
             if (r < k) {
-              const int nid = in_lds ? s_nid[r] : ld_agent(Ld.idx + r);
+              const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
               wv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
-#pragma unroll
-              for (int b = 0; b < NB; ++b) hv[u][b] = b < B ? ld_agent(Ld.hact + (size_t)r * B + b) : 0.f;
             }
           }
+          unsigned long long hv[kRD * NB];
+          const int nrow = min(kRD, (k - rb + d_rs - 1) / d_rs);
+          poll_tagged<kRD * NB>(hv, nrow * B,
+                                [&](int i) { return p.hact + (size_t)(rb + (i / B) * d_rs) * B + (i % B); }, tag,
+                                p.err);
 #pragma unroll
           for (int u = 0; u < kRD; ++u) {
-            const int r = rb + u * d_rs;
-            if (r < k) {
+            if (u < nrow) {
               float wf[8];
               unpack<T, 4>(wv[u].w, wf);
 #pragma unroll
               for (int b = 0; b < NB; ++b)
+                if (b < B) {
+                  const float hvf = __uint_as_float((uint32_t)hv[u * B + b]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) yacc[b * 8 + e] = fmaf(hv[u][b], wf[e], yacc[b * 8 + e]);
+                  for (int e = 0; e < 8; ++e) yacc[b * 8 + e] = fmaf(hvf, wf[e], yacc[b * 8 + e]);
+                }
             }
           }
         }
@@ -477,8 +511,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
     }
-    if (l + 1 < p.L) grid_barrier(p, ++epoch);
+    if (l + 1 < p.L) grid_barrier(p, e0 + (uint32_t)l + 1u);
   }
+  // Every workgroup ends with its flag at e0 + L, so all flags agree at the next call.
+  if (threadIdx.x == 0) store_through(p.flags + blockIdx.x, e0 + (uint32_t)p.L);
 }
 
 template <class T, int NB, int DL>

@@ -48,10 +48,14 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   return g;
 }
 
-size_t step_ws_bytes(int B, int h, int P) {
-  const size_t flags = ((size_t)P * 4 + 255) & ~(size_t)255;
-  const size_t hid = ((size_t)B * h * 4 + 255) & ~(size_t)255;
-  return 256 + flags + hid;
+namespace {
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+}  // namespace
+
+// control line | flags [P] | hidden [B][h] | union [W] | hact [f][B]  (tagged words: 8 bytes)
+size_t step_ws_bytes(int B, int h, int f, int P) {
+  const size_t W = ((size_t)f + 31) / 32;
+  return 256 + up256((size_t)P * 4) + up256((size_t)B * h * 8) + up256(W * 8) + up256((size_t)f * B * 8);
 }
 
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,
@@ -71,7 +75,12 @@ hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int
   p.err = (uint32_t*)base;
   p.go = (uint32_t*)(base + 128);
   p.flags = (uint32_t*)(base + 256);
-  p.hid = (float*)(base + 256 + (((size_t)g.P * 4 + 255) & ~(size_t)255));
+  size_t off = 256 + up256((size_t)g.P * 4);
+  p.hid = (unsigned long long*)(base + off);
+  off += up256((size_t)B * h * 8);
+  p.uni = (unsigned long long*)(base + off);
+  off += up256((size_t)p.W * 8);
+  p.hact = (unsigned long long*)(base + off);
   if (wdt == DT_F16) return launch_step_f16(s, p, act, g.P, g.dl);
   return launch_step_bf16(s, p, act, g.P, g.dl);
 }

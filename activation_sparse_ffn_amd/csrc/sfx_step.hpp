@@ -16,10 +16,12 @@ struct StepParams {
   int nr1;        // hidden rows per workgroup (ceil(h / P))
   int w2_lds;     // 1: the workgroup's W2 rows are staged in LDS
   int cw;         // columns of y per workgroup in the down phase (8, 16, 32 or 64)
-  uint32_t* err;  // nonzero after a barrier timed out
+  uint32_t* err;               // nonzero after a wait timed out
   uint32_t* go;
-  uint32_t* flags;
-  float* hid;     // [B][h]
+  uint32_t* flags;             // one arrival counter per workgroup
+  unsigned long long* hid;     // [B][h]  {tag, hidden}
+  unsigned long long* uni;     // [W]     {tag, union word}
+  unsigned long long* hact;    // [f][B]  {tag, activation}
 };
 
 struct StepGeom {
@@ -28,7 +30,7 @@ struct StepGeom {
 };
 
 StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P);
-size_t step_ws_bytes(int B, int h, int P);
+size_t step_ws_bytes(int B, int h, int f, int P);
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L,
                        const LayerDesc* layers, void* ws, const StepGeom& g);
 
