@@ -47,6 +47,7 @@ constexpr int kUwBytes = kMaxWords * 4;
 constexpr int kNidCap = (kXBytes - kPrefBytes - kUwBytes) / 4;
 constexpr int kSpin = 1 << 20;
 
+
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -58,66 +59,104 @@ __device__ __forceinline__ void st_tagged(unsigned long long* p, uint32_t tag, u
 }
 __device__ __forceinline__ bool tag_ok(unsigned long long v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
 
-// Poll N tagged words (entries i < n, addresses addr(i)) until all carry `tag`.
-// Loads are issued as one batch, then only stale entries are reloaded.  Bounded:
-// on timeout (or when another workgroup already failed) the error word is set and
-// whatever was read is returned.
-template <int N, class Addr>
-__device__ __forceinline__ void poll_tagged(unsigned long long (&v)[N], int n, Addr addr, uint32_t tag,
-                                            uint32_t* err) {
+// Poll N tagged words (entries i with valid(i), addresses addr(i)) until all carry
+// `tag`.  Loads are issued as one batch, then only stale entries are reloaded.
+// Bounded: on timeout (or when another workgroup already failed) the error word is
+// set and whatever was read is returned.
+template <int N, class Valid, class Addr>
+__device__ __forceinline__ void poll_tagged_if(unsigned long long (&v)[N], Valid valid, Addr addr, uint32_t tag,
+                                               uint32_t* err) {
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    if (i < n) v[i] = ld_agent64(addr(i));
+    if (valid(i)) v[i] = ld_agent64(addr(i));
   for (int spins = 0;; ++spins) {
     bool stale = false;
 #pragma unroll
-    for (int i = 0; i < N; ++i) stale |= (i < n) && !tag_ok(v[i], tag);
+    for (int i = 0; i < N; ++i) stale |= valid(i) && !tag_ok(v[i], tag);
     if (!stale) return;
     if (spins > kSpin || ((spins & 255) == 255 && ld_agent(err) != 0u)) {
       store_through(err, 3u);
       return;
     }
-    // back off: thousands of waves re-reading uncached words would otherwise
-    // crowd out the loads that do the work
+    // back off: many waves re-reading uncached words would otherwise crowd out
+    // the loads that do the work
     __builtin_amdgcn_s_sleep(2);
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      if (i < n && !tag_ok(v[i], tag)) v[i] = ld_agent64(addr(i));
+      if (valid(i) && !tag_ok(v[i], tag)) v[i] = ld_agent64(addr(i));
+  }
+}
+template <int N, class Addr>
+__device__ __forceinline__ void poll_tagged(unsigned long long (&v)[N], int n, Addr addr, uint32_t tag,
+                                            uint32_t* err) {
+  poll_tagged_if<N>(v, [&](int i) { return i < n; }, addr, tag, err);
+}
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also orders LDS
+// writes still in flight from global->LDS loads, so it waits for every one of them;
+// this barrier leaves those streaming (they are waited for explicitly where their
+// data is read).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS accesses are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Hand-off completion flags: one 32-bit word per workgroup and hand-off kind,
+// raised to the layer tag once the workgroup has issued all its tagged words of
+// that kind.  A consumer waits for all P flags with one wave (P/64 coalesced loads
+// per round), then reads the tagged words once; a word that is still stale (its
+// store overtaken by the flag) is simply polled again.  Polling every tagged word
+// from every workgroup instead would load the memory system with re-reads while
+// slower workgroups are still gathering rows.
+constexpr int kMaxP = 256;
+// Flags sit kFS words apart: flags sharing a cache line with many writers become
+// visible to other compute units much later.
+constexpr int kFS = kFlagStride;
+constexpr int kHidBlock = 16;            // tagged hidden words per workgroup: [nr1 <= 4][NB <= 4]
+
+// Layer descriptors are read-only for the whole launch: read them through the
+// constant address space so they come in on scalar loads.
+typedef const LayerDesc __attribute__((address_space(4))) CLayer;
+__device__ __forceinline__ void wait_flags(const uint32_t* fl, int P, uint32_t tag, uint32_t* err, uint32_t code) {
+  constexpr int N = kMaxP / kWave;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));           // keep the flag addresses out of the layer loop
+  const int lane = tid & (kWave - 1);
+  uint32_t v[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = lane + u * kWave;
+    v[u] = i < P ? ld_agent(fl + (size_t)i * kFS) : tag;
+  }
+  for (int spins = 0;; ++spins) {
+    bool stale = false;
+#pragma unroll
+    for (int u = 0; u < N; ++u) stale |= (int)(v[u] - tag) < 0;
+    if (__ballot(stale) == 0) return;
+    if (spins > kSpin || ((spins & 63) == 63 && ld_agent(err) != 0u)) {
+      if (lane == 0) store_through(err, code);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int i = lane + u * kWave;
+      if (i < P && (int)(v[u] - tag) < 0) v[u] = ld_agent(fl + (size_t)i * kFS);
+    }
   }
 }
 
-// Grid barrier between layers.  Thread 0 raises the workgroup's flag to `target`;
-// workgroup 0 polls all flags and raises `go`; the others poll `go`.  Bounded:
-// on timeout the error word is set, and once it is set no later wait spins.
-__device__ __forceinline__ void grid_barrier(const StepParams& p, uint32_t target) {
-  __syncthreads();
-  if (threadIdx.x == 0) store_through(p.flags + blockIdx.x, target);
-  if (blockIdx.x == 0) {
-    int spins = 0;
-    while (true) {
-      int ok = 1;
-      for (int i = threadIdx.x; i < (int)gridDim.x; i += kNT) ok &= ((int)(ld_agent(p.flags + i) - target) >= 0);
-      const int bad = threadIdx.x == 0 && ld_agent(p.err) != 0u;
-      const int all_ok = __syncthreads_and(ok);
-      if (all_ok || __syncthreads_or(bad)) break;
-      if (++spins > kSpin) {
-        if (threadIdx.x == 0) store_through(p.err, 1u);
-        break;
-      }
-    }
-    if (threadIdx.x == 0) store_through(p.go, target);
-  } else if (threadIdx.x == 0) {
-    int spins = 0;
-    while ((int)(ld_agent(p.go) - target) < 0) {
-      __builtin_amdgcn_s_sleep(1);
-      if (ld_agent(p.err) != 0u) break;
-      if (++spins > kSpin) {
-        store_through(p.err, 2u);
-        break;
-      }
+// Lane 0 of each of n waves calls this after issuing its tagged stores; the last
+// one raises the workgroup's flag.
+__device__ __forceinline__ void arrive(uint32_t* s_cnt, uint32_t n, uint32_t* flag, uint32_t tag) {
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    if (atomicAdd(s_cnt, 1u) == n - 1) {
+      *s_cnt = 0u;
+      store_through(flag, tag);
     }
   }
-  __syncthreads();
 }
 
 template <class T>
@@ -156,6 +195,60 @@ __device__ __forceinline__ int rank_to_neuron(int r, const uint32_t* s_pref, con
   return 32 * lo + __builtin_ctz(wd);
 }
 
+// Wave roles.  A wave's loads and stores complete in issue order, so a wave that
+// waits for a flag must have nothing slow in flight ahead of the flag loads:
+//   waves 0..3  W1 rows (registers) and phase A;
+//   waves 4..6  stream the next layer's W2 rows into LDS;
+//   wave 7      the control wave: every wait for other workgroups' flags;
+//   waves 0..6  up rows and down segments.
+constexpr int kAW = 4;                   // waves [0, kAW): W1 rows
+constexpr int kCW = 7;                   // control wave; waves [kAW, kCW) stream W2
+
+// Weights of a layer that do not depend on its input, fetched before the layer
+// starts (behind the previous layer's barrier): the W1 row of each of waves 0..3
+// into registers, and the workgroup's W2 rows (mask words g = w, w + P, ...: 32
+// rows each) straight into LDS with 16-byte global->LDS loads.
+template <int kU>
+__device__ __forceinline__ void prefetch_weights(const StepParams& p, CLayer* Ld, uint8_t* s_w2,
+                                                 Raw<16> (&w1r)[kU]) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int w = blockIdx.x;
+  const int P = gridDim.x;
+  if (wave < kAW) {
+    const int a_row = w + P * wave;
+    if (wave < p.nr1 && a_row < p.h) {
+      const uint8_t* row = (const uint8_t*)Ld->W1 + (size_t)a_row * p.d * 2;
+      const int nch1 = p.d / 8;
+#pragma unroll
+      for (int m = 0; m < kU; ++m) {
+        const int c = lane + m * kWave;
+        if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
+      }
+    }
+  } else if (wave < kCW && p.w2_lds != 0) {
+    const uint8_t* W2 = (const uint8_t*)Ld->W2;
+    const int nch2 = p.h / 8;
+    const size_t rb2 = (size_t)p.h * 2;
+    const int nw2 = w < p.W ? (p.W - w + P - 1) / P : 0;
+    const int items = nw2 * 32 * nch2;
+#pragma unroll 1
+    for (int i0 = (wave - kAW) * kWave; i0 < items; i0 += (kCW - kAW) * kWave) {
+      const int i = i0 + lane;
+      if (i < items) {
+        const int q = i / nch2;
+        const int c = i - q * nch2;
+        int row = 32 * (w + P * (q >> 5)) + (q & 31);
+        if (row >= p.f) row = p.f - 1;       // rows past f are loaded but never used
+        __builtin_amdgcn_global_load_lds((const void*)(W2 + (size_t)row * rb2 + (size_t)c * 16),
+                                         (__attribute__((address_space(3))) void*)(s_w2 + (size_t)i0 * 16), 16, 0, 0);
+      }
+    }
+  }
+}
+
 // T: TF16 or TBF16.  NB: token class (1, 2, 4).  DL: 1 for d <= 4096.
 template <class T, int NB, bool REGLU, int DL>
 __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
@@ -163,6 +256,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int TB = NB < 4 ? NB : 4;     // tokens per pass in phase B
   constexpr int kUP = (REGLU || NB >= 4) ? 4 : kU;   // up-row chunks per lane loaded together
   constexpr int kRD = 8 / NB;             // down rows per lane loaded together
+  constexpr int kRB = TB <= 2 ? 8 : 4;    // score rows per lane per pass
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
@@ -172,7 +266,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
 
-  const uint32_t e0 = ld_agent(p.flags + blockIdx.x);
+  __shared__ uint32_t s_cnt[2];             // arrivals: [1] hact
+  if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0u;
+  lds_barrier();
+  const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
+  Raw<16> w1r[kU];
+  prefetch_weights<kU>(p, (CLayer*)p.layers, s_w2, w1r);
   for (int l = 0; l < p.L; ++l) {
     // Re-derived per layer behind opaque copies, so per-thread offsets are not
     // hoisted out of the layer loop (that would keep every phase's values live).
@@ -189,49 +288,38 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     const size_t rb1 = (size_t)d * 2, rb2 = (size_t)h * 2;
     const uint32_t tag = e0 + (uint32_t)l + 1u;
 
-    // Phase-A geometry: rows w + P s (s < nr1) of W1, wpr waves per row.
+    // Phase-A geometry: row w + P s of W1 in wave s (s < nr1 <= 4).
     const int nr1 = p.nr1;
-    const int wpr = kNW / nr1;
-    const int a_slot = wave / wpr;
-    const int a_part = wave - a_slot * wpr;
-    const int a_row = w + P * a_slot;
-    const bool a_active = a_slot < nr1 && a_row < h;
-    const int a_stride = wpr * kWave;
+    const int a_row = w + P * wave;
+    const bool a_active = wave < nr1 && a_row < h;
     // Phase-B geometry: owned mask words w + P m, m < nw2.
     const int nw2 = w < W ? (W - w + P - 1) / P : 0;
     const int rows2 = nw2 * 32;
     const bool w2_lds = p.w2_lds != 0;
-    // Phase-D geometry.
+    // Phase-D geometry: workers are waves 0..6; lane group j = lane mod nct
+    // (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct walks
+    // the active rows.
     const int nct = p.cw / 8;
     const int c0 = tile_of(w, P) * p.cw;
-    const int d_j = wave % nct;
-    const int d_rr = (wave / nct) * kWave + lane;
-    const int d_rs = (kNW / nct) * kWave;
+    const int d_j = lane & (nct - 1);
+    const int d_rr = wave * (kWave / nct) + lane / nct;
+    const int d_rs = kCW * (kWave / nct);
     const int d_col = c0 + d_j * 8;
-    const bool d_ok = d_col < d;
+    const bool d_ok = wave < kCW && d_col < d;
 
-    const LayerDesc& Ld = p.layers[l];
-    const uint8_t* x = (const uint8_t*)Ld.x;
-    const uint8_t* W2 = (const uint8_t*)Ld.W2;
+    CLayer* Ld = (CLayer*)p.layers + l;
+    const uint8_t* x = (const uint8_t*)Ld->x;
+    const uint8_t* W2 = (const uint8_t*)Ld->W2;
 
     // ---------------------------------------------------------------- phase A
     {
-      Raw<16> w1r[kU];
-      if (a_active) {
-        const uint8_t* row = (const uint8_t*)Ld.W1 + (size_t)a_row * rb1;
-#pragma unroll
-        for (int m = 0; m < kU; ++m) {
-          const int c = a_part * kWave + lane + m * a_stride;
-          if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
-        }
-      }
       float acc[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] = 0.f;
       if (a_active) {
 #pragma unroll
         for (int m = 0; m < kU; ++m) {
-          const int c = a_part * kWave + lane + m * a_stride;
+          const int c = lane + m * kWave;
           if (c < nch1) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -241,60 +329,43 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
               }
           }
         }
-      }
-      const float v = wave_reduce_multi<NB>(acc);
-      if (reduce_owner<NB>(lane)) s_red[wave * NB + reduce_index<NB>(lane)] = v;
-      __syncthreads();
-      if (tid < nr1 * B) {
-        const int slot = tid / B, b = tid - slot * B;
-        const int row = w + P * slot;
-        if (row < h) {
-          float s = 0.f;
-          for (int q = 0; q < wpr; ++q) s += s_red[(slot * wpr + q) * NB + b];
-          st_tagged(p.hid + (size_t)b * h + row, tag, __float_as_uint(fmaxf(s, 0.f)));
-        }
+        const float v = wave_reduce_multi<NB>(acc);
+        const int b = reduce_index<NB>(lane);
+        if (reduce_owner<NB>(lane) && b < B)
+          st_tagged(p.hid + (size_t)w * kHidBlock + wave * NB + b, tag, __float_as_uint(fmaxf(v, 0.f)));
       }
     }
-    if (w2_lds) {
-      // the owned W2 rows -> LDS, row-major, 16 bytes per lane
-      const int items = rows2 * nch2;
-      for (int i0 = wave * kWave; i0 < items; i0 += kNT) {
-        const int i = i0 + lane;
-        if (i < items) {
-          const int q = i / nch2;
-          const int c = i - q * nch2;
-          int row = 32 * (w + P * (q >> 5)) + (q & 31);
-          if (row >= f) row = f - 1;     // rows past f are loaded but never used
-          __builtin_amdgcn_global_load_lds((const void*)(W2 + (size_t)row * rb2 + (size_t)c * 16),
-                                           (__attribute__((address_space(3))) void*)(s_w2 + (size_t)i0 * 16), 16, 0,
-                                           0);
-        }
-      }
-    }
-
     // ---------------------------------------------------------------- phase B
     {
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
-      if (w2_lds) {
-        wait_memory();                         // this thread's LDS rows have landed
+      if (w2_lds && wave >= kAW && wave < kCW) {
+        wait_memory();                         // this wave's LDS rows have landed
       }
-      for (int b0 = 0; b0 < B; b0 += TB) {
-        const int tb = min(TB, B - b0);
-        __syncthreads();                       // previous use of s_hid / s_w2 done
-        for (int i0 = tid; i0 < tb * h; i0 += 8 * kNT) {
-          unsigned long long hw[8];
-          const int n = min(8, (tb * h - i0 + kNT - 1) / kNT);
-          poll_tagged<8>(hw, n, [&](int u) { return p.hid + (size_t)b0 * h + i0 + u * kNT; }, tag, p.err);
+      // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
+      // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row]
+      constexpr int kPT = kAW * kWave;
+      if (wave < kAW) {
+#pragma unroll 1
+        for (int o = tid; o < P; o += kPT) {
+          const int ns = o < h ? (h - o + P - 1) / P : 0;
+          // block entry s NB + b holds row o + P s, token b
+          unsigned long long hw[4 * NB];
+          auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
+          poll_tagged_if<4 * NB>(hw, valid, [&](int i) { return p.hid + (size_t)o * kHidBlock + i; }, tag, p.err);
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (u < n) s_hid[i0 + u * kNT] = __uint_as_float((uint32_t)hw[u]);
+          for (int i = 0; i < 4 * NB; ++i)
+            if (valid(i)) s_hid[(i % NB) * h + o + P * (i / NB)] = __uint_as_float((uint32_t)hw[i]);
         }
-        __syncthreads();
-        for (int q0 = wave; q0 < rows2; q0 += kNW * 8) {
-          float a2[8 * TB];
+      }
+      __syncthreads();
+      {
+        constexpr int b0 = 0;
+        const int tb = B;
+        for (int q0 = wave; q0 < rows2; q0 += kNW * kRB) {
+          float a2[kRB * TB];
 #pragma unroll
-          for (int i = 0; i < 8 * TB; ++i) a2[i] = 0.f;
+          for (int i = 0; i < kRB * TB; ++i) a2[i] = 0.f;
           for (int c = lane; c < nch2; c += kWave) {
             float hv[TB][8];
 #pragma unroll
@@ -304,30 +375,32 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
               hv[b][0] = u0.x; hv[b][1] = u0.y; hv[b][2] = u0.z; hv[b][3] = u0.w;
               hv[b][4] = u1.x; hv[b][5] = u1.y; hv[b][6] = u1.z; hv[b][7] = u1.w;
             }
+            // kRB rows per lane, no per-row branches (rows past the end are clamped
+            // and their sums dropped), so the kRB TB accumulation chains interleave
+            Raw<16> wv[kRB];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const int q = q0 + r * kNW;
-              if (q < rows2) {
-                Raw<16> wv;
-                if (w2_lds) {
-                  wv = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
-                } else {
-                  const int row = 32 * (w + P * (q >> 5)) + (q & 31);
-                  if (row < f) wv = load_raw<16>(W2 + (size_t)row * rb2 + (size_t)c * 16);
-                  else wv.w[0] = wv.w[1] = wv.w[2] = wv.w[3] = 0u;
-                }
-                float wf[8];
-                unpack<T, 4>(wv.w, wf);
-#pragma unroll
-                for (int b = 0; b < TB; ++b)
-#pragma unroll
-                  for (int e = 0; e < 8; ++e) a2[r * TB + b] = fmaf(wf[e], hv[b][e], a2[r * TB + b]);
+            for (int r = 0; r < kRB; ++r) {
+              const int q = min(q0 + r * kNW, rows2 - 1);
+              if (w2_lds) {
+                wv[r] = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
+              } else {
+                const int row = min(32 * (w + P * (q >> 5)) + (q & 31), f - 1);
+                wv[r] = load_raw<16>(W2 + (size_t)row * rb2 + (size_t)c * 16);
               }
             }
+            float wf[kRB][8];
+#pragma unroll
+            for (int r = 0; r < kRB; ++r) unpack<T, 4>(wv[r].w, wf[r]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+              for (int r = 0; r < kRB; ++r)
+#pragma unroll
+                for (int b = 0; b < TB; ++b) a2[r * TB + b] = fmaf(wf[r][e], hv[b][e], a2[r * TB + b]);
           }
-          const float v = wave_reduce_multi<8 * TB>(a2);
-          if (reduce_owner<8 * TB>(lane)) {
-            const int idx = reduce_index<8 * TB>(lane);
+          const float v = wave_reduce_multi<kRB * TB>(a2);
+          if (reduce_owner<kRB * TB>(lane)) {
+            const int idx = reduce_index<kRB * TB>(lane);
             const int r = idx / TB, b = idx - r * TB;
             const int q = q0 + r * kNW;
             if (q < rows2 && b < tb) s_sc[q * NB + b0 + b] = v;
@@ -342,12 +415,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const int g = w + P * m;
         const int row = 32 * g + (lane & 31);
         const bool in = m < nw2 && row < f;
-        const float thr = Ld.threshold;
+        const float thr = Ld->threshold;
         for (int b = 0; b < B; ++b) {
           const uint64_t bal = __ballot(in && s_sc[(32 * m + (lane & 31)) * NB + b] >= thr);
           if ((lane & 31) == 0 && m < nw2) {
             const uint32_t word = (uint32_t)(lane == 0 ? bal : (bal >> 32));
-            if (Ld.tok_bits != nullptr) Ld.tok_bits[(size_t)b * W + g] = word;
+            if (Ld->tok_bits != nullptr) Ld->tok_bits[(size_t)b * W + g] = word;
             s_words[m * NB + b] = word;
           }
         }
@@ -357,25 +430,34 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         uint32_t u = 0;
         for (int b = 0; b < B; ++b) u |= s_words[tid * NB + b];
         const int g = w + P * tid;
-        st_tagged(p.uni + g, tag, u);
-        Ld.union_bits[g] = u;
+        st_tagged(p.uni + (size_t)w * p.us + tid, tag, u);
+        Ld->union_bits[g] = u;
       }
       for (int i = tid; i < rows2 * B; i += kNT) {
         const int q = i / B, b = i - q * B;
         const int row = 32 * (w + P * (q >> 5)) + (q & 31);
-        if (row < f) Ld.scores[(size_t)b * f + row] = s_sc[q * NB + b];
+        if (row < f) Ld->scores[(size_t)b * f + row] = s_sc[q * NB + b];
       }
     }
 
     // ---------------------------------------------------------------- phase C
-    unsigned long long uw[2];
-    {
-      const int base2 = 2 * tid;
-      const int n = base2 + 1 < W ? 2 : (base2 < W ? 1 : 0);
-      poll_tagged<2>(uw, n, [&](int u) { return p.uni + base2 + u; }, tag, p.err);
+    // thread o polls the union block of workgroup o (words o + P m) into s_uw
+#pragma unroll 1
+    for (int o = tid; o < P; o += kNT) {
+      const int nw = o < W ? (W - o + P - 1) / P : 0;
+#pragma unroll 1
+      for (int m0 = 0; m0 < nw; m0 += 8) {
+        unsigned long long uv[8];
+        const int n = min(8, nw - m0);
+        poll_tagged<8>(uv, n, [&](int i) { return p.uni + (size_t)o * p.us + m0 + i; }, tag, p.err);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < n) s_uw[o + P * (m0 + i)] = (uint32_t)uv[i];
+      }
     }
-    const uint32_t w0 = 2 * tid < W ? (uint32_t)uw[0] : 0u;
-    const uint32_t w1 = 2 * tid + 1 < W ? (uint32_t)uw[1] : 0u;
+    lds_barrier();
+    const uint32_t w0 = 2 * tid < W ? s_uw[2 * tid] : 0u;
+    const uint32_t w1 = 2 * tid + 1 < W ? s_uw[2 * tid + 1] : 0u;
     const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
     uint32_t inc = cnt;
 #pragma unroll
@@ -393,8 +475,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       total += t;
     }
     const uint32_t base = before + inc - cnt;
-    if (2 * tid < W) { s_pref[2 * tid] = base; s_uw[2 * tid] = w0; }
-    if (2 * tid + 1 < W) { s_pref[2 * tid + 1] = base + cnt0; s_uw[2 * tid + 1] = w1; }
+    if (2 * tid < W) s_pref[2 * tid] = base;
+    if (2 * tid + 1 < W) s_pref[2 * tid + 1] = base + cnt0;
     if (tid == 0) s_pref[W] = total;
     const int k = (int)total;
     const bool in_lds = k <= kNidCap;
@@ -405,17 +487,31 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       wd = w1;
       while (wd) { s_nid[pos++] = 64 * tid + 32 + __builtin_ctz(wd); wd &= wd - 1; }
     }
-    if (w == 0 && tid == 0) *Ld.count = k;
+    if (w == 0 && tid == 0) *Ld->count = k;
     __syncthreads();
+
+    // Phase-D loads of this thread's Wd segments, kRD rows at a time.
+    const uint8_t* Wd = (const uint8_t*)Ld->Wd;
+    Raw<16> wdv[kRD];
+    auto load_wd = [&](int rb) {
+#pragma unroll
+      for (int u = 0; u < kRD; ++u) {
+        const int r = rb + u * d_rs;
+        if (r < k) {
+          const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
+          wdv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
+        }
+      }
+    };
 
     {
       const int r0 = (int)(((long long)k * w) / P);
       const int r1 = (int)(((long long)k * (w + 1)) / P);
-      for (int r = r0 + wave; r < r1; r += kNW) {
+      for (int r = r0 + (wave < kCW ? wave : r1); r < r1; r += kCW) {
         const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
-        if (lane == 0) Ld.idx[r] = nid;
-        const uint8_t* ra = (const uint8_t*)Ld.Wa + (size_t)nid * rb1;
-        const uint8_t* rl = REGLU ? (const uint8_t*)Ld.Wl + (size_t)nid * rb1 : nullptr;
+        if (lane == 0) Ld->idx[r] = nid;
+        const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
+        const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
         float za[NB], zl[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
@@ -444,7 +540,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             }
           }
         }
-        const float bias = Ld.ba != nullptr ? Ld.ba[nid] : 0.f;
+        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
         const float ta = wave_reduce_multi<NB>(za);
         float v = fmaxf(ta + bias, 0.f);
         if (REGLU) v *= wave_reduce_multi<NB>(zl);
@@ -452,29 +548,25 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           const int b = reduce_index<NB>(lane);
           if (b < B) {
             st_tagged(p.hact + (size_t)r * B + b, tag, __float_as_uint(v));
-            Ld.hact[(size_t)r * B + b] = v;
+            Ld->hact[(size_t)r * B + b] = v;
           }
         }
       }
+      arrive(&s_cnt[1], kNW, p.fhact + (size_t)w * kFS, tag);
     }
 
     // ---------------------------------------------------------------- phase D
+    // The workers' first Wd batch goes out before the wait for the activations.
+    if (d_ok) load_wd(d_rr);
+    if (wave == kCW) wait_flags(p.fhact, P, tag, p.err, 5u);
+    lds_barrier();
     {
       float yacc[NB * 8];
 #pragma unroll
       for (int i = 0; i < NB * 8; ++i) yacc[i] = 0.f;
       if (d_ok) {
-        const uint8_t* Wd = (const uint8_t*)Ld.Wd;
         for (int rb = d_rr; rb < k; rb += d_rs * kRD) {
-          Raw<16> wv[kRD];
-#pragma unroll
-          for (int u = 0; u < kRD; ++u) {
-            const int r = rb + u * d_rs;
-            if (r < k) {
-              const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
-              wv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
-            }
-          }
+          if (rb != d_rr) load_wd(rb);
           unsigned long long hv[kRD * NB];
           const int nrow = min(kRD, (k - rb + d_rs - 1) / d_rs);
           poll_tagged<kRD * NB>(hv, nrow * B,
@@ -484,7 +576,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           for (int u = 0; u < kRD; ++u) {
             if (u < nrow) {
               float wf[8];
-              unpack<T, 4>(wv[u].w, wf);
+              unpack<T, 4>(wdv[u].w, wf);
 #pragma unroll
               for (int b = 0; b < NB; ++b)
                 if (b < B) {
@@ -496,9 +588,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           }
         }
       }
-      const float v = wave_reduce_multi<NB * 8>(yacc);
+      // sum over the lanes of each lane group, then over the worker waves (lane
+      // groups 0 and 1 are the same columns when nct = 1), in a fixed order
+      constexpr int V = NB * 8;
+      const float v = wave_reduce_multi_groups<V, 2>(yacc);
       __syncthreads();                                   // s_red was read in phase B
-      if (reduce_owner<NB * 8>(lane)) s_red[wave * 64 + reduce_index<NB * 8>(lane)] = v;
+      if ((lane & (kWave / V - 1)) < 2) s_red[wave * 64 + (lane >> (6 - ilog2c(V))) * 2 + (lane & 1)] = v;
       __syncthreads();
       for (int i = tid; i < nct * B * 8; i += kNT) {
         const int j = i / (B * 8);
@@ -506,15 +601,24 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const int col = c0 + j * 8 + (be & 7);
         if (col < d) {
           float s = 0.f;
-          for (int wv2 = j; wv2 < kNW; wv2 += nct) s += s_red[wv2 * 64 + be];
-          Ld.y[(size_t)(be >> 3) * d + col] = s;
+          for (int wv2 = 0; wv2 < kCW; ++wv2)
+            for (int jj = j; jj < 2; jj += nct) s += s_red[wv2 * 64 + be * 2 + jj];
+          Ld->y[(size_t)(be >> 3) * d + col] = s;
         }
       }
     }
-    if (l + 1 < p.L) grid_barrier(p, e0 + (uint32_t)l + 1u);
+    if (l + 1 < p.L) {
+      // grid barrier: every workgroup raises its flag once its layer is done and
+      // waits for all flags; the next layer's weights stream in meanwhile
+      lds_barrier();
+      if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
+      prefetch_weights<kU>(p, (CLayer*)p.layers + l + 1, s_w2, w1r);
+      if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
+      lds_barrier();
+    }
   }
-  // Every workgroup ends with its flag at e0 + L, so all flags agree at the next call.
-  if (threadIdx.x == 0) store_through(p.flags + blockIdx.x, e0 + (uint32_t)p.L);
+  // Every workgroup ends with all its flags at e0 + L, so all flags agree at the next call.
+  if (threadIdx.x == 0) store_through(p.fbar + (size_t)blockIdx.x * kFS, e0 + (uint32_t)p.L);
 }
 
 template <class T, int NB, int DL>

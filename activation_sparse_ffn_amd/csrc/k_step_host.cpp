@@ -21,7 +21,7 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   StepGeom g{};
   g.ok = false;
   g.P = P;
-  if (P < 8 || (wdt != DT_F16 && wdt != DT_BF16) || B < 1 || B > 4 || (act != 0 && act != 1)) return g;
+  if (P < 8 || P > 256 || (wdt != DT_F16 && wdt != DT_BF16) || B < 1 || B > 4 || (act != 0 && act != 1)) return g;
   if (d < 8 || h < 8 || d % 8 != 0 || h % 8 != 0 || f < 1) return g;
   const int W = (f + 31) / 32;
   if (W > kMaxWords) return g;
@@ -29,7 +29,7 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   g.dl = nch1 <= 512 ? 1 : 0;
   if (g.dl == 0) return g;
   g.nr1 = (h + P - 1) / P;
-  if (g.nr1 > kNW) return g;
+  if (g.nr1 > 4) return g;                  // one W1 row per wave of waves 0..3
   const int NB = nb_class(B);
   const int nw2max = (W + P - 1) / P;
   if (32 * nw2max * NB > kRedFloats) return g;
@@ -41,7 +41,7 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   int nct = (d + 8 * P - 1) / (8 * P);
   int n = 1;
   while (n < nct) n <<= 1;
-  if (n > kNW) return g;
+  if (n > 2) return g;                       // down: at most 2 lane groups of 8 columns
   g.cw = 8 * n;
   g.ok = true;
   (void)kNT;
@@ -52,14 +52,23 @@ namespace {
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
-// control line | flags [P] | hidden [B][h] | union [W] | hact [f][B]  (tagged words: 8 bytes)
-size_t step_ws_bytes(int B, int h, int f, int P) {
-  const size_t W = ((size_t)f + 31) / 32;
-  return 256 + up256((size_t)P * 4) + up256((size_t)B * h * 8) + up256(W * 8) + up256((size_t)f * B * 8);
+// Tagged union words per workgroup block.
+int step_union_block(int f, int P) {
+  const int W = (f + 31) / 32;
+  const int nw2max = (W + P - 1) / P;
+  return (nw2max + 7) & ~7;
 }
 
-hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,
-                       void* ws, const StepGeom& g) {
+// control line | 2 flag arrays [P][kFlagStride] | hidden [P][16] | union [P][us] |
+// hact [f][B]  (tagged words: 8 bytes)
+size_t step_ws_bytes(int B, int h, int f, int P) {
+  (void)h;
+  const size_t fl = up256((size_t)P * kFlagStride * 4);
+  return 256 + 2 * fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P) * 8) +
+         up256((size_t)f * B * 8);
+}
+
+StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layers, void* ws, const StepGeom& g) {
   StepParams p{};
   p.layers = layers;
   p.L = L;
@@ -73,14 +82,22 @@ hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int
   p.cw = g.cw;
   uint8_t* base = (uint8_t*)ws;
   p.err = (uint32_t*)base;
-  p.go = (uint32_t*)(base + 128);
-  p.flags = (uint32_t*)(base + 256);
-  size_t off = 256 + up256((size_t)g.P * 4);
+  p.us = step_union_block(f, g.P);
+  const size_t fl = up256((size_t)g.P * kFlagStride * 4);
+  p.fbar = (uint32_t*)(base + 256);
+  p.fhact = (uint32_t*)(base + 256 + fl);
+  size_t off = 256 + 2 * fl;
   p.hid = (unsigned long long*)(base + off);
-  off += up256((size_t)B * h * 8);
+  off += up256((size_t)g.P * 16 * 8);
   p.uni = (unsigned long long*)(base + off);
-  off += up256((size_t)p.W * 8);
+  off += up256((size_t)g.P * p.us * 8);
   p.hact = (unsigned long long*)(base + off);
+  return p;
+}
+
+hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,
+                       void* ws, const StepGeom& g) {
+  const StepParams p = step_params(B, d, h, f, L, layers, ws, g);
   if (wdt == DT_F16) return launch_step_f16(s, p, act, g.P, g.dl);
   return launch_step_bf16(s, p, act, g.P, g.dl);
 }

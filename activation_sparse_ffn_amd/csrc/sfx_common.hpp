@@ -60,7 +60,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // halving the values held per lane at every exchange (about V + 6 shuffles instead
 // of 6 V).  On return v[0] of lane L holds the total of value index
 // L >> (6 - log2 V).  The pattern is fixed, so results are reproducible.
-template <int V, int O>
+template <int V, int O, int M = 1>
 struct WaveReduceStep {
   __device__ __forceinline__ static void run(float* v, int lane) {
     constexpr int half = V / 2;
@@ -71,20 +71,29 @@ struct WaveReduceStep {
       const float keep = up ? v[i + half] : v[i];
       v[i] = keep + __shfl_xor(send, O, kWave);
     }
-    WaveReduceStep<half, O / 2>::run(v, lane);
+    WaveReduceStep<half, O / 2, M>::run(v, lane);
   }
 };
-template <int O>
-struct WaveReduceStep<1, O> {
+template <int O, int M>
+struct WaveReduceStep<1, O, M> {
   __device__ __forceinline__ static void run(float* v, int) {
 #pragma unroll
-    for (int o = O; o > 0; o >>= 1) v[0] += __shfl_xor(v[0], o, kWave);
+    for (int o = O; o >= M; o >>= 1) v[0] += __shfl_xor(v[0], o, kWave);
   }
 };
 template <int V>
 __device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
   static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
   WaveReduceStep<V, 32>::run(v, threadIdx.x & (kWave - 1));
+  return v[0];
+}
+// As wave_reduce_multi, but lanes are only summed across lane bits >= log2 M:
+// lane L ends with value index L >> (6 - log2 V) of lane group L mod M, and lanes
+// with (L mod 64/V) < M hold distinct (index, group) pairs.
+template <int V, int M>
+__device__ __forceinline__ float wave_reduce_multi_groups(float (&v)[V]) {
+  static_assert(V >= 1 && V * M <= 64 && (V & (V - 1)) == 0 && (M & (M - 1)) == 0, "bad V / M");
+  WaveReduceStep<V, 32, M>::run(v, threadIdx.x & (kWave - 1));
   return v[0];
 }
 __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }

@@ -16,12 +16,13 @@ struct StepParams {
   int nr1;        // hidden rows per workgroup (ceil(h / P))
   int w2_lds;     // 1: the workgroup's W2 rows are staged in LDS
   int cw;         // columns of y per workgroup in the down phase (8, 16, 32 or 64)
+  int us;         // tagged union words per workgroup block (multiple of 8)
   uint32_t* err;               // nonzero after a wait timed out
-  uint32_t* go;
-  uint32_t* flags;             // one arrival counter per workgroup
-  unsigned long long* hid;     // [B][h]  {tag, hidden}
-  unsigned long long* uni;     // [W]     {tag, union word}
-  unsigned long long* hact;    // [f][B]  {tag, activation}
+  uint32_t* fbar;              // [P] x kFlagStride: layer done (grid barrier); holds layer tags
+  uint32_t* fhact;             // [P] x kFlagStride: activations issued; holds layer tags
+  unsigned long long* hid;     // [P][16]  {tag, hidden}: rows w + P s, s < nr1, all tokens
+  unsigned long long* uni;     // [P][us]  {tag, union word}: words w + P m
+  unsigned long long* hact;    // [f][B]   {tag, activation} by active rank
 };
 
 struct StepGeom {
@@ -30,7 +31,12 @@ struct StepGeom {
 };
 
 StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P);
+#ifndef SFX_FLAG_STRIDE
+#define SFX_FLAG_STRIDE 16
+#endif
+constexpr int kFlagStride = SFX_FLAG_STRIDE;   // words between two workgroups' flags
 size_t step_ws_bytes(int B, int h, int f, int P);
+StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layers, void* ws, const StepGeom& g);
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L,
                        const LayerDesc* layers, void* ws, const StepGeom& g);
 
