@@ -103,6 +103,26 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier among some waves of the workgroup only: each arriving wave adds 1 to an
+// LDS counter that only grows, and waits until it reaches `target`.  Lets waves that
+// are busy issuing a long stream of loads stay out of the way.
+__device__ __forceinline__ void lds_wait_at_least(const uint32_t* ctr, uint32_t target, uint32_t* err) {
+  for (int spins = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; ++spins) {
+    if (spins > kSpin) {                  // cannot happen unless a wave skipped its arrival
+      if ((threadIdx.x & (kWave - 1)) == 0) store_through(err, 6u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t target, uint32_t* err) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS accesses are done
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(ctr, 1u);
+  lds_wait_at_least(ctr, target, err);
+  asm volatile("" ::: "memory");
+}
+
 // Hand-off completion flags: one 32-bit word per workgroup and hand-off kind,
 // raised to the layer tag once the workgroup has issued all its tagged words of
 // that kind.  A consumer waits for all P flags with one wave (P/64 coalesced loads
@@ -201,34 +221,49 @@ __device__ __forceinline__ int rank_to_neuron(int r, const uint32_t* s_pref, con
 //   waves 4..6  stream the next layer's W2 rows into LDS;
 //   wave 7      the control wave: every wait for other workgroups' flags;
 //   waves 0..6  up rows and down segments.
+#ifndef SFX_PF_AT
+#define SFX_PF_AT 1
+#endif
+// When a layer's W2 rows are streamed into LDS: 0 before the previous layer's grid
+// barrier, 1 after it (once phase A has requested its input rows), 2 right after
+// the previous layer's scores (the streaming waves then take no up or down rows).
+constexpr int kPfAt = SFX_PF_AT;
 constexpr int kAW = 4;                   // waves [0, kAW): W1 rows
 constexpr int kCW = 7;                   // control wave; waves [kAW, kCW) stream W2
+constexpr int kWork = kPfAt == 2 ? kAW : kCW;   // waves [0, kWork) take up and down rows
 
 // Weights of a layer that do not depend on its input, fetched before the layer
 // starts (behind the previous layer's barrier): the W1 row of each of waves 0..3
 // into registers, and the workgroup's W2 rows (mask words g = w, w + P, ...: 32
 // rows each) straight into LDS with 16-byte global->LDS loads.
 template <int kU>
-__device__ __forceinline__ void prefetch_weights(const StepParams& p, CLayer* Ld, uint8_t* s_w2,
-                                                 Raw<16> (&w1r)[kU]) {
+__device__ __forceinline__ void prefetch_w1(const StepParams& p, CLayer* Ld, Raw<16> (&w1r)[kU]) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int w = blockIdx.x;
   const int P = gridDim.x;
-  if (wave < kAW) {
-    const int a_row = w + P * wave;
-    if (wave < p.nr1 && a_row < p.h) {
-      const uint8_t* row = (const uint8_t*)Ld->W1 + (size_t)a_row * p.d * 2;
-      const int nch1 = p.d / 8;
+  const int a_row = w + P * wave;
+  if (wave < kAW && wave < p.nr1 && a_row < p.h) {
+    const uint8_t* row = (const uint8_t*)Ld->W1 + (size_t)a_row * p.d * 2;
+    const int nch1 = p.d / 8;
 #pragma unroll
-      for (int m = 0; m < kU; ++m) {
-        const int c = lane + m * kWave;
-        if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
-      }
+    for (int m = 0; m < kU; ++m) {
+      const int c = lane + m * kWave;
+      if (c < nch1) w1r[m] = load_raw<16>(row + (size_t)c * 16);
     }
-  } else if (wave < kCW && p.w2_lds != 0) {
+  }
+}
+
+__device__ __forceinline__ void prefetch_w2(const StepParams& p, CLayer* Ld, uint8_t* s_w2) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int w = blockIdx.x;
+  const int P = gridDim.x;
+  if (wave >= kAW && wave < kCW && p.w2_lds != 0) {
     const uint8_t* W2 = (const uint8_t*)Ld->W2;
     const int nch2 = p.h / 8;
     const size_t rb2 = (size_t)p.h * 2;
@@ -249,6 +284,24 @@ __device__ __forceinline__ void prefetch_weights(const StepParams& p, CLayer* Ld
   }
 }
 
+// Thread and shape values, re-derived at the start of every phase behind opaque
+// copies: values computed once would be hoisted out of the layer loop and kept
+// live through every phase.
+#define SFX_PHASE_IDS                                                      \
+  int tid = threadIdx.x;                                                   \
+  asm volatile("" : "+v"(tid));                                            \
+  const int lane = tid & (kWave - 1);                                      \
+  const int wave = tid >> 6;                                               \
+  int w = blockIdx.x;                                                      \
+  asm volatile("" : "+s"(w));                                              \
+  const int P = gridDim.x;                                                 \
+  const int B = p.B, d = p.d, h = p.h, f = p.f, W = p.W;                   \
+  const int nch1 = d / 8;        /* 16-byte chunks per W1 / Wa / Wd row */ \
+  const int nch2 = h / 8;        /* 16-byte chunks per W2 row */           \
+  const size_t rb1 = (size_t)d * 2, rb2 = (size_t)h * 2;                   \
+  (void)lane; (void)wave; (void)P; (void)B; (void)d; (void)h; (void)f; (void)W; \
+  (void)nch1; (void)nch2; (void)rb1; (void)rb2
+
 // T: TF16 or TBF16.  NB: token class (1, 2, 4).  DL: 1 for d <= 4096.
 template <class T, int NB, bool REGLU, int DL>
 __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
@@ -267,52 +320,50 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
 
   __shared__ uint32_t s_cnt[2];             // arrivals: [1] hact
+  __shared__ uint32_t s_grp;                 // group_sync arrivals of waves 0..3
   if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) s_grp = 0u;
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
   Raw<16> w1r[kU];
-  prefetch_weights<kU>(p, (CLayer*)p.layers, s_w2, w1r);
+  prefetch_w1<kU>(p, (CLayer*)p.layers, w1r);
+  prefetch_w2(p, (CLayer*)p.layers, s_w2);
   for (int l = 0; l < p.L; ++l) {
-    // Re-derived per layer behind opaque copies, so per-thread offsets are not
-    // hoisted out of the layer loop (that would keep every phase's values live).
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    int w = blockIdx.x;
-    asm volatile("" : "+s"(w));
-    const int P = gridDim.x;
-    const int B = p.B, d = p.d, h = p.h, f = p.f, W = p.W;
-    const int nch1 = d / 8;        // 16-byte chunks per W1 / Wa / Wd row
-    const int nch2 = h / 8;        // 16-byte chunks per W2 row
-    const size_t rb1 = (size_t)d * 2, rb2 = (size_t)h * 2;
     const uint32_t tag = e0 + (uint32_t)l + 1u;
-
-    // Phase-A geometry: row w + P s of W1 in wave s (s < nr1 <= 4).
-    const int nr1 = p.nr1;
-    const int a_row = w + P * wave;
-    const bool a_active = wave < nr1 && a_row < h;
-    // Phase-B geometry: owned mask words w + P m, m < nw2.
-    const int nw2 = w < W ? (W - w + P - 1) / P : 0;
-    const int rows2 = nw2 * 32;
-    const bool w2_lds = p.w2_lds != 0;
-    // Phase-D geometry: workers are waves 0..6; lane group j = lane mod nct
-    // (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct walks
-    // the active rows.
-    const int nct = p.cw / 8;
-    const int c0 = tile_of(w, P) * p.cw;
-    const int d_j = lane & (nct - 1);
-    const int d_rr = wave * (kWave / nct) + lane / nct;
-    const int d_rs = kCW * (kWave / nct);
-    const int d_col = c0 + d_j * 8;
-    const bool d_ok = wave < kCW && d_col < d;
-
     CLayer* Ld = (CLayer*)p.layers + l;
-    const uint8_t* x = (const uint8_t*)Ld->x;
-    const uint8_t* W2 = (const uint8_t*)Ld->W2;
 
     // ---------------------------------------------------------------- phase A
     {
+      SFX_PHASE_IDS;
+      // row w + P s of W1 in wave s (s < nr1 <= 4)
+      const int a_row = w + P * wave;
+      const bool a_active = wave < p.nr1 && a_row < h;
+      const uint8_t* x = (const uint8_t*)Ld->x;
+      // The input rows go to LDS first (waves 0..3, 16 bytes per lane) and only
+      // then does this layer's W2 stream start (kPfAt == 1), so they are not
+      // queued behind it.  Inputs larger than the staging area are read directly.
+      // Waves 0..3 synchronise among themselves (group_sync) so the streaming
+      // waves, blocked while their loads issue, hold nobody up.
+      const bool x_lds = (size_t)B * rb1 <= (size_t)kXBytes;
+      uint8_t* s_xin = s_x;
+      const uint32_t g0 = 3u * kAW * (uint32_t)l;      // s_grp arrivals before this layer
+      if (wave < kAW) {
+        if (x_lds) {
+          const int items = B * nch1;
+#pragma unroll 1
+          for (int i0 = wave * kWave; i0 < items; i0 += kAW * kWave)
+            if (i0 + lane < items)
+              __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)(i0 + lane) * 16),
+                                               (__attribute__((address_space(3))) void*)(s_xin + (size_t)i0 * 16),
+                                               16, 0, 0);
+        }
+        group_sync(&s_grp, g0 + kAW, p.err);                  // inputs requested
+        if (x_lds) wait_memory();
+        group_sync(&s_grp, g0 + 2 * kAW, p.err);              // inputs landed
+      } else if (kPfAt == 1 && l > 0 && wave < kCW) {
+        lds_wait_at_least(&s_grp, g0 + kAW, p.err);
+        prefetch_w2(p, Ld, s_w2);
+      }
       float acc[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] = 0.f;
@@ -324,7 +375,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
               if (b < B) {
-                Raw<16> xv = load_raw<16>(x + (size_t)b * rb1 + (size_t)c * 16);
+                const Raw<16> xv = x_lds ? *reinterpret_cast<const Raw<16>*>(s_xin + (size_t)b * rb1 + (size_t)c * 16)
+                                         : load_raw<16>(x + (size_t)b * rb1 + (size_t)c * 16);
                 dot_chunk<T>(w1r[m].w, xv.w, acc[b]);
               }
           }
@@ -334,9 +386,16 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         if (reduce_owner<NB>(lane) && b < B)
           st_tagged(p.hid + (size_t)w * kHidBlock + wave * NB + b, tag, __float_as_uint(fmaxf(v, 0.f)));
       }
+      if (wave < kAW) group_sync(&s_grp, g0 + 3 * kAW, p.err);  // inputs read: s_x is reused in phase B
     }
     // ---------------------------------------------------------------- phase B
     {
+      SFX_PHASE_IDS;
+      // owned mask words w + P m, m < nw2
+      const int nw2 = w < W ? (W - w + P - 1) / P : 0;
+      const int rows2 = nw2 * 32;
+      const bool w2_lds = p.w2_lds != 0;
+      const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
       if (w2_lds && wave >= kAW && wave < kCW) {
@@ -408,6 +467,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
       __syncthreads();
+      if (kPfAt == 2 && l + 1 < p.L) prefetch_w2(p, Ld + 1, s_w2);
       // mask words by wave ballots (lane = row of a 64-row pair of words), then the
       // union goes out tagged, then the scores
       for (int m0 = 2 * wave; m0 < nw2; m0 += 2 * kNW) {
@@ -425,7 +485,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < nw2) {
         uint32_t u = 0;
         for (int b = 0; b < B; ++b) u |= s_words[tid * NB + b];
@@ -441,6 +501,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
 
     // ---------------------------------------------------------------- phase C
+    int k;                                     // active neurons of the layer
+    bool in_lds;                               // their list fits in LDS (s_nid)
+    {
+    SFX_PHASE_IDS;
     // thread o polls the union block of workgroup o (words o + P m) into s_uw
 #pragma unroll 1
     for (int o = tid; o < P; o += kNT) {
@@ -466,7 +530,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       if (lane >= o) inc += n;
     }
     if (lane == kWave - 1) s_wt[wave] = inc;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, total = 0;
 #pragma unroll
     for (int v = 0; v < kNW; ++v) {
@@ -478,8 +542,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     if (2 * tid < W) s_pref[2 * tid] = base;
     if (2 * tid + 1 < W) s_pref[2 * tid + 1] = base + cnt0;
     if (tid == 0) s_pref[W] = total;
-    const int k = (int)total;
-    const bool in_lds = k <= kNidCap;
+    k = (int)total;
+    in_lds = k <= kNidCap;
     if (in_lds) {
       uint32_t pos = base;
       uint32_t wd = w0;
@@ -488,26 +552,13 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       while (wd) { s_nid[pos++] = 64 * tid + 32 + __builtin_ctz(wd); wd &= wd - 1; }
     }
     if (w == 0 && tid == 0) *Ld->count = k;
-    __syncthreads();
-
-    // Phase-D loads of this thread's Wd segments, kRD rows at a time.
-    const uint8_t* Wd = (const uint8_t*)Ld->Wd;
-    Raw<16> wdv[kRD];
-    auto load_wd = [&](int rb) {
-#pragma unroll
-      for (int u = 0; u < kRD; ++u) {
-        const int r = rb + u * d_rs;
-        if (r < k) {
-          const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
-          wdv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
-        }
-      }
-    };
+    lds_barrier();
 
     {
+      const uint8_t* x = (const uint8_t*)Ld->x;
       const int r0 = (int)(((long long)k * w) / P);
       const int r1 = (int)(((long long)k * (w + 1)) / P);
-      for (int r = r0 + (wave < kCW ? wave : r1); r < r1; r += kCW) {
+      for (int r = r0 + (wave < kWork ? wave : r1); r < r1; r += kWork) {
         const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
         if (lane == 0) Ld->idx[r] = nid;
         const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
@@ -554,13 +605,36 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
       arrive(&s_cnt[1], kNW, p.fhact + (size_t)w * kFS, tag);
     }
+    }
 
     // ---------------------------------------------------------------- phase D
-    // The workers' first Wd batch goes out before the wait for the activations.
-    if (d_ok) load_wd(d_rr);
-    if (wave == kCW) wait_flags(p.fhact, P, tag, p.err, 5u);
-    lds_barrier();
     {
+      SFX_PHASE_IDS;
+      // workers are waves [0, kWork); lane group j = lane mod nct (nct <= 2) reads
+      // columns c0 + 8 j, lane slot wave * 64/nct + lane / nct walks the active rows
+      const int nct = p.cw / 8;
+      const int c0 = tile_of(w, P) * p.cw;
+      const int d_j = lane & (nct - 1);
+      const int d_rr = wave * (kWave / nct) + lane / nct;
+      const int d_rs = kWork * (kWave / nct);
+      const int d_col = c0 + d_j * 8;
+      const bool d_ok = wave < kWork && d_col < d;
+      const uint8_t* Wd = (const uint8_t*)Ld->Wd;
+      Raw<16> wdv[kRD];
+      auto load_wd = [&](int rb) {               // kRD rows at a time
+#pragma unroll
+        for (int u = 0; u < kRD; ++u) {
+          const int r = rb + u * d_rs;
+          if (r < k) {
+            const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
+            wdv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
+          }
+        }
+      };
+      // the workers' first batch goes out before the wait for the activations
+      if (d_ok) load_wd(d_rr);
+      if (wave == kCW) wait_flags(p.fhact, P, tag, p.err, 5u);
+      lds_barrier();
       float yacc[NB * 8];
 #pragma unroll
       for (int i = 0; i < NB * 8; ++i) yacc[i] = 0.f;
@@ -592,16 +666,16 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       // groups 0 and 1 are the same columns when nct = 1), in a fixed order
       constexpr int V = NB * 8;
       const float v = wave_reduce_multi_groups<V, 2>(yacc);
-      __syncthreads();                                   // s_red was read in phase B
+      lds_barrier();                                     // s_red was read in phase B
       if ((lane & (kWave / V - 1)) < 2) s_red[wave * 64 + (lane >> (6 - ilog2c(V))) * 2 + (lane & 1)] = v;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < nct * B * 8; i += kNT) {
         const int j = i / (B * 8);
         const int be = i - j * B * 8;                    // b * 8 + e
         const int col = c0 + j * 8 + (be & 7);
         if (col < d) {
           float s = 0.f;
-          for (int wv2 = 0; wv2 < kCW; ++wv2)
+          for (int wv2 = 0; wv2 < kWork; ++wv2)
             for (int jj = j; jj < 2; jj += nct) s += s_red[wv2 * 64 + be * 2 + jj];
           Ld->y[(size_t)(be >> 3) * d + col] = s;
         }
@@ -609,10 +683,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
     if (l + 1 < p.L) {
       // grid barrier: every workgroup raises its flag once its layer is done and
-      // waits for all flags; the next layer's weights stream in meanwhile
+      // waits for all flags
+      SFX_PHASE_IDS;
       lds_barrier();
       if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
-      prefetch_weights<kU>(p, (CLayer*)p.layers + l + 1, s_w2, w1r);
+      prefetch_w1<kU>(p, (CLayer*)p.layers + l + 1, w1r);
+      if (kPfAt == 0) prefetch_w2(p, (CLayer*)p.layers + l + 1, s_w2);
       if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
       lds_barrier();
     }

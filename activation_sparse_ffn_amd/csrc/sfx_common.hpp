@@ -60,6 +60,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 // halving the values held per lane at every exchange (about V + 6 shuffles instead
 // of 6 V).  On return v[0] of lane L holds the total of value index
 // L >> (6 - log2 V).  The pattern is fixed, so results are reproducible.
+// Lane index behind an opaque copy: lane masks derived from threadIdx.x directly
+// are loop-invariant, get hoisted out of long loops and pin scalar registers.
+__device__ __forceinline__ int opaque_lane() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t & (kWave - 1);
+}
+
 template <int V, int O, int M = 1>
 struct WaveReduceStep {
   __device__ __forceinline__ static void run(float* v, int lane) {
@@ -84,7 +92,7 @@ struct WaveReduceStep<1, O, M> {
 template <int V>
 __device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
   static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-  WaveReduceStep<V, 32>::run(v, threadIdx.x & (kWave - 1));
+  WaveReduceStep<V, 32>::run(v, opaque_lane());
   return v[0];
 }
 // As wave_reduce_multi, but lanes are only summed across lane bits >= log2 M:
@@ -93,7 +101,7 @@ __device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
 template <int V, int M>
 __device__ __forceinline__ float wave_reduce_multi_groups(float (&v)[V]) {
   static_assert(V >= 1 && V * M <= 64 && (V & (V - 1)) == 0 && (M & (M - 1)) == 0, "bad V / M");
-  WaveReduceStep<V, 32, M>::run(v, threadIdx.x & (kWave - 1));
+  WaveReduceStep<V, 32, M>::run(v, opaque_lane());
   return v[0];
 }
 __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
