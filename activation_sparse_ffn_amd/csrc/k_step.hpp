@@ -131,6 +131,14 @@ __device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t target, uint3
 // from every workgroup instead would load the memory system with re-reads while
 // slower workgroups are still gathering rows.
 constexpr int kMaxP = 256;
+#ifndef SFX_POLL_SLEEP
+#define SFX_POLL_SLEEP 2
+#endif
+constexpr int kPollSleep = SFX_POLL_SLEEP;
+#ifndef SFX_TLB_TOUCH
+#define SFX_TLB_TOUCH 0
+#endif
+constexpr bool kTlbTouch = SFX_TLB_TOUCH != 0;   // pause between flag polls, in units of 64 clocks
 // Flags sit kFS words apart: flags sharing a cache line with many writers become
 // visible to other compute units much later.
 constexpr int kFS = kFlagStride;
@@ -159,7 +167,7 @@ __device__ __forceinline__ void wait_flags(const uint32_t* fl, int P, uint32_t t
       if (lane == 0) store_through(err, code);
       return;
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(kPollSleep);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int i = lane + u * kWave;
@@ -307,9 +315,11 @@ template <class T, int NB, bool REGLU, int DL>
 __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int kU = 8 * DL;              // 16-byte chunks per lane of a d-row
   constexpr int TB = NB < 4 ? NB : 4;     // tokens per pass in phase B
-  constexpr int kUP = (REGLU || NB >= 4) ? 4 : kU;   // up-row chunks per lane loaded together
+  // up-row chunks per lane loaded together (with the input chunks they meet)
+  constexpr int kUP = (NB == 1 && !REGLU) ? kU : (NB == 1 || (NB == 2 && !REGLU)) ? 4 : 2;
   constexpr int kRD = 8 / NB;             // down rows per lane loaded together
   constexpr int kRB = TB <= 2 ? 8 : 4;    // score rows per lane per pass
+  constexpr bool kREGLU = REGLU;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
@@ -400,6 +410,17 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       float* s_sc = s_red;                     // [rows2][NB]
       if (w2_lds && wave >= kAW && wave < kCW) {
         wait_memory();                         // this wave's LDS rows have landed
+      }
+      if (kTlbTouch && wave == kCW && lane < 2 * (kREGLU ? 3 : 2)) {
+        // warm the address translations of the up / down matrices: one load per
+        // 2 MiB page, spread over the workgroups of each XCD
+        const int mat = lane >> 1;
+        const uint8_t* base = (const uint8_t*)(mat == 0 ? Ld->Wa : mat == 1 ? Ld->Wd : Ld->Wl);
+        const size_t page = (size_t)((w >> 3) + (lane & 1) * ((P + 7) >> 3)) << 21;
+        if (base != nullptr && page < (size_t)f * rb1) {
+          const uint32_t v = __builtin_nontemporal_load((const uint32_t*)(base + page));
+          if (v == 0x7fc00001u && f < 0) Ld->y[0] = 0.f;   // keeps the load
+        }
       }
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
       // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row]
@@ -568,25 +589,26 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
 #pragma unroll
         for (int u0 = 0; u0 < kU; u0 += kUP) {
-          Raw<16> wa[kUP], wl[kUP];
+          // every load of the batch is issued before the first is used: chunk
+          // indices are clamped instead of branched on, so the compiler keeps
+          // them together and waits once
+          Raw<16> wa[kUP], wl[kUP], xq[kUP][NB];
 #pragma unroll
           for (int u = 0; u < kUP; ++u) {
-            const int c = lane + (u0 + u) * kWave;
-            if (c < nch1) {
-              wa[u] = load_raw<16>(ra + (size_t)c * 16);
-              if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
-            }
+            const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
+            wa[u] = load_raw<16>(ra + (size_t)c * 16);
+            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
           }
 #pragma unroll
           for (int u = 0; u < kUP; ++u) {
-            const int c = lane + (u0 + u) * kWave;
-            if (c < nch1) {
+            if (lane + (u0 + u) * kWave < nch1) {
 #pragma unroll
               for (int b = 0; b < NB; ++b)
                 if (b < B) {
-                  Raw<16> xv = load_raw<16>(x + (size_t)b * rb1 + (size_t)c * 16);
-                  dot_chunk<T>(wa[u].w, xv.w, za[b]);
-                  if (REGLU) dot_chunk<T>(wl[u].w, xv.w, zl[b]);
+                  dot_chunk<T>(wa[u].w, xq[u][b].w, za[b]);
+                  if (REGLU) dot_chunk<T>(wl[u].w, xq[u][b].w, zl[b]);
                 }
             }
           }
@@ -621,18 +643,22 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const bool d_ok = wave < kWork && d_col < d;
       const uint8_t* Wd = (const uint8_t*)Ld->Wd;
       Raw<16> wdv[kRD];
-      auto load_wd = [&](int rb) {               // kRD rows at a time
+      auto load_wd = [&](int rb) {               // kRD rows at a time, rb < k
+        // ranks past k are clamped to k - 1 (loaded, never used), so the loads
+        // are issued back to back without branches
+        int nid[kRD];
+        if (in_lds) {
 #pragma unroll
-        for (int u = 0; u < kRD; ++u) {
-          const int r = rb + u * d_rs;
-          if (r < k) {
-            const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
-            wdv[u] = load_raw<16>(Wd + (size_t)nid * rb1 + (size_t)d_col * 2);
-          }
+          for (int u = 0; u < kRD; ++u) nid[u] = s_nid[min(rb + u * d_rs, k - 1)];
+        } else {
+#pragma unroll
+          for (int u = 0; u < kRD; ++u) nid[u] = rank_to_neuron(min(rb + u * d_rs, k - 1), s_pref, s_uw, W);
         }
+#pragma unroll
+        for (int u = 0; u < kRD; ++u) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
       };
       // the workers' first batch goes out before the wait for the activations
-      if (d_ok) load_wd(d_rr);
+      if (d_ok && d_rr < k) load_wd(d_rr);
       if (wave == kCW) wait_flags(p.fhact, P, tag, p.err, 5u);
       lds_barrier();
       float yacc[NB * 8];
@@ -643,9 +669,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           if (rb != d_rr) load_wd(rb);
           unsigned long long hv[kRD * NB];
           const int nrow = min(kRD, (k - rb + d_rs - 1) / d_rs);
-          poll_tagged<kRD * NB>(hv, nrow * B,
-                                [&](int i) { return p.hact + (size_t)(rb + (i / B) * d_rs) * B + (i % B); }, tag,
-                                p.err);
+          // entry u NB + b: activation of rank rb + u d_rs, token b
+          poll_tagged_if<kRD * NB>(
+              hv, [&](int i) { return i / NB < nrow && i % NB < B; },
+              [&](int i) { return p.hact + (size_t)(rb + (i / NB) * d_rs) * B + (i % NB); }, tag, p.err);
 #pragma unroll
           for (int u = 0; u < kRD; ++u) {
             if (u < nrow) {
@@ -654,7 +681,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
               for (int b = 0; b < NB; ++b)
                 if (b < B) {
-                  const float hvf = __uint_as_float((uint32_t)hv[u * B + b]);
+                  const float hvf = __uint_as_float((uint32_t)hv[u * NB + b]);
 #pragma unroll
                   for (int e = 0; e < 8; ++e) yacc[b * 8 + e] = fmaf(hvf, wf[e], yacc[b * 8 + e]);
                 }
