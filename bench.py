@@ -35,10 +35,12 @@ def parse():
     p.add_argument("--roofline-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=4)
-    p.add_argument("--cpu-steps", type=int, default=32)
+    p.add_argument("--cpu-steps", type=int, default=64)
     p.add_argument("--tam-lambda", type=float, default=0.9)
     p.add_argument("--tam-eps", type=float, default=0.01)
     p.add_argument("--separate", action="store_true", help="time the five separate calls per layer")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (5 times): the calibration of HBM byte counters")
     return p.parse_args()
 
 
@@ -64,6 +66,31 @@ def kernel_bytes(cfg, B, k):
         "up": B * d * ep + k * 4 + na * k * er + k * 4 + B * k * 4,
         "down": k * 4 + B * k * 4 + k * er + B * d * 4,
     }
+
+
+STEP_SOURCES = ["k_step.hpp", "k_step_host.cpp", "sfx_step.hpp", "sfx_common.hpp", "k_step_f16.hip", "k_step_bf16.hip"]
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "k_step_traffic_opt6.7b_fp16_b1.txt")
+
+
+def measured_traffic(cfg, B, L):
+    """HBM bytes per fused-step launch from the committed rocprofv3 counter summary,
+    or None when that summary is for another workload or for other kernel sources."""
+    import hashlib
+    if not (cfg.name == "C2" and B == 1 and L == cfg.layers) or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "activation_sparse_ffn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if vals.get("source_sha256") != h.hexdigest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, layers_np, xs_np, B, steps):
@@ -94,6 +121,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
+        return
     import synthetic as S
     from activation_sparse_ffn_amd import StackStep, StepBuffers, TamState, run_layer
     from activation_sparse_ffn_amd import _abi as A
@@ -239,7 +275,8 @@ def main():
         "path": "fused" if fused else "separate",
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
+                     "traffic": measured_traffic(cfg, B, L) if fused else None,
+                     "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
                      "bytes_per_launch": round(dom_bytes), "launches": int(dur_ms.size)},
     }
 
