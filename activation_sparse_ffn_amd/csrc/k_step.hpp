@@ -134,11 +134,7 @@ constexpr int kMaxP = 256;
 #ifndef SFX_POLL_SLEEP
 #define SFX_POLL_SLEEP 2
 #endif
-constexpr int kPollSleep = SFX_POLL_SLEEP;
-#ifndef SFX_TLB_TOUCH
-#define SFX_TLB_TOUCH 0
-#endif
-constexpr bool kTlbTouch = SFX_TLB_TOUCH != 0;   // pause between flag polls, in units of 64 clocks
+constexpr int kPollSleep = SFX_POLL_SLEEP;   // pause between flag polls, in units of 64 clocks
 // Flags sit kFS words apart: flags sharing a cache line with many writers become
 // visible to other compute units much later.
 constexpr int kFS = kFlagStride;
@@ -319,7 +315,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int kUP = (NB == 1 && !REGLU) ? kU : (NB == 1 || (NB == 2 && !REGLU)) ? 4 : 2;
   constexpr int kRD = 8 / NB;             // down rows per lane loaded together
   constexpr int kRB = TB <= 2 ? 8 : 4;    // score rows per lane per pass
-  constexpr bool kREGLU = REGLU;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
@@ -410,17 +405,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       float* s_sc = s_red;                     // [rows2][NB]
       if (w2_lds && wave >= kAW && wave < kCW) {
         wait_memory();                         // this wave's LDS rows have landed
-      }
-      if (kTlbTouch && wave == kCW && lane < 2 * (kREGLU ? 3 : 2)) {
-        // warm the address translations of the up / down matrices: one load per
-        // 2 MiB page, spread over the workgroups of each XCD
-        const int mat = lane >> 1;
-        const uint8_t* base = (const uint8_t*)(mat == 0 ? Ld->Wa : mat == 1 ? Ld->Wd : Ld->Wl);
-        const size_t page = (size_t)((w >> 3) + (lane & 1) * ((P + 7) >> 3)) << 21;
-        if (base != nullptr && page < (size_t)f * rb1) {
-          const uint32_t v = __builtin_nontemporal_load((const uint32_t*)(base + page));
-          if (v == 0x7fc00001u && f < 0) Ld->y[0] = 0.f;   // keeps the load
-        }
       }
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
       // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row]
@@ -541,8 +525,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
     }
     lds_barrier();
-    const uint32_t w0 = 2 * tid < W ? s_uw[2 * tid] : 0u;
-    const uint32_t w1 = 2 * tid + 1 < W ? s_uw[2 * tid + 1] : 0u;
+    // thread t owns words [wpt t, wpt t + wpt): one word when W <= 512, so a full
+    // (hot) word costs 32 steps of the extraction below, not 64
+    const int wpt = W <= kNT ? 1 : 2;
+    const int g0 = wpt * tid;
+    const uint32_t w0 = g0 < W ? s_uw[g0] : 0u;
+    const uint32_t w1 = wpt == 2 && g0 + 1 < W ? s_uw[g0 + 1] : 0u;
     const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
     uint32_t inc = cnt;
 #pragma unroll
@@ -560,20 +548,21 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       total += t;
     }
     const uint32_t base = before + inc - cnt;
-    if (2 * tid < W) s_pref[2 * tid] = base;
-    if (2 * tid + 1 < W) s_pref[2 * tid + 1] = base + cnt0;
+    if (g0 < W) s_pref[g0] = base;
+    if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
     if (tid == 0) s_pref[W] = total;
     k = (int)total;
     in_lds = k <= kNidCap;
     if (in_lds) {
       uint32_t pos = base;
       uint32_t wd = w0;
-      while (wd) { s_nid[pos++] = 64 * tid + __builtin_ctz(wd); wd &= wd - 1; }
+      while (wd) { s_nid[pos++] = 32 * g0 + __builtin_ctz(wd); wd &= wd - 1; }
       wd = w1;
-      while (wd) { s_nid[pos++] = 64 * tid + 32 + __builtin_ctz(wd); wd &= wd - 1; }
+      while (wd) { s_nid[pos++] = 32 * (g0 + 1) + __builtin_ctz(wd); wd &= wd - 1; }
     }
     if (w == 0 && tid == 0) *Ld->count = k;
     lds_barrier();
+
 
     {
       const uint8_t* x = (const uint8_t*)Ld->x;
@@ -627,13 +616,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
       arrive(&s_cnt[1], kNW, p.fhact + (size_t)w * kFS, tag);
     }
-    }
 
     // ---------------------------------------------------------------- phase D
     {
-      SFX_PHASE_IDS;
-      // workers are waves [0, kWork); lane group j = lane mod nct (nct <= 2) reads
-      // columns c0 + 8 j, lane slot wave * 64/nct + lane / nct walks the active rows
+      // Down-phase geometry: workers are waves [0, kWork); lane group j = lane mod
+      // nct (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct
+      // walks the active rows.
       const int nct = p.cw / 8;
       const int c0 = tile_of(w, P) * p.cw;
       const int d_j = lane & (nct - 1);
@@ -643,7 +631,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const bool d_ok = wave < kWork && d_col < d;
       const uint8_t* Wd = (const uint8_t*)Ld->Wd;
       Raw<16> wdv[kRD];
-      auto load_wd = [&](int rb) {               // kRD rows at a time, rb < k
+      auto load_wd = [&](int rb) {                 // kRD rows at a time, rb < k
         // ranks past k are clamped to k - 1 (loaded, never used), so the loads
         // are issued back to back without branches
         int nid[kRD];
@@ -708,6 +696,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
     }
+    }                                          // phases C and D
     if (l + 1 < p.L) {
       // grid barrier: every workgroup raises its flag once its layer is done and
       // waits for all flags
