@@ -3,31 +3,30 @@
 // predictor, hybrid-execution pseudocode, neuron-aware operators; KAIROX page, Core
 // method, item 3: neurons stored in contiguous groups of 32).
 //
-// One workgroup of 512 threads per compute unit, all resident.  Inside a layer,
-// data one workgroup hands to others (hidden values, union mask words, hact) is
-// written as 64-bit words {layer tag, value} with one agent-scope atomic store each;
-// readers poll those words with agent-scope atomic loads until the tag of the
-// current layer shows up.  So a hand-off costs one store and one poll, with no
-// store-completion wait and no grid barrier.  Between layers a grid barrier
-// (arrival flags polled by workgroup 0, which then releases a `go` word) makes the
-// layer's y complete before the next layer's input is read.  Every wait is bounded
-// and sets an error word instead of hanging.  Per layer:
+// One workgroup of 512 threads per compute unit, all resident.  Data one workgroup
+// hands to the others (hidden values, union mask words, activations) is written as
+// 64-bit words {layer tag, value}, one agent-scope atomic store each, in a block of
+// its own per producer; readers load those words with agent-scope loads and
+// re-poll the ones whose tag is stale.  Waits on every workgroup (activations, the
+// grid barrier between layers) poll one flag per workgroup from the control wave.
+// Every wait is bounded and sets an error word instead of hanging.  Per layer:
 //
-//   A  hidden rows owned round-robin (row r -> workgroup r mod P), W1 chunks and x
-//      in registers, fp32 dot products, relu, tagged hidden out.  Then the
-//      workgroup's W2 rows (mask words g = w, w + P, ...: 32 rows each) stream
-//      straight into LDS with 16-byte global->LDS loads.
-//   B  poll the hidden, scores of the owned rows from LDS (or from HBM when the rows
-//      do not fit), threshold, per-token and union mask words (union tagged out).
-//   C  poll the union words, scan their popcounts (the active list lands in LDS);
+//   A  hidden rows w + P s (one W1 row per wave of waves 0..3, held in registers
+//      since the previous layer), input rows staged in LDS, fp32 dot products,
+//      relu, tagged hidden out; then this layer's W2 rows (mask words g = w, w + P,
+//      ...: 32 rows each) start streaming into LDS (waves 4..6).
+//   B  read the hidden, scores of the owned rows from LDS (or from HBM when the
+//      rows do not fit), threshold, per-token and union mask words (union tagged
+//      out).
+//   C  read the union words, scan their popcounts (the active list lands in LDS);
 //      workgroup w takes active ranks [w k / P, (w+1) k / P) -- an even split of
 //      the work whatever the mask looks like -- writes idx, gathers its up (and
-//      gate) rows, applies bias and ReLU / ReGLU, tagged hact out.
-//   D  down by column tiles: workgroup w owns d/P columns (rounded to 8) of y and
-//      reads that segment of every active row (polling each row's hact), so y
-//      needs no partial sums and no atomics; the reduction order is fixed, so y is
-//      bitwise reproducible.  Tiles are mapped so workgroups sharing a 128-byte
-//      line of Wd run on one XCD.                                grid barrier
+//      gate) rows, applies bias and ReLU / ReGLU, tagged activations out.
+//   D  down by column tiles: workgroup w owns 8 or 16 columns of y and reads that
+//      segment of every active row, so y needs no partial sums and no atomics;
+//      the reduction order is fixed, so y is bitwise reproducible.  Tiles are
+//      mapped so workgroups sharing a 128-byte line of Wd run on one XCD.
+//                                                                   grid barrier
 #pragma once
 #include "sfx_common.hpp"
 #include "sfx_step.hpp"
@@ -222,19 +221,12 @@ __device__ __forceinline__ int rank_to_neuron(int r, const uint32_t* s_pref, con
 // Wave roles.  A wave's loads and stores complete in issue order, so a wave that
 // waits for a flag must have nothing slow in flight ahead of the flag loads:
 //   waves 0..3  W1 rows (registers) and phase A;
-//   waves 4..6  stream the next layer's W2 rows into LDS;
+//   waves 4..6  stream the layer's W2 rows into LDS once phase A has asked for its inputs;
 //   wave 7      the control wave: every wait for other workgroups' flags;
 //   waves 0..6  up rows and down segments.
-#ifndef SFX_PF_AT
-#define SFX_PF_AT 1
-#endif
-// When a layer's W2 rows are streamed into LDS: 0 before the previous layer's grid
-// barrier, 1 after it (once phase A has requested its input rows), 2 right after
-// the previous layer's scores (the streaming waves then take no up or down rows).
-constexpr int kPfAt = SFX_PF_AT;
 constexpr int kAW = 4;                   // waves [0, kAW): W1 rows
 constexpr int kCW = 7;                   // control wave; waves [kAW, kCW) stream W2
-constexpr int kWork = kPfAt == 2 ? kAW : kCW;   // waves [0, kWork) take up and down rows
+constexpr int kWork = kCW;               // waves [0, kWork) take up and down rows
 
 // Weights of a layer that do not depend on its input, fetched before the layer
 // starts (behind the previous layer's barrier): the W1 row of each of waves 0..3
@@ -345,7 +337,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const bool a_active = wave < p.nr1 && a_row < h;
       const uint8_t* x = (const uint8_t*)Ld->x;
       // The input rows go to LDS first (waves 0..3, 16 bytes per lane) and only
-      // then does this layer's W2 stream start (kPfAt == 1), so they are not
+      // then does this layer's W2 stream start, so they are not
       // queued behind it.  Inputs larger than the staging area are read directly.
       // Waves 0..3 synchronise among themselves (group_sync) so the streaming
       // waves, blocked while their loads issue, hold nobody up.
@@ -365,7 +357,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         group_sync(&s_grp, g0 + kAW, p.err);                  // inputs requested
         if (x_lds) wait_memory();
         group_sync(&s_grp, g0 + 2 * kAW, p.err);              // inputs landed
-      } else if (kPfAt == 1 && l > 0 && wave < kCW) {
+      } else if (l > 0 && wave < kCW) {
         lds_wait_at_least(&s_grp, g0 + kAW, p.err);
         prefetch_w2(p, Ld, s_w2);
       }
@@ -472,7 +464,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
       __syncthreads();
-      if (kPfAt == 2 && l + 1 < p.L) prefetch_w2(p, Ld + 1, s_w2);
       // mask words by wave ballots (lane = row of a 64-row pair of words), then the
       // union goes out tagged, then the scores
       for (int m0 = 2 * wave; m0 < nw2; m0 += 2 * kNW) {
@@ -704,7 +695,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       lds_barrier();
       if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
       prefetch_w1<kU>(p, (CLayer*)p.layers + l + 1, w1r);
-      if (kPfAt == 0) prefetch_w2(p, (CLayer*)p.layers + l + 1, s_w2);
       if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
       lds_barrier();
     }
