@@ -7,8 +7,8 @@
 // hands to the others (hidden values, union mask words, activations) is written as
 // 64-bit words {layer tag, value}, one agent-scope atomic store each, in a block of
 // its own per producer; readers load those words with agent-scope loads and
-// re-poll the ones whose tag is stale.  Waits on every workgroup (activations, the
-// grid barrier between layers) poll one flag per workgroup from the control wave.
+// re-poll the ones whose tag is stale.  The grid barrier between layers polls one
+// flag per workgroup from the control wave.
 // Every wait is bounded and sets an error word instead of hanging.  Per layer:
 //
 //   A  hidden rows w + P s (one W1 row per wave of waves 0..3, held in registers
@@ -171,17 +171,6 @@ __device__ __forceinline__ void wait_flags(const uint32_t* fl, int P, uint32_t t
   }
 }
 
-// Lane 0 of each of n waves calls this after issuing its tagged stores; the last
-// one raises the workgroup's flag.
-__device__ __forceinline__ void arrive(uint32_t* s_cnt, uint32_t n, uint32_t* flag, uint32_t tag) {
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    if (atomicAdd(s_cnt, 1u) == n - 1) {
-      *s_cnt = 0u;
-      store_through(flag, tag);
-    }
-  }
-}
-
 template <class T>
 __device__ __forceinline__ void dot_chunk(const uint32_t* w, const uint32_t* x, float& acc) {
   float wf[8], xf[8];
@@ -222,11 +211,11 @@ __device__ __forceinline__ int rank_to_neuron(int r, const uint32_t* s_pref, con
 // waits for a flag must have nothing slow in flight ahead of the flag loads:
 //   waves 0..3  W1 rows (registers) and phase A;
 //   waves 4..6  stream the layer's W2 rows into LDS once phase A has asked for its inputs;
-//   wave 7      the control wave: every wait for other workgroups' flags;
-//   waves 0..6  up rows and down segments.
+//   wave 7      the control wave: polls the grid-barrier flags;
+//   all waves   up rows and down segments.
 constexpr int kAW = 4;                   // waves [0, kAW): W1 rows
 constexpr int kCW = 7;                   // control wave; waves [kAW, kCW) stream W2
-constexpr int kWork = kCW;               // waves [0, kWork) take up and down rows
+constexpr int kWork = kNW;               // waves [0, kWork) take up and down rows
 
 // Weights of a layer that do not depend on its input, fetched before the layer
 // starts (behind the previous layer's barrier): the W1 row of each of waves 0..3
@@ -316,9 +305,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
 
-  __shared__ uint32_t s_cnt[2];             // arrivals: [1] hact
   __shared__ uint32_t s_grp;                 // group_sync arrivals of waves 0..3
-  if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0u;
   if (threadIdx.x == 0) s_grp = 0u;
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
@@ -605,7 +592,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           }
         }
       }
-      arrive(&s_cnt[1], kNW, p.fhact + (size_t)w * kFS, tag);
     }
 
     // ---------------------------------------------------------------- phase D
@@ -636,10 +622,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
         for (int u = 0; u < kRD; ++u) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
       };
-      // the workers' first batch goes out before the wait for the activations
+      // the workers' first batch goes out before the activations are polled
       if (d_ok && d_rr < k) load_wd(d_rr);
-      if (wave == kCW) wait_flags(p.fhact, P, tag, p.err, 5u);
-      lds_barrier();
       float yacc[NB * 8];
 #pragma unroll
       for (int i = 0; i < NB * 8; ++i) yacc[i] = 0.f;

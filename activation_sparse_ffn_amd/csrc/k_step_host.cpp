@@ -59,12 +59,12 @@ int step_union_block(int f, int P) {
   return (nw2max + 7) & ~7;
 }
 
-// control line | 2 flag arrays [P][kFlagStride] | hidden [P][16] | union [P][us] |
+// control line | barrier flags [P][kFlagStride] | hidden [P][16] | union [P][us] |
 // hact [f][B]  (tagged words: 8 bytes)
 size_t step_ws_bytes(int B, int h, int f, int P) {
   (void)h;
   const size_t fl = up256((size_t)P * kFlagStride * 4);
-  return 256 + 2 * fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P) * 8) +
+  return 256 + fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P) * 8) +
          up256((size_t)f * B * 8);
 }
 
@@ -85,8 +85,7 @@ StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layer
   p.us = step_union_block(f, g.P);
   const size_t fl = up256((size_t)g.P * kFlagStride * 4);
   p.fbar = (uint32_t*)(base + 256);
-  p.fhact = (uint32_t*)(base + 256 + fl);
-  size_t off = 256 + 2 * fl;
+  size_t off = 256 + fl;
   p.hid = (unsigned long long*)(base + off);
   off += up256((size_t)g.P * 16 * 8);
   p.uni = (unsigned long long*)(base + off);

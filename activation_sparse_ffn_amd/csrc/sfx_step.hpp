@@ -19,7 +19,6 @@ struct StepParams {
   int us;         // tagged union words per workgroup block (multiple of 8)
   uint32_t* err;               // nonzero after a wait timed out
   uint32_t* fbar;              // [P] x kFlagStride: layer done (grid barrier); holds layer tags
-  uint32_t* fhact;             // [P] x kFlagStride: activations issued; holds layer tags
   unsigned long long* hid;     // [P][16]  {tag, hidden}: rows w + P s, s < nr1, all tokens
   unsigned long long* uni;     // [P][us]  {tag, union word}: words w + P m
   unsigned long long* hact;    // [f][B]   {tag, activation} by active rank
