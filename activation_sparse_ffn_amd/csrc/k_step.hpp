@@ -254,17 +254,23 @@ __device__ __forceinline__ void prefetch_w2(const StepParams& p, CLayer* Ld, uin
     const size_t rb2 = (size_t)p.h * 2;
     const int nw2 = w < p.W ? (p.W - w + P - 1) / P : 0;
     const int items = nw2 * 32 * nch2;
+    // item i = q nch2 + c: chunk c of the workgroup's row q; (q, c) advance by the
+    // stride with a carry instead of a division per load, so issuing stays cheap
+    constexpr int kStride = (kCW - kAW) * kWave;
+    const int i_first = (wave - kAW) * kWave + lane;
+    int q = i_first / nch2, c = i_first - q * nch2;
+    const int dq = kStride / nch2, dc = kStride - dq * nch2;
 #pragma unroll 1
-    for (int i0 = (wave - kAW) * kWave; i0 < items; i0 += (kCW - kAW) * kWave) {
-      const int i = i0 + lane;
-      if (i < items) {
-        const int q = i / nch2;
-        const int c = i - q * nch2;
+    for (int i0 = (wave - kAW) * kWave; i0 < items; i0 += kStride) {
+      if (i0 + lane < items) {
         int row = 32 * (w + P * (q >> 5)) + (q & 31);
         if (row >= p.f) row = p.f - 1;       // rows past f are loaded but never used
         __builtin_amdgcn_global_load_lds((const void*)(W2 + (size_t)row * rb2 + (size_t)c * 16),
                                          (__attribute__((address_space(3))) void*)(s_w2 + (size_t)i0 * 16), 16, 0, 0);
       }
+      q += dq;
+      c += dc;
+      if (c >= nch2) { c -= nch2; ++q; }
     }
   }
 }
