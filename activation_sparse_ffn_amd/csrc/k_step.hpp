@@ -134,6 +134,10 @@ constexpr int kMaxP = 256;
 #define SFX_POLL_SLEEP 2
 #endif
 constexpr int kPollSleep = SFX_POLL_SLEEP;   // pause between flag polls, in units of 64 clocks
+#ifndef SFX_TLB_WARM
+#define SFX_TLB_WARM 1
+#endif
+constexpr bool kTlbWarm = SFX_TLB_WARM != 0;
 // Flags sit kFS words apart: flags sharing a cache line with many writers become
 // visible to other compute units much later.
 constexpr int kFS = kFlagStride;
@@ -685,6 +689,24 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       lds_barrier();
       if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
       prefetch_w1<kU>(p, (CLayer*)p.layers + l + 1, w1r);
+      if (kTlbWarm && wave == kCW - 1 && lane == 0) {
+        // one load per 2 MiB page of the next layer's weights, spread over the
+        // workgroups, so their address translations are warm when the layer starts
+        CLayer* Ln = (CLayer*)p.layers + l + 1;
+        const size_t bw1 = (size_t)h * rb1, bw2 = (size_t)f * rb2, brow = (size_t)f * rb1;
+        const size_t n1 = (bw1 + (1u << 21) - 1) >> 21, n2 = (bw2 + (1u << 21) - 1) >> 21;
+        const size_t n3 = (brow + (1u << 21) - 1) >> 21;
+        for (size_t pg = w; pg < n1 + n2 + 2 * n3; pg += P) {
+          const uint8_t* base;
+          size_t off;
+          if (pg < n1) { base = (const uint8_t*)Ln->W1; off = pg << 21; }
+          else if (pg < n1 + n2) { base = (const uint8_t*)Ln->W2; off = (pg - n1) << 21; }
+          else if (pg < n1 + n2 + n3) { base = (const uint8_t*)Ln->Wa; off = (pg - n1 - n2) << 21; }
+          else { base = (const uint8_t*)Ln->Wd; off = (pg - n1 - n2 - n3) << 21; }
+          const uint32_t v = __builtin_nontemporal_load((const uint32_t*)(base + off));
+          if (v == 0x7fc00001u && f < 0) Ld->y[0] = 0.f;   // keeps the load
+        }
+      }
       if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
       lds_barrier();
     }
