@@ -58,12 +58,21 @@ __global__ __launch_bounds__(kT) void k_compact(const float* __restrict__ scores
   const int n = blockIdx.x * kT + threadIdx.x;
   const int w0 = n >> 5;  // lanes 0 and 32 own words w0
   uint64_t uni = 0;
-  for (int b = 0; b < B; ++b) {
-    const bool m = (n < f) && (scores[(size_t)b * f + n] >= t);  // NaN compares false
-    const uint64_t bal = __ballot(m);
-    uni |= bal;
-    if (tok_bits != nullptr && (lane == 0 || lane == 32) && w0 < W)
-      tok_bits[(size_t)b * W + w0] = (uint32_t)(lane == 0 ? bal : (bal >> 32));
+  const int nc = min(n, f - 1);
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    float v[8];   // eight tokens' scores in flight together (clamped, not branched on)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = scores[(size_t)min(b0 + q, B - 1) * f + nc];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (b0 + q < B) {
+        const bool m = (n < f) && (v[q] >= t);  // NaN compares false
+        const uint64_t bal = __ballot(m);
+        uni |= bal;
+        if (tok_bits != nullptr && (lane == 0 || lane == 32) && w0 < W)
+          tok_bits[(size_t)(b0 + q) * W + w0] = (uint32_t)(lane == 0 ? bal : (bal >> 32));
+      }
+    }
   }
   if ((lane == 0 || lane == 32) && w0 < W) store_through(union_bits + w0, (uint32_t)(lane == 0 ? uni : (uni >> 32)));
 

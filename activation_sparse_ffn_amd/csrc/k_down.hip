@@ -5,7 +5,8 @@
 //   y[b][:] = sum_{j < count} hact[j][b] * Wd[idx_j][:]
 //
 // Grid = S neuron slices x T column tiles.  Workgroup (s, t) reads the tile-t
-// segment (64 lanes x LW bytes, contiguous) of every row in slice s, accumulates
+// segment (64 lanes x LW bytes, contiguous) of list rows s, s + S, s + 2S, ...
+// (the slice), with their indices and activations staged in LDS, accumulates
 // B x CPL fp32 sums per lane, adds its four waves in LDS in a fixed order and
 // writes one partial tile.  The last workgroup of a tile to finish (ticket in the
 // workspace) adds the S partials in slice order and writes y: no atomics on data,
@@ -59,7 +60,10 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   constexpr int CPL = Seg<T, LW>::cpl;
   constexpr int TW = kWave * CPL;
   constexpr bool Q4 = T::bytes == 0;
+  constexpr int CH = kWavesPerBlock * kRowsInFlight;  // rows per staged chunk
   __shared__ float s_red[kWavesPerBlock - 1][NB][TW];
+  __shared__ float s_h[CH * NB];
+  __shared__ int s_idx[CH];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -67,12 +71,10 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   const int tile = blockIdx.x % ntiles;
   const int slice = blockIdx.x / ntiles;
   const int k = min(*count, kmax);
-  const int j0 = (int)(((long long)k * slice) / S);
-  const int j1 = (int)(((long long)k * (slice + 1)) / S);
   const int col0 = tile * TW + lane * CPL;
   const bool valid = col0 < d;
   const size_t rb = RowGeom<T>::row_bytes(d);
-  const size_t cb = RowGeom<T>::col_byte(col0);
+  const size_t cb = RowGeom<T>::col_byte(valid ? col0 : 0);  // lanes past d read column 0, never store
   const int ngroup = d >> 5;
 
   float acc[NB][CPL];
@@ -81,35 +83,59 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[b][c] = 0.f;
 
-  for (int jb = j0 + wave; jb < j1; jb += kWavesPerBlock * kRowsInFlight) {
+  // Slice s takes rows j = s, s + S, s + 2S, ... (CH of them per chunk), so the
+  // first chunk's index and activation loads do not depend on the count and go
+  // out together with it.  Rows past the count are skipped; loads past kmax are
+  // clamped (idx and hact hold kmax rows).
+  int m = 0;
+  do {
+    const int jr = slice + S * m * CH;  // row of chunk entry 0; entry r is jr + S * r
+    if (threadIdx.x < CH) {
+      const int j = jr + S * (int)threadIdx.x;
+      int i = idx[min(j, kmax - 1)];
+      if (j >= k || (unsigned)i >= (unsigned)f) i = -1;
+      s_idx[threadIdx.x] = i;
+    }
+    {
+      constexpr int HQ = (CH * NB + kBlock - 1) / kBlock;
+      float hv[HQ];
+#pragma unroll
+      for (int q = 0; q < HQ; ++q) {
+        const int e = min((int)threadIdx.x + q * kBlock, CH * NB - 1);
+        const int j = jr + S * (e / NB);
+        hv[q] = hact[(size_t)min(j, kmax - 1) * B + min(e % NB, B - 1)];
+      }
+#pragma unroll
+      for (int q = 0; q < HQ; ++q) {
+        const int e = threadIdx.x + q * kBlock;
+        if (e < CH * NB) s_h[e] = hv[q];
+      }
+    }
+    __syncthreads();
+
+    // Entry r of the chunk goes to wave r mod 4; every segment load is issued
+    // before the first is used (skipped entries read row 0).
     Raw<LW> w[kRowsInFlight];
     float sc[kRowsInFlight];
-    int rows[kRowsInFlight];
+    int rowi[kRowsInFlight];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      const int j = jb + u * kWavesPerBlock;
-      int i = (j < j1) ? idx[j] : -1;
-      if ((unsigned)i >= (unsigned)f) i = -1;
-      rows[u] = i;
-      if (i >= 0 && valid) {
-        w[u] = load_raw<LW>(Wd + (size_t)i * rb + cb);
-        if (Q4) sc[u] = (float)__builtin_bit_cast(_Float16, Wd_s[(size_t)i * ngroup + (col0 >> 5)]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < LW / 4; ++q) w[u].w[q] = 0u;
-        sc[u] = 0.f;
-      }
+      const int i = s_idx[wave + u * kWavesPerBlock];
+      rowi[u] = i;
+      const size_t ir = (size_t)(i < 0 ? 0 : i);
+      w[u] = load_raw<LW>(Wd + ir * rb + cb);
+      if (Q4) sc[u] = (float)__builtin_bit_cast(_Float16, Wd_s[ir * ngroup + ((valid ? col0 : 0) >> 5)]);
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      const int j = jb + u * kWavesPerBlock;
-      if (rows[u] >= 0) {
+      if (rowi[u] >= 0) {
+        const int r = wave + u * kWavesPerBlock;
         float wf[CPL];
         Seg<T, LW>::decode(w[u], nullptr, 0, wf);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (b < B) {
-            float hv = hact[(size_t)j * B + b];
+            float hv = s_h[r * NB + b];
             if (Q4) hv *= sc[u];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[b][c] = fmaf(hv, wf[c], acc[b][c]);
@@ -117,7 +143,8 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
         }
       }
     }
-  }
+    __syncthreads();
+  } while (slice + S * (++m) * CH < k);
 
   // Combine the four waves in LDS: wave 0 + wave 1 + wave 2 + wave 3, in that order.
   if (wave > 0) {
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   acquire_agent();
 
   // Last workgroup of this tile: y = sum of the S partials in slice order.  Each
-  // thread owns 4 consecutive columns of one token and keeps up to 16 partial
+  // thread owns 4 consecutive columns of one token and keeps up to 32 partial
   // loads in flight.
   for (int e = threadIdx.x; e < B * (TW / 4); e += kBlock) {
     const int b = e / (TW / 4);
@@ -177,13 +204,13 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
     const int col = tile * TW + cc;
     if (col >= d) continue;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      float4 v[16];
+    for (int s0 = 0; s0 < S; s0 += 32) {
+      float4 v[32];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (s0 + u < S) v[u] = *reinterpret_cast<const float4*>(part + ((size_t)((s0 + u) * ntiles + tile) * B + b) * TW + cc);
+      for (int u = 0; u < 32; ++u)
+        v[u] = *reinterpret_cast<const float4*>(part + ((size_t)(min(s0 + u, S - 1) * ntiles + tile) * B + b) * TW + cc);
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         if (s0 + u < S) { sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w; }
     }
     float* yo = y + (size_t)b * d + col;

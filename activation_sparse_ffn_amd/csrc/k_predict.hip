@@ -36,27 +36,39 @@ __global__ __launch_bounds__(kBlock) void k_pred_hidden(const uint8_t* __restric
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = 0.f;
 
-  for (int c0 = 0; c0 < nchunk; c0 += kU * kWave) {
-    Raw<16> w[kU];
+  // Chunk indices are clamped, not branched on, so every load of a batch is in
+  // flight before the first is used (loads under per-chunk branches are issued
+  // one round trip at a time).
+  constexpr int KB = NB == 1 ? kU : NB == 2 ? 4 : 2;   // row chunks per lane per batch
+  constexpr int TG = NB < 4 ? NB : 4;                  // tokens whose input chunks load together
+  for (int c0 = 0; c0 < nchunk; c0 += KB * kWave) {
+    Raw<16> w[KB];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c < nchunk) w[u] = load_raw<16>(wrow + (size_t)c * 16);
-    }
+    for (int u = 0; u < KB; ++u) w[u] = load_raw<16>(wrow + (size_t)min(c0 + u * kWave + lane, nchunk - 1) * 16);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c < nchunk) {
-        float wf[T::vec];
-        unpack<T, 4>(w[u].w, wf);
+    for (int b0 = 0; b0 < NB; b0 += TG) {
+      if (b0 < B) {
+        Raw<16> xq[KB][TG];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b < B) {
-            Raw<16> xv = load_raw<16>(x + (size_t)b * row_bytes + (size_t)c * 16);
-            float xf[T::vec];
-            unpack<T, 4>(xv.w, xf);
+        for (int u = 0; u < KB; ++u) {
+          const int c = min(c0 + u * kWave + lane, nchunk - 1);
 #pragma unroll
-            for (int e = 0; e < T::vec; ++e) acc[b] = fmaf(wf[e], xf[e], acc[b]);
+          for (int t = 0; t < TG; ++t) xq[u][t] = load_raw<16>(x + (size_t)min(b0 + t, B - 1) * row_bytes + (size_t)c * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          if (c0 + u * kWave + lane < nchunk) {
+            float wf[T::vec];
+            unpack<T, 4>(w[u].w, wf);
+#pragma unroll
+            for (int t = 0; t < TG; ++t) {
+              if (b0 + t < B) {
+                float xf[T::vec];
+                unpack<T, 4>(xq[u][t].w, xf);
+#pragma unroll
+                for (int e = 0; e < T::vec; ++e) acc[b0 + t] = fmaf(wf[e], xf[e], acc[b0 + t]);
+              }
+            }
           }
         }
       }
@@ -87,37 +99,39 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const uint8_t* __restric
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
 
-  for (int c = lane; c < nchunk; c += kWave) {
-    Raw<16> w[R];
+  // Rows past f and chunks past the row end are clamped, not branched on, so the
+  // R x KC weight loads of a batch and the hidden loads are all in flight together.
+  constexpr int KC = R >= 4 ? 2 : 4;                  // chunks per lane per batch
+  for (int c0 = 0; c0 < nchunk; c0 += KC * kWave) {
+    Raw<16> w[KC][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row0 + r < f) w[r] = load_raw<16>(W2 + (size_t)(row0 + r) * row_bytes + (size_t)c * 16);
-    float wf[R][T::vec];
+    for (int u = 0; u < KC; ++u) {
+      const int c = min(c0 + u * kWave + lane, nchunk - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (row0 + r < f) unpack<T, 4>(w[r].w, wf[r]);
-      else {
-#pragma unroll
-        for (int e = 0; e < T::vec; ++e) wf[r][e] = 0.f;
-      }
+      for (int r = 0; r < R; ++r) w[u][r] = load_raw<16>(W2 + (size_t)min(row0 + r, f - 1) * row_bytes + (size_t)c * 16);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b < B) {
-        const float* hb = hid + (size_t)b * h + (size_t)c * T::vec;
-        float hv[T::vec];
+        Raw<16> hq[KC][T::vec / 4];
 #pragma unroll
-        for (int e = 0; e < T::vec; e += 4) {
-          Raw<16> q = load_raw<16>(hb + e);
-          hv[e] = __uint_as_float(q.w[0]);
-          hv[e + 1] = __uint_as_float(q.w[1]);
-          hv[e + 2] = __uint_as_float(q.w[2]);
-          hv[e + 3] = __uint_as_float(q.w[3]);
+        for (int u = 0; u < KC; ++u) {
+          const int c = min(c0 + u * kWave + lane, nchunk - 1);
+#pragma unroll
+          for (int e = 0; e < T::vec / 4; ++e) hq[u][e] = load_raw<16>(hid + (size_t)b * h + (size_t)c * T::vec + e * 4);
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int u = 0; u < KC; ++u) {
+          if (c0 + u * kWave + lane < nchunk) {
 #pragma unroll
-          for (int e = 0; e < T::vec; ++e) acc[r][b] = fmaf(wf[r][e], hv[e], acc[r][b]);
+            for (int r = 0; r < R; ++r) {
+              float wf[T::vec];
+              unpack<T, 4>(w[u][r].w, wf);
+#pragma unroll
+              for (int e = 0; e < T::vec; ++e) acc[r][b] = fmaf(wf[e], __uint_as_float(hq[u][e / 4].w[e % 4]), acc[r][b]);
+            }
+          }
+        }
       }
     }
   }

@@ -12,7 +12,7 @@ hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, i
 hipError_t launch_step_bf16(hipStream_t s, const StepParams& p, int act, int P, int DL);
 
 namespace {
-constexpr int kNT = 512, kNW = 8, kW2Bytes = 131072, kRedFloats = 1024;
+constexpr int kNT = 512, kW2Bytes = 131072, kRedFloats = 1024;
 constexpr int kXBytes = 163840 - kW2Bytes - kRedFloats * 4 - 768;
 constexpr int kMaxWords = 1024;
 }  // namespace

@@ -31,42 +31,61 @@ __global__ __launch_bounds__(kBlock) void k_up(const uint8_t* __restrict__ x, co
   const int nchunk = d / T::vec;
   const size_t row_bytes = (size_t)d * T::bytes;
 
+  // The first index is loaded before the count is known (clamped to the list's
+  // capacity), and each row's bias is loaded with its row, so no load waits on
+  // another that it does not need.
+  int i_next = idx[min(wave, kmax - 1)];
   for (int j = wave; j < k; j += nwaves) {
-    const int i = idx[j];
+    const int i = i_next;
+    i_next = idx[min(j + nwaves, kmax - 1)];
     const bool ok = (unsigned)i < (unsigned)f;
+    const float bias = (ok && ba != nullptr) ? ba[ok ? i : 0] : 0.f;
     float za[NB], zl[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
     if (ok) {
       const uint8_t* ra = Wa + (size_t)i * row_bytes;
       const uint8_t* rl = REGLU ? Wl + (size_t)i * row_bytes : nullptr;
-      for (int c0 = 0; c0 < nchunk; c0 += kU * kWave) {
-        Raw<16> wa[kU], wl[kU];
+      // Every load of a batch is issued before the first is used: chunk indices
+      // are clamped instead of branched on (in branches the compiler serialises the
+      // input loads, one round trip per chunk).
+      constexpr int KB = NB == 1 ? kU : NB == 2 ? 4 : 2;   // row chunks per lane per batch
+      constexpr int TG = NB < 4 ? NB : 4;                  // tokens whose input chunks load together
+      for (int c0 = 0; c0 < nchunk; c0 += KB * kWave) {
+        Raw<16> wa[KB], wl[KB];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int c = c0 + u * kWave + lane;
-          if (c < nchunk) {
-            wa[u] = load_raw<16>(ra + (size_t)c * 16);
-            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
-          }
+        for (int u = 0; u < KB; ++u) {
+          const int c = min(c0 + u * kWave + lane, nchunk - 1);
+          wa[u] = load_raw<16>(ra + (size_t)c * 16);
+          if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int c = c0 + u * kWave + lane;
-          if (c < nchunk) {
-            float af[T::vec], lf[T::vec];
-            unpack<T, 4>(wa[u].w, af);
-            if (REGLU) unpack<T, 4>(wl[u].w, lf);
+        for (int b0 = 0; b0 < NB; b0 += TG) {
+          if (b0 < B) {
+            Raw<16> xq[KB][TG];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              if (b < B) {
-                Raw<16> xv = load_raw<16>(x + (size_t)b * row_bytes + (size_t)c * 16);
-                float xf[T::vec];
-                unpack<T, 4>(xv.w, xf);
+            for (int u = 0; u < KB; ++u) {
+              const int c = min(c0 + u * kWave + lane, nchunk - 1);
 #pragma unroll
-                for (int e = 0; e < T::vec; ++e) {
-                  za[b] = fmaf(af[e], xf[e], za[b]);
-                  if (REGLU) zl[b] = fmaf(lf[e], xf[e], zl[b]);
+              for (int t = 0; t < TG; ++t) xq[u][t] = load_raw<16>(x + (size_t)min(b0 + t, B - 1) * row_bytes + (size_t)c * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+              if (c0 + u * kWave + lane < nchunk) {
+                float af[T::vec], lf[T::vec];
+                unpack<T, 4>(wa[u].w, af);
+                if (REGLU) unpack<T, 4>(wl[u].w, lf);
+#pragma unroll
+                for (int t = 0; t < TG; ++t) {
+                  if (b0 + t < B) {
+                    float xf[T::vec];
+                    unpack<T, 4>(xq[u][t].w, xf);
+#pragma unroll
+                    for (int e = 0; e < T::vec; ++e) {
+                      za[b0 + t] = fmaf(af[e], xf[e], za[b0 + t]);
+                      if (REGLU) zl[b0 + t] = fmaf(lf[e], xf[e], zl[b0 + t]);
+                    }
+                  }
                 }
               }
             }
@@ -80,7 +99,6 @@ __global__ __launch_bounds__(kBlock) void k_up(const uint8_t* __restrict__ x, co
       if (REGLU) zl[b] = wave_sum(zl[b]);
     }
     if (lane == 0) {
-      const float bias = (ok && ba != nullptr) ? ba[i] : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b < B) {
@@ -108,59 +126,82 @@ __global__ __launch_bounds__(kBlock) void k_up_q4(const uint8_t* __restrict__ x,
   const size_t row_bytes = (size_t)d >> 1;
   const size_t x_bytes = (size_t)d * 2;
 
+  // The first index is loaded before the count is known (clamped to the list's
+  // capacity), and each row's bias is loaded with its row, so no load waits on
+  // another that it does not need.
+  int i_next = idx[min(wave, kmax - 1)];
   for (int j = wave; j < k; j += nwaves) {
-    const int i = idx[j];
+    const int i = i_next;
+    i_next = idx[min(j + nwaves, kmax - 1)];
     const bool ok = (unsigned)i < (unsigned)f;
+    const float bias = (ok && ba != nullptr) ? ba[ok ? i : 0] : 0.f;
     float za[NB], zl[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
     if (ok) {
-      for (int g0 = 0; g0 < ngroup; g0 += 4 * kWave) {
-        Raw<16> qa[4], ql[4];
-        float sa[4], sl[4];
+      // Same batching as the fp16 rows: clamped group indices, every load of a
+      // batch in flight before the first decode.
+      constexpr int KQ = NB == 1 ? 4 : 2;   // groups per lane per batch
+      constexpr int TG = NB == 1 ? 1 : 2;   // tokens whose input groups load together
+      const uint8_t* ra = Wa + (size_t)i * row_bytes;
+      const uint8_t* rl = REGLU ? Wl + (size_t)i * row_bytes : nullptr;
+      for (int g0 = 0; g0 < ngroup; g0 += KQ * kWave) {
+        Raw<16> qa[KQ], ql[KQ];
+        float sa[KQ], sl[KQ];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int g = g0 + u * kWave + lane;
-          if (g < ngroup) {
-            qa[u] = load_raw<16>(Wa + (size_t)i * row_bytes + (size_t)g * 16);
-            sa[u] = (float)__builtin_bit_cast(_Float16, Wa_s[(size_t)i * ngroup + g]);
-            if (REGLU) {
-              ql[u] = load_raw<16>(Wl + (size_t)i * row_bytes + (size_t)g * 16);
-              sl[u] = (float)__builtin_bit_cast(_Float16, Wl_s[(size_t)i * ngroup + g]);
-            }
+        for (int u = 0; u < KQ; ++u) {
+          const int g = min(g0 + u * kWave + lane, ngroup - 1);
+          qa[u] = load_raw<16>(ra + (size_t)g * 16);
+          sa[u] = (float)__builtin_bit_cast(_Float16, Wa_s[(size_t)i * ngroup + g]);
+          if (REGLU) {
+            ql[u] = load_raw<16>(rl + (size_t)g * 16);
+            sl[u] = (float)__builtin_bit_cast(_Float16, Wl_s[(size_t)i * ngroup + g]);
           }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int g = g0 + u * kWave + lane;
-          if (g < ngroup) {
+        for (int b0 = 0; b0 < NB; b0 += TG) {
+          if (b0 < B) {
+            Raw<16> xq[KQ][TG][4];              // 32 fp16 columns of each token per group
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              if (b < B) {
-                const uint8_t* xg = x + (size_t)b * x_bytes + (size_t)g * 64;
-                float pa = 0.f, pl = 0.f;
+            for (int u = 0; u < KQ; ++u) {
+              const int g = min(g0 + u * kWave + lane, ngroup - 1);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {           // 4 words of codes = 32 columns
-                  Raw<16> xv = load_raw<16>(xg + q * 16);  // 8 fp16 = columns 8q..8q+7
-                  float xf[8];
-                  unpack<TF16, 4>(xv.w, xf);
-                  const uint32_t wa = qa[u].w[q];
+              for (int t = 0; t < TG; ++t) {
+                const uint8_t* xg = x + (size_t)min(b0 + t, B - 1) * x_bytes + (size_t)g * 64;
 #pragma unroll
-                  for (int e = 0; e < 8; ++e) {
-                    const float c = (float)((int32_t)(wa << (28 - 4 * e)) >> 28);
-                    pa = fmaf(c, xf[e], pa);
-                  }
-                  if (REGLU) {
-                    const uint32_t wl = ql[u].w[q];
+                for (int q = 0; q < 4; ++q) xq[u][t][q] = load_raw<16>(xg + q * 16);
+              }
+            }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                      const float c = (float)((int32_t)(wl << (28 - 4 * e)) >> 28);
-                      pl = fmaf(c, xf[e], pl);
+            for (int u = 0; u < KQ; ++u) {
+              if (g0 + u * kWave + lane < ngroup) {
+#pragma unroll
+                for (int t = 0; t < TG; ++t) {
+                  if (b0 + t < B) {
+                    float pa = 0.f, pl = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {       // 4 words of codes = 32 columns
+                      float xf[8];
+                      unpack<TF16, 4>(xq[u][t][q].w, xf);
+                      const uint32_t wa = qa[u].w[q];
+#pragma unroll
+                      for (int e = 0; e < 8; ++e) {
+                        const float c = (float)((int32_t)(wa << (28 - 4 * e)) >> 28);
+                        pa = fmaf(c, xf[e], pa);
+                      }
+                      if (REGLU) {
+                        const uint32_t wl = ql[u].w[q];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                          const float c = (float)((int32_t)(wl << (28 - 4 * e)) >> 28);
+                          pl = fmaf(c, xf[e], pl);
+                        }
+                      }
                     }
+                    za[b0 + t] = fmaf(sa[u], pa, za[b0 + t]);
+                    if (REGLU) zl[b0 + t] = fmaf(sl[u], pl, zl[b0 + t]);
                   }
                 }
-                za[b] = fmaf(sa[u], pa, za[b]);
-                if (REGLU) zl[b] = fmaf(sl[u], pl, zl[b]);
               }
             }
           }
@@ -173,7 +214,6 @@ __global__ __launch_bounds__(kBlock) void k_up_q4(const uint8_t* __restrict__ x,
       if (REGLU) zl[b] = wave_sum(zl[b]);
     }
     if (lane == 0) {
-      const float bias = (ok && ba != nullptr) ? ba[i] : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b < B) {
