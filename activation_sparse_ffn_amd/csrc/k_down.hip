@@ -13,6 +13,7 @@
 // and y is the same bit for bit on every run.
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
+#include "sfx_mfma.hpp"
 
 namespace sfx {
 namespace {
@@ -51,6 +52,45 @@ struct RowGeom<TQ4> {
   __device__ static size_t col_byte(int col) { return (size_t)col >> 1; }
 };
 
+// Called by every thread of a workgroup after its partial tile has been stored
+// (agent-scope stores).  The last workgroup of the tile to take the ticket adds
+// the S partials in slice order and writes y.  Each thread owns 4 consecutive
+// columns of one token and keeps up to 32 partial loads in flight.
+__device__ __forceinline__ void finish_tile(const float* __restrict__ part, uint32_t* __restrict__ tickets,
+                                            float* __restrict__ y, int B, int d, int S, int ntiles, int tile,
+                                            int TW) {
+  __shared__ int s_last;
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (take_ticket(tickets + tile) == (uint32_t)(S - 1));
+  __syncthreads();
+  if (!s_last) return;
+  acquire_agent();
+
+  for (int e = threadIdx.x; e < B * (TW / 4); e += kBlock) {
+    const int b = e / (TW / 4);
+    const int cc = (e - b * (TW / 4)) * 4;
+    const int col = tile * TW + cc;
+    if (col >= d) continue;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += 32) {
+      float4 v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        v[u] = *reinterpret_cast<const float4*>(part + ((size_t)(min(s0 + u, S - 1) * ntiles + tile) * B + b) * TW + cc);
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (s0 + u < S) { sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w; }
+    }
+    float* yo = y + (size_t)b * d + col;
+    yo[0] = sum.x;
+    if (col + 1 < d) yo[1] = sum.y;
+    if (col + 2 < d) yo[2] = sum.z;
+    if (col + 3 < d) yo[3] = sum.w;
+  }
+  if (threadIdx.x == 0) tickets[tile] = 0u;
+}
+
 template <class T, int NB, int LW>
 __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd, const uint16_t* __restrict__ Wd_s,
                                                  const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
@@ -64,7 +104,6 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   __shared__ float s_red[kWavesPerBlock - 1][NB][TW];
   __shared__ float s_h[CH * NB];
   __shared__ int s_idx[CH];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -90,14 +129,10 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   int m = 0;
   do {
     const int jr = slice + S * m * CH;  // row of chunk entry 0; entry r is jr + S * r
-    if (threadIdx.x < CH) {
-      const int j = jr + S * (int)threadIdx.x;
-      int i = idx[min(j, kmax - 1)];
-      if (j >= k || (unsigned)i >= (unsigned)f) i = -1;
-      s_idx[threadIdx.x] = i;
-    }
     {
       constexpr int HQ = (CH * NB + kBlock - 1) / kBlock;
+      const int jt = jr + S * min((int)threadIdx.x, CH - 1);
+      const int it = idx[min(jt, kmax - 1)];          // issued with the activation loads
       float hv[HQ];
 #pragma unroll
       for (int q = 0; q < HQ; ++q) {
@@ -105,11 +140,13 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
         const int j = jr + S * (e / NB);
         hv[q] = hact[(size_t)min(j, kmax - 1) * B + min(e % NB, B - 1)];
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < HQ; ++q) {
         const int e = threadIdx.x + q * kBlock;
         if (e < CH * NB) s_h[e] = hv[q];
       }
+      if (threadIdx.x < CH) s_idx[threadIdx.x] = (jt >= k || (unsigned)it >= (unsigned)f) ? -1 : it;
     }
     __syncthreads();
 
@@ -126,6 +163,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
       w[u] = load_raw<LW>(Wd + ir * rb + cb);
       if (Q4) sc[u] = (float)__builtin_bit_cast(_Float16, Wd_s[ir * ngroup + ((valid ? col0 : 0) >> 5)]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       if (rowi[u] >= 0) {
@@ -188,38 +226,140 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   }
   if (S == 1) return;
 
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (take_ticket(tickets + tile) == (uint32_t)(S - 1));
-  __syncthreads();
-  if (!s_last) return;
-  acquire_agent();
+  finish_tile(part, tickets, y, B, d, S, ntiles, tile, TW);
+}
 
-  // Last workgroup of this tile: y = sum of the S partials in slice order.  Each
-  // thread owns 4 consecutive columns of one token and keeps up to 32 partial
-  // loads in flight.
-  for (int e = threadIdx.x; e < B * (TW / 4); e += kBlock) {
-    const int b = e / (TW / 4);
-    const int cc = (e - b * (TW / 4)) * 4;
-    const int col = tile * TW + cc;
-    if (col >= d) continue;
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < S; s0 += 32) {
-      float4 v[32];
+
+// ------------------------------------------------------------------ B >= 8
+// From 8 tokens on the products run on the matrix cores: v_mfma_f32_16x16x4_f32
+// (fp32 operands, so the fp32 activations are used as they are and the 16-bit
+// weights convert exactly).  A = 16 column slots x 4 list entries: lane l reads 16
+// bytes (8 consecutive columns) of entry l / 16's row at column slot l % 16, which
+// gives the A operand of 8 products, one per column of the slot; B = 4 list
+// entries x 16 tokens, lane l holding the activation of entry l / 16 for token
+// l % 16.  A tile is 128 columns (16 slots x 8) by all tokens.  Grid, slices,
+// partial tiles and the fixed-order final sum are those of the kernel above;
+// a slice takes groups of 4 list entries g = s, s + S, ..., its four waves every
+// fourth of them, U groups in flight per wave, the next batch's indices and
+// activations loading while the current batch's rows are multiplied.
+constexpr int kMfmaTW = 128;
+
+template <class T, int NT>
+__global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict__ Wd,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ count, int kmax,
+                                                      const float* __restrict__ hact, int B, int d, int f,
+                                                      float* __restrict__ y, float* __restrict__ part,
+                                                      uint32_t* __restrict__ tickets, int S, int ntiles) {
+  constexpr int TW = kMfmaTW;
+  constexpr int U = NT <= 2 ? 8 : 4;
+  __shared__ f32x4 s_red[kWavesPerBlock - 1][8][NT][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x % ntiles;
+  const int slice = blockIdx.x / ntiles;
+  const int k = min(*count, kmax);
+  const int ng = (k + 3) >> 2;
+  const int r = lane >> 4;                        // list entry of this lane within a group
+  const int col = tile * TW + 8 * (lane & 15);    // first of this lane's 8 columns
+  const bool cvalid = col < d;
+  const size_t rb = (size_t)d * 2;
+  const size_t cb = (size_t)(cvalid ? col : 0) * 2;
+
+  f32x4 acc[8][NT];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        v[u] = *reinterpret_cast<const float4*>(part + ((size_t)(min(s0 + u, S - 1) * ntiles + tile) * B + b) * TW + cc);
+  for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (s0 + u < S) { sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w; }
+    for (int n = 0; n < NT; ++n) acc[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Metadata of one batch: list entry, its index and its activations (raw loads,
+  // clamped; validity is applied when the batch is used).
+  int jm[U], im[U];
+  float hm[U][NT];
+  auto load_meta = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long g = (long long)slice + (long long)S * (t0 + 4 * u);
+      const int j = (int)min(g * 4 + r, (long long)kmax);   // kmax marks "past the list"
+      const int jc = min(j, kmax - 1);
+      jm[u] = j;
+      im[u] = idx[jc];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) hm[u][n] = hact[(size_t)jc * B + min(n * 16 + (lane & 15), B - 1)];
     }
-    float* yo = y + (size_t)b * d + col;
-    yo[0] = sum.x;
-    if (col + 1 < d) yo[1] = sum.y;
-    if (col + 2 < d) yo[2] = sum.z;
-    if (col + 3 < d) yo[3] = sum.w;
+  };
+  load_meta(wave);
+  for (int t0 = wave; slice + (long long)S * t0 < ng; t0 += 4 * U) {
+    int iv[U];
+    float hv[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = jm[u] < k && (unsigned)im[u] < (unsigned)f;
+      iv[u] = ok ? im[u] : -1;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) hv[u][n] = (ok && n * 16 + (lane & 15) < B) ? hm[u][n] : 0.f;
+    }
+    Raw<16> w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = load_raw<16>(Wd + (size_t)(iv[u] < 0 ? 0 : iv[u]) * rb + cb);
+    load_meta(t0 + 4 * U);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a[8];
+      unpack<T, 4>(w[u].w, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ae = iv[u] < 0 ? 0.f : a[e];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[e][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(ae, hv[u][n], acc[e][n], 0, 0, 0);
+      }
+    }
   }
-  if (threadIdx.x == 0) tickets[tile] = 0u;
+
+  // Waves 1..3 to LDS; wave 0 adds them in wave order.  D layout: lane l holds
+  // slots 4 (l / 16) + i for token l % 16; slot m, product e is column 8 m + e.
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s_red[wave - 1][e][n][lane] = acc[e][n];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll 1
+    for (int v = 0; v < kWavesPerBlock - 1; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[e][n] += s_red[v][e][n][lane];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int b = n * 16 + (lane & 15);
+      if (b >= B) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tile * TW + 8 * (4 * r + i);     // 8 consecutive columns c .. c + 7
+        if (c >= d) continue;
+        const float4 lo = make_float4(acc[0][n][i], acc[1][n][i], acc[2][n][i], acc[3][n][i]);
+        const float4 hi = make_float4(acc[4][n][i], acc[5][n][i], acc[6][n][i], acc[7][n][i]);
+        if (S == 1) {
+          float4* yo = reinterpret_cast<float4*>(y + (size_t)b * d + c);
+          yo[0] = lo;
+          yo[1] = hi;
+        } else {
+          float* p = part + ((size_t)(slice * ntiles + tile) * B + b) * TW + (c - tile * TW);
+          store_through2(p + 0, lo.x, lo.y);
+          store_through2(p + 2, lo.z, lo.w);
+          store_through2(p + 4, hi.x, hi.y);
+          store_through2(p + 6, hi.z, hi.w);
+        }
+      }
+    }
+  }
+  (void)cvalid;
+  if (S == 1) return;
+  finish_tile(part, tickets, y, B, d, S, ntiles, tile, TW);
 }
 
 // Load width (bytes per lane per row) for a storage type and token class: keep
@@ -230,9 +370,27 @@ constexpr int lw_for(int nb) {
                        : (nb * (16 / T::bytes) <= 64 ? 16 : nb * (8 / T::bytes) <= 64 ? 8 : 4);
 }
 
-struct Plan { int lw, cpl, tw, ntiles, S; };
+struct Plan { int lw, cpl, tw, ntiles, S; bool mfma; };
+
+bool down_mfma_eligible(int wdt, int B) { return (wdt == DT_F16 || wdt == DT_BF16) && B >= 8 && B <= 64; }
 
 Plan plan_for(int wdt, int B, int d, int kmax) {
+  if (down_mfma_eligible(wdt, B)) {
+    Plan p;
+    p.mfma = true;
+    p.lw = 16;
+    p.cpl = 8;
+    p.tw = kMfmaTW;
+    p.ntiles = (d + p.tw - 1) / p.tw;
+    int S = 2 * kTargetBlocks / p.ntiles;
+    if (S > kMaxSlices) S = kMaxSlices;
+    const int groups = (kmax + 3) / 4;
+    const int cap = (groups + kWavesPerBlock - 1) / kWavesPerBlock;   // >= one group per wave
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    p.S = S;
+    return p;
+  }
   const int nb = nb_class(B);
   int lw = 16, cpl = 4;
   switch (wdt) {
@@ -242,6 +400,7 @@ Plan plan_for(int wdt, int B, int d, int kmax) {
     default: lw = lw_for<TQ4>(nb); cpl = lw * 2; break;
   }
   Plan p;
+  p.mfma = false;
   p.lw = lw;
   p.cpl = cpl;
   p.tw = kWave * cpl;
@@ -268,9 +427,27 @@ hipError_t run(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd
   return hipGetLastError();
 }
 
+template <class T, int NT>
+hipError_t run_mfma(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd, const int32_t* idx,
+                    const int32_t* count, int kmax, const float* hact, float* y, void* ws) {
+  uint32_t* tickets = (uint32_t*)ws;
+  const size_t tick_bytes = ((size_t)p.ntiles * 4 + 255) & ~(size_t)255;
+  float* part = (float*)((uint8_t*)ws + tick_bytes);
+  k_down_mfma<T, NT><<<dim3(p.S * p.ntiles), dim3(kBlock), 0, s>>>((const uint8_t*)Wd, idx, count, kmax, hact, B,
+                                                                   d, f, y, part, tickets, p.S, p.ntiles);
+  return hipGetLastError();
+}
+
 template <class T>
 hipError_t dispatch(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd, const void* Wd_s,
                     const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y, void* ws) {
+  if constexpr (T::bytes == 2) {
+    if (p.mfma) {
+      if (B <= 16) return run_mfma<T, 1>(s, p, B, d, f, Wd, idx, count, kmax, hact, y, ws);
+      if (B <= 32) return run_mfma<T, 2>(s, p, B, d, f, Wd, idx, count, kmax, hact, y, ws);
+      return run_mfma<T, 4>(s, p, B, d, f, Wd, idx, count, kmax, hact, y, ws);
+    }
+  }
   switch (nb_class(B)) {
     case 1: return run<T, 1>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
     case 2: return run<T, 2>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);

@@ -14,6 +14,12 @@
 #include "sfx_launch.hpp"
 
 namespace sfx {
+
+bool up_mfma_eligible(int wdt, int B, int d);
+hipError_t launch_up_mfma(hipStream_t s, int wdt, int act, int B, int d, int f, const void* x, const void* Wa,
+                          const float* ba, const void* Wl, const int32_t* idx, const int32_t* count, int kmax,
+                          float* hact);
+
 namespace {
 
 constexpr int kU = 8;         // 16-byte chunks per lane issued together
@@ -289,6 +295,7 @@ hipError_t launch_up(hipStream_t s, int wdt, int act, int B, int d, int f, const
                      const void* Wa, const void* Wa_s, const float* ba, const void* Wl,
                      const void* Wl_s, const int32_t* idx, const int32_t* count, int kmax,
                      float* hact) {
+  if (up_mfma_eligible(wdt, B, d)) return launch_up_mfma(s, wdt, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
   switch (wdt) {
     case DT_F32: return dispatch<TF32>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
     case DT_F16: return dispatch<TF16>(s, act, B, d, f, x, Wa, ba, Wl, idx, count, kmax, hact);
