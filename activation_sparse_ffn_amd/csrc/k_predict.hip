@@ -6,7 +6,7 @@
 // read once and feeds B multiply-adds.  Layer 1 gives one wave per hidden row;
 // layer 2 gives each wave R rows of W2, so a lane keeps R 16-byte loads in flight
 // per chunk.  The hidden vector is kept in fp32 (workspace), never rounded to the
-// weight type.  From B = 16 on (fp16 / bf16) both layers are dense contractions
+// weight type.  From B = 8 on (fp16 / bf16) both layers are dense contractions
 // and run on the matrix cores (k_predict_mfma.hip).
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
@@ -14,8 +14,9 @@
 namespace sfx {
 
 hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
-                            const void* W2, float* hid, float* scores);
+                            const void* W2, void* ws, float* scores);
 bool pred_mfma_eligible(int wdt, int B, int h, int f);
+size_t pred_mfma_ws_bytes(int wdt, int B, int h);
 
 namespace {
 
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const uint8_t* __restric
 template <class T, int NB>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
                const void* W2, float* scores, float* hid, bool mfma, int wdt) {
-  if (mfma) return launch_pred_mfma(s, wdt, B, d, h, f, x, W1, W2, hid, scores);
+  if (mfma) return launch_pred_mfma(s, wdt, B, d, h, f, x, W1, W2, hid, scores);   // hid = the pieces buffer
   dim3 blk(kBlock);
   k_pred_hidden<T, NB><<<dim3((h + kWavesPerBlock - 1) / kWavesPerBlock), blk, 0, s>>>(
       (const uint8_t*)x, (const uint8_t*)W1, hid, B, d, h);
@@ -179,8 +180,9 @@ hipError_t dispatch_nb(hipStream_t s, int B, int d, int h, int f, const void* x,
 }  // namespace
 
 size_t predict_ws_bytes(int wdt, int B, int d, int h, int f) {
-  (void)wdt; (void)d; (void)f;
-  const size_t hid = (size_t)B * h * sizeof(float);
+  (void)d;
+  size_t hid = (size_t)B * h * sizeof(float);
+  if (pred_mfma_eligible(wdt, B, h, f)) hid = pred_mfma_ws_bytes(wdt, B, h);
   return (hid + 255) & ~(size_t)255;
 }
 

@@ -1,6 +1,6 @@
-// Per-layer predictor on the matrix cores for B >= 16 tokens (PowerInfer page,
-// Method, per-layer predictor of §5.1).  From 16 tokens on, each predictor weight
-// feeds >= 16 multiply-adds and the two layers are dense contractions:
+// Per-layer predictor on the matrix cores for B >= 8 tokens (PowerInfer page,
+// Method, per-layer predictor of §5.1).  From 8 tokens on, each predictor weight
+// feeds >= 8 multiply-adds and the two layers are dense contractions:
 //
 //   layer 1   hidden[b][j] = max(sum_c W1[j][c] x[b][c], 0)       W1, x: fp16 / bf16
 //   layer 2   scores[b][i] = sum_j W2[i][j] hidden[b][j]           hidden: fp32
@@ -12,6 +12,10 @@
 // (22 significant bits, lo scaled so it does not fall into fp16 subnormals);
 // bf16 weights: hidden = hi + mid + lo, three bf16 terms (24 bits, exact for
 // normal values).  Products of two 16-bit values are exact in fp32 (sfx_mfma.hpp).
+//
+// Layer 1 writes the pieces once, already in layer 2's B-operand layout
+// (hp[piece][token][hidden row], 16-bit), so layer 2 streams W2 and reads its B
+// fragments with plain 16-byte loads: no LDS staging and no barriers in its loop.
 #include "sfx_launch.hpp"
 #include "sfx_mfma.hpp"
 
@@ -19,42 +23,48 @@ namespace sfx {
 namespace {
 
 // ------------------------------------------------------------------ layer 1
-// Workgroup = one tile of 16 W1 rows; its 8 waves take interleaved 32-wide k
-// steps; partial tiles are added in wave order in LDS.
-constexpr int kHW = 8;
+// Workgroup = one tile of 16 W1 rows; its 16 waves take interleaved 32-wide k
+// steps (kHU in flight each); every wave's partial tile goes to LDS, and wave n
+// adds token tile n's partials in wave order, applies the ReLU and stores the
+// pieces (pad tokens past B store 0).
+constexpr int kHW = 16;
+constexpr int kHU = 4;
 
 template <class T, int NT>
 __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __restrict__ x,
                                                             const uint8_t* __restrict__ W1,
-                                                            float* __restrict__ hid, int B, int d, int h) {
+                                                            uint16_t* __restrict__ hp, int B, int d, int h) {
+  constexpr int NP = Split<T>::pieces;
   __shared__ f32x4 s_acc[kHW][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * 16;
-  const int r = row0 + (lane & 15);
+  const int r = min(row0 + (lane & 15), h - 1);      // rows past h read row h - 1, never stored
   const int kq = (lane >> 4) * 8;
-  const int nsteps = (d + 31) / 32;
+  const int nsteps = (d + 31) >> 5;
+  const uint8_t* ar = W1 + (size_t)r * d * 2;
+  const uint8_t* xr[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) xr[n] = x + (size_t)min(n * 16 + (lane & 15), B - 1) * d * 2;
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
-  for (int s0 = wave; s0 < nsteps; s0 += kHW * U) {
-    Raw<16> a[U], bx[U][NT];
+  for (int s0 = wave; s0 < nsteps; s0 += kHW * kHU) {
+    Raw<16> a[kHU], bx[kHU][NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (s0 + u * kHW) * 32 + kq;
-      const bool kin = (s0 + u * kHW) < nsteps && k < d;
-      a[u] = (kin && r < h) ? load_raw<16>(W1 + ((size_t)r * d + k) * 2) : zero16();
+    for (int u = 0; u < kHU; ++u) {
+      const size_t off = (size_t)min((s0 + u * kHW) * 32 + kq, d - 8) * 2;
+      a[u] = load_raw<16>(ar + off);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int tok = n * 16 + (lane & 15);
-        bx[u][n] = (kin && tok < B) ? load_raw<16>(x + ((size_t)tok * d + k) * 2) : zero16();
-      }
+      for (int n = 0; n < NT; ++n) bx[u][n] = load_raw<16>(xr[n] + off);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < kHU; ++u) {
+      if ((s0 + u * kHW) * 32 + kq >= d) a[u] = zero16();   // steps and columns past d add nothing
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = Mma<T>::run(a[u], bx[u][n], acc[n]);
+    }
   }
 #pragma unroll
   for (int n = 0; n < NT; ++n) s_acc[wave][n][lane] = acc[n];
@@ -63,71 +73,75 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
     const int n = wave;
     f32x4 t = s_acc[0][n][lane];
     for (int v = 1; v < kHW; ++v) t += s_acc[v][n][lane];
+    // D layout: lane l holds rows 4 (l / 16) + i of the tile for token l % 16.
     const int tok = n * 16 + (lane & 15);
+    const size_t tstride = (size_t)NT * 16 * h;   // one piece plane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + (lane >> 4) * 4 + i;
-      if (tok < B && row < h) hid[(size_t)tok * h + row] = fmaxf(t[i], 0.f);
+      if (row < h) {
+        uint16_t pc[NP];
+        Split<T>::run(tok < B ? fmaxf(t[i], 0.f) : 0.f, pc);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) hp[p * tstride + (size_t)tok * h + row] = pc[p];
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ layer 2
-// Workgroup = 8 waves x one 16-row tile of W2 each (128 rows); the fp32 hidden of
-// all tokens is split into 16-bit pieces in LDS, KC columns at a time.
-constexpr int kSW = 8;
-constexpr int kKC = 256;                 // k columns per LDS chunk
-constexpr int kPad = 8;                  // halves of padding per token row (bank spread)
-constexpr int kStride = kKC + kPad;
+// Each wave owns one tile of 16 W2 rows and walks all h columns in 32-wide steps,
+// kSU steps in flight: per step one 16-byte W2 load and NT x pieces 16-byte piece
+// loads per lane (the pieces are small and shared by every wave: cache hits).
+constexpr int kSWB = 4;   // waves (row tiles) per workgroup
+constexpr int kSU = 4;
 
 template <class T, int NT>
-__global__ __launch_bounds__(kSW * kWave) void k_scores_mfma(const uint8_t* __restrict__ W2,
-                                                            const float* __restrict__ hid,
-                                                            float* __restrict__ scores, int B, int h, int f) {
+__global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __restrict__ W2,
+                                                             const uint16_t* __restrict__ hp,
+                                                             float* __restrict__ scores, int B, int h, int f) {
   constexpr int NP = Split<T>::pieces;
-  __shared__ __attribute__((aligned(16))) uint16_t s_h[NP][NT * 16][kStride];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
-  const int row0 = blockIdx.x * (kSW * 16) + wave * 16;
-  const int r = row0 + (lane & 15);
+  constexpr int NACC = Split<T>::accumulators;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * kSWB + wave) * 16;
+  if (row0 >= f) return;
+  const int r = min(row0 + (lane & 15), f - 1);
   const int kq = (lane >> 4) * 8;
-  f32x4 acc[NP == 2 ? 2 : 1][NT];
+  const int nsteps = (h + 31) >> 5;
+  const uint8_t* ar = W2 + (size_t)r * h * 2;
+  const size_t tstride = (size_t)NT * 16 * h;
+  const uint16_t* br[NT];
 #pragma unroll
-  for (int p = 0; p < (NP == 2 ? 2 : 1); ++p)
+  for (int n = 0; n < NT; ++n) br[n] = hp + (size_t)(n * 16 + (lane & 15)) * h;
+  f32x4 acc[NACC][NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[p][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NACC; ++q)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < h; kc += kKC) {
-    // issue this chunk's W2 loads first; they stream while the hidden is split
-    Raw<16> a[kKC / 32];
+  for (int s0 = 0; s0 < nsteps; s0 += kSU) {
+    Raw<16> a[kSU], b[kSU][NT][NP];
 #pragma unroll
-    for (int s = 0; s < kKC / 32; ++s) {
-      const int k = kc + s * 32 + kq;
-      a[s] = (r < f && k < h) ? load_raw<16>(W2 + ((size_t)r * h + k) * 2) : zero16();
+    for (int u = 0; u < kSU; ++u) {
+      const int c = min((s0 + u) * 32 + kq, h - 8);
+      a[u] = load_raw<16>(ar + (size_t)c * 2);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) b[u][n][p] = load_raw<16>(br[n] + p * tstride + c);
     }
-    __syncthreads();                        // previous chunk's pieces are consumed
-    for (int i = tid; i < NT * 16 * kKC; i += kSW * kWave) {
-      const int tok = i / kKC, j = i - tok * kKC;
-      const float v = (tok < B && kc + j < h) ? hid[(size_t)tok * h + kc + j] : 0.f;
-      uint16_t pc[NP];
-      Split<T>::run(v, pc);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int p = 0; p < NP; ++p) s_h[p][tok][j] = pc[p];
-    }
-    __syncthreads();
+    for (int u = 0; u < kSU; ++u) {
+      if ((s0 + u) * 32 + kq >= h) a[u] = zero16();        // steps and columns past h add nothing
 #pragma unroll
-    for (int s = 0; s < kKC / 32; ++s) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int tok = n * 16 + (lane & 15);
+      for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const Raw<16> b = *reinterpret_cast<const Raw<16>*>(&s_h[p][tok][s * 32 + kq]);
-          const int ai = NP == 2 ? p : 0;
-          acc[ai][n] = Mma<T>::run(a[s], b, acc[ai][n]);
+          const int q = NACC == 1 ? 0 : p;
+          acc[q][n] = Mma<T>::run(a[u], b[u][n][p], acc[q][n]);
         }
-      }
     }
   }
 #pragma unroll
@@ -136,8 +150,7 @@ __global__ __launch_bounds__(kSW * kWave) void k_scores_mfma(const uint8_t* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + (lane >> 4) * 4 + i;
-      float v = acc[0][n][i];
-      if (NP == 2) v += acc[NP == 2 ? 1 : 0][n][i] * (1.0f / 2048.0f);
+      const float v = Split<T>::combine(acc[0][n][i], acc[NACC - 1][n][i]);
       if (tok < B && row < f) scores[(size_t)tok * f + row] = v;
     }
   }
@@ -145,33 +158,40 @@ __global__ __launch_bounds__(kSW * kWave) void k_scores_mfma(const uint8_t* __re
 
 template <class T, int NT>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-               float* hid, float* scores) {
+               uint16_t* hp, float* scores) {
   k_hidden_mfma<T, NT><<<dim3((h + 15) / 16), dim3(kHW * kWave), 0, s>>>((const uint8_t*)x, (const uint8_t*)W1,
-                                                                           hid, B, d, h);
-  k_scores_mfma<T, NT><<<dim3((f + kSW * 16 - 1) / (kSW * 16)), dim3(kSW * kWave), 0, s>>>(
-      (const uint8_t*)W2, hid, scores, B, h, f);
+                                                                           hp, B, d, h);
+  k_scores_mfma<T, NT><<<dim3((f + kSWB * 16 - 1) / (kSWB * 16)), dim3(kSWB * kWave), 0, s>>>(
+      (const uint8_t*)W2, hp, scores, B, h, f);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t dispatch(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-                    float* hid, float* scores) {
-  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hid, scores);
-  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hid, scores);
-  return run<T, 4>(s, B, d, h, f, x, W1, W2, hid, scores);
+                    uint16_t* hp, float* scores) {
+  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hp, scores);
+  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hp, scores);
+  return run<T, 4>(s, B, d, h, f, x, W1, W2, hp, scores);
 }
 
 }  // namespace
 
 bool pred_mfma_eligible(int wdt, int B, int h, int f) {
   (void)h; (void)f;
-  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 16 && B <= 64;
+  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 8 && B <= 64;
+}
+
+// Bytes of the pieces buffer: pieces x (16 x token tiles) x h halves.
+size_t pred_mfma_ws_bytes(int wdt, int B, int h) {
+  const int np = wdt == DT_BF16 ? Split<TBF16>::pieces : Split<TF16>::pieces;
+  const int nt = B <= 16 ? 1 : B <= 32 ? 2 : 4;
+  return (size_t)np * nt * 16 * h * sizeof(uint16_t);
 }
 
 hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
-                            const void* W2, float* hid, float* scores) {
-  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, hid, scores);
-  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, hid, scores);
+                            const void* W2, void* ws, float* scores) {
+  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, (uint16_t*)ws, scores);
+  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, (uint16_t*)ws, scores);
 }
 
 }  // namespace sfx

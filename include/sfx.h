@@ -91,8 +91,10 @@ int sfx_abi_version(void);
  *   scores  [B][f] fp32, written.
  *   ws      >= sfx_predict_ws(wdt, B, d, h, f) bytes.
  * Rows: d*sizeof(wdt) and h*sizeof(wdt) must be multiples of 16 bytes.
- * B >= 16 runs the second layer on the matrix cores with the hidden vector split
- * into two half-precision terms, so scores keep fp32 accuracy.
+ * From B = 8 on (fp16 / bf16) both layers run on the matrix cores; the second
+ * takes the fp32 hidden as exact 16-bit pieces (two fp16 or three bf16 terms),
+ * so scores keep fp32 accuracy.  The workspace then holds those pieces for
+ * 16 * ceil(B / 16) tokens; below 8 tokens it holds the fp32 hidden [B][h].
  * ------------------------------------------------------------------------------- */
 size_t sfx_predict_ws(int wdt, int B, int d, int h, int f);
 int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
@@ -138,7 +140,8 @@ int sfx_compact(void* stream, int B, int f, const float* scores, float threshold
  *                  [0, f)); count is read on the device and clamped to kmax; an
  *                  index outside [0, f) yields a zero activation.
  *   hact     [kmax][B] fp32; rows j < count are written, the rest are unchanged.
- * Q4 requires d % 32 == 0.
+ * Q4 requires d % 32 == 0.  From B = 8 on, fp16 / bf16 rows are multiplied on the
+ * matrix cores (exact 16-bit products, fp32 sums).
  * ------------------------------------------------------------------------------- */
 int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f,
                   const void* x, const void* Wa, const void* Wa_scales, const float* ba,
@@ -155,6 +158,8 @@ int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f,
  * The neurons are split into slices; each slice's partial sum goes to the
  * workspace and the last slice to finish a column tile adds the partials in slice
  * order, so y is bitwise reproducible.  y is overwritten (zero when count = 0).
+ * From B = 8 on, fp16 / bf16 rows are multiplied on the matrix cores in fp32
+ * (16x16x4 fp32 products, the activations used as they are).
  *
  *   Wd        [f][d] wdt, row = neuron (Q4: packed codes); Wd_scales as for Wa.
  *   idx, count, kmax, hact   as produced by sfx_compact / sfx_sparse_up.

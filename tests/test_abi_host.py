@@ -117,7 +117,13 @@ def test_workspace_queries_are_monotone(lib):
     a = lib.sfx_sparse_down_ws(1, 1, 4096, 16384)
     b = lib.sfx_sparse_down_ws(1, 8, 4096, 16384)
     assert b > a
-    assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == 8 * 1024 * 4
+    # below 8 tokens (and for fp32 weights) the fp32 hidden [B][h]; from 8 tokens on
+    # (fp16 / bf16) its exact 16-bit pieces for 16 tokens per matrix-core tile
+    assert lib.sfx_predict_ws(1, 4, 4096, 1024, 16384) == 4 * 1024 * 4
+    assert lib.sfx_predict_ws(0, 8, 4096, 1024, 16384) == 8 * 1024 * 4
+    assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == 2 * 16 * 1024 * 2
+    assert lib.sfx_predict_ws(2, 8, 4096, 1024, 16384) == 3 * 16 * 1024 * 2
+    assert lib.sfx_predict_ws(1, 17, 4096, 1024, 16384) == 2 * 32 * 1024 * 2
     assert lib.sfx_predict_ws(1, 0, 4096, 1024, 16384) == 0
 
 
