@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
 // l % 16.  A tile is 128 columns (16 slots x 8) by all tokens.  Grid, slices,
 // partial tiles and the fixed-order final sum are those of the kernel above;
 // a slice takes groups of 4 list entries g = s, s + S, ..., its four waves every
-// fourth of them, U groups in flight per wave, the next batch's indices and
-// activations loading while the current batch's rows are multiplied.
+// fourth of them, in batches of U groups: while a batch is multiplied the next
+// batch's rows and the batch after that's indices and activations are loading.
 constexpr int kMfmaTW = 128;
 
 template <class T, int NT>
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict_
   constexpr int U = NT <= 2 ? 8 : 4;
   __shared__ f32x4 s_red[kWavesPerBlock - 1][8][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = blockIdx.x % ntiles;
   const int slice = blockIdx.x / ntiles;
   const int k = min(*count, kmax);
@@ -272,38 +272,39 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict_
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Metadata of one batch: list entry, its index and its activations (raw loads,
-  // clamped; validity is applied when the batch is used).
-  int jm[U], im[U];
-  float hm[U][NT];
-  auto load_meta = [&](int t0) {
+  // Software pipeline over batches of U groups.  Metadata of a batch (list entry,
+  // index, activations: raw clamped loads) goes out two batches ahead and its rows
+  // one batch ahead, in the order M(i+2), W(i+1) before batch i is multiplied, so
+  // the in-order memory counter lets the products of batch i start while W(i+1)
+  // and M(i+2) are still in flight.
+  struct Meta { int j[U], i[U]; float h[U][NT]; };
+  auto load_meta = [&](Meta& m, int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long long g = (long long)slice + (long long)S * (t0 + 4 * u);
       const int j = (int)min(g * 4 + r, (long long)kmax);   // kmax marks "past the list"
       const int jc = min(j, kmax - 1);
-      jm[u] = j;
-      im[u] = idx[jc];
+      m.j[u] = j;
+      m.i[u] = idx[jc];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) hm[u][n] = hact[(size_t)jc * B + min(n * 16 + (lane & 15), B - 1)];
+      for (int n = 0; n < NT; ++n) m.h[u][n] = hact[(size_t)jc * B + min(n * 16 + (lane & 15), B - 1)];
     }
   };
-  load_meta(wave);
-  for (int t0 = wave; slice + (long long)S * t0 < ng; t0 += 4 * U) {
-    int iv[U];
-    float hv[U][NT];
+  // Validity of a batch: rows past the count or out of [0, f) multiply as zeros
+  // (their A and B operands are zero) and load row 0.
+  auto settle = [&](const Meta& m, int (&iv)[U], float (&hv)[U][NT], Raw<16> (&w)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = jm[u] < k && (unsigned)im[u] < (unsigned)f;
-      iv[u] = ok ? im[u] : -1;
+      const bool ok = m.j[u] < k && (unsigned)m.i[u] < (unsigned)f;
+      iv[u] = ok ? m.i[u] : -1;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) hv[u][n] = (ok && n * 16 + (lane & 15) < B) ? hm[u][n] : 0.f;
+      for (int n = 0; n < NT; ++n) hv[u][n] = (ok && n * 16 + (lane & 15) < B) ? m.h[u][n] : 0.f;
     }
-    Raw<16> w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = load_raw<16>(Wd + (size_t)(iv[u] < 0 ? 0 : iv[u]) * rb + cb);
-    load_meta(t0 + 4 * U);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto multiply = [&](const int (&iv)[U], const float (&hv)[U][NT], const Raw<16> (&w)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float a[8];
@@ -312,9 +313,33 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict_
       for (int e = 0; e < 8; ++e) {
         const float ae = iv[u] < 0 ? 0.f : a[e];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[e][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(ae, hv[u][n], acc[e][n], 0, 0, 0);
+        for (int n = 0; n < NT; ++n)
+          acc[e][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(ae, hv[u][n], acc[e][n], 0, 0, 0);
       }
     }
+  };
+  // Two register sets used in turn (no copies between batches: a copy of a loaded
+  // register would wait for its load).
+  Meta mA, mB;
+  int ivA[U], ivB[U];
+  float hvA[U][NT], hvB[U][NT];
+  Raw<16> wA[U], wB[U];
+  load_meta(mA, wave);
+  load_meta(mB, wave + 4 * U);
+  settle(mA, ivA, hvA, wA);
+  // Batches go in pairs with no exit between them (a load behind a conditional
+  // exit would be moved down to its use); a batch past the list multiplies zeros.
+  for (int t0 = wave; slice + (long long)S * t0 < ng; t0 += 8 * U) {
+    load_meta(mA, t0 + 8 * U);
+    settle(mB, ivB, hvB, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(ivA, hvA, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_meta(mB, t0 + 12 * U);
+    settle(mA, ivA, hvA, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(ivB, hvB, wB);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Waves 1..3 to LDS; wave 0 adds them in wave order.  D layout: lane l holds
