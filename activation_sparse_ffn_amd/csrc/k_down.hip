@@ -18,7 +18,6 @@
 namespace sfx {
 namespace {
 
-constexpr int kRowsInFlight = 16;  // rows per wave whose segments are loaded together
 constexpr int kTargetBlocks = 256;
 constexpr int kMaxSlices = 64;
 
@@ -100,6 +99,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
   constexpr int CPL = Seg<T, LW>::cpl;
   constexpr int TW = kWave * CPL;
   constexpr bool Q4 = T::bytes == 0;
+  constexpr int kRowsInFlight = 16;                   // rows per wave whose segments load together
   constexpr int CH = kWavesPerBlock * kRowsInFlight;  // rows per staged chunk
   __shared__ float s_red[kWavesPerBlock - 1][NB][TW];
   __shared__ float s_h[CH * NB];
@@ -388,10 +388,12 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict_
 }
 
 // Load width (bytes per lane per row) for a storage type and token class: keep
-// NB x CPL accumulators per lane at <= 64 (<= 128 for int4 at B = 16).
+// NB x CPL accumulators per lane at <= 64 (<= 128 for int4 at B = 16).  Tiles stay
+// at <= 512 columns: the last workgroup of a tile reads S partial tiles, and wide
+// tiles (few tiles, many slices) made that one workgroup read ~0.5 MB.
 template <class T>
 constexpr int lw_for(int nb) {
-  return T::bytes == 0 ? (nb <= 2 ? 16 : nb <= 4 ? 8 : 4)
+  return T::bytes == 0 ? 4   // 8 int4 columns per lane: 512-column tiles, as for 16-bit rows
                        : (nb * (16 / T::bytes) <= 64 ? 16 : nb * (8 / T::bytes) <= 64 ? 8 : 4);
 }
 
