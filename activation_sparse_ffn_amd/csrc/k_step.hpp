@@ -28,6 +28,7 @@
 //      mapped so workgroups sharing a 128-byte line of Wd run on one XCD.
 //                                                                   grid barrier
 #pragma once
+#include <type_traits>
 #include "sfx_common.hpp"
 #include "sfx_step.hpp"
 
@@ -412,7 +413,11 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         }
       }
       __syncthreads();
-      {
+      // The W2 source is chosen once, outside the loop: with the choice inside it,
+      // every row read became its own branch with a full memory wait, one LDS
+      // round trip per row.
+      auto scores_pass = [&](auto from_lds) {
+        constexpr bool kLds = decltype(from_lds)::value;
         constexpr int b0 = 0;
         const int tb = B;
         for (int q0 = wave; q0 < rows2; q0 += kNW * kRB) {
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
             for (int r = 0; r < kRB; ++r) {
               const int q = min(q0 + r * kNW, rows2 - 1);
-              if (w2_lds) {
+              if constexpr (kLds) {
                 wv[r] = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
               } else {
                 const int row = min(32 * (w + P * (q >> 5)) + (q & 31), f - 1);
@@ -459,7 +464,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             if (q < rows2 && b < tb) s_sc[q * NB + b0 + b] = v;
           }
         }
-      }
+      };
+      if (w2_lds) scores_pass(std::true_type{});
+      else scores_pass(std::false_type{});
       __syncthreads();
       // mask words by wave ballots (lane = row of a 64-row pair of words), then the
       // union goes out tagged, then the scores
