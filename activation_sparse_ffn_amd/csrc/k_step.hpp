@@ -363,19 +363,36 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] = 0.f;
       if (a_active) {
+        // The input source is chosen once, outside the loop, and a group's input
+        // chunks are all read before the first product (clamped, not branched
+        // on): with the choice per chunk every read waited for all memory.
+        auto dots = [&](auto from_lds) {
+          constexpr bool kL = decltype(from_lds)::value;
+          constexpr int MG = NB == 1 ? kU : NB == 2 ? (kU >= 4 ? kU / 2 : kU) : (kU >= 8 ? kU / 4 : kU);
 #pragma unroll
-        for (int m = 0; m < kU; ++m) {
-          const int c = lane + m * kWave;
-          if (c < nch1) {
+          for (int m0 = 0; m0 < kU; m0 += MG) {
+            Raw<16> xv[MG][NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-              if (b < B) {
-                const Raw<16> xv = x_lds ? *reinterpret_cast<const Raw<16>*>(s_xin + (size_t)b * rb1 + (size_t)c * 16)
-                                         : load_raw<16>(x + (size_t)b * rb1 + (size_t)c * 16);
-                dot_chunk<T>(w1r[m].w, xv.w, acc[b]);
+            for (int i = 0; i < MG; ++i) {
+              const int c = min(lane + (m0 + i) * kWave, nch1 - 1);
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                const size_t off = (size_t)min(b, B - 1) * rb1 + (size_t)c * 16;
+                if constexpr (kL) xv[i][b] = *reinterpret_cast<const Raw<16>*>(s_xin + off);
+                else xv[i][b] = load_raw<16>(x + off);
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < MG; ++i)
+              if (lane + (m0 + i) * kWave < nch1) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                  if (b < B) dot_chunk<T>(w1r[m0 + i].w, xv[i][b].w, acc[b]);
               }
           }
-        }
+        };
+        if (x_lds) dots(std::true_type{});
+        else dots(std::false_type{});
         const float v = wave_reduce_multi<NB>(acc);
         const int b = reduce_index<NB>(lane);
         if (reduce_owner<NB>(lane) && b < B)
@@ -568,6 +585,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         if (lane == 0) Ld->idx[r] = nid;
         const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
         const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
+        // the bias goes out ahead of the row (loaded after the dot products it
+        // was one more round trip per row)
+        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
         float za[NB], zl[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
@@ -597,7 +617,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             }
           }
         }
-        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
         const float ta = wave_reduce_multi<NB>(za);
         float v = fmaxf(ta + bias, 0.f);
         if (REGLU) v *= wave_reduce_multi<NB>(zl);
