@@ -522,6 +522,70 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     bool in_lds;                               // their list fits in LDS (s_nid)
     {
     SFX_PHASE_IDS;
+    // Up rows first, for this workgroup's own active neurons: the union bits of its
+    // mask words w + P m (still in s_words), so no exchange is waited for.  The
+    // activations go out tagged and indexed by neuron; the union exchange and the
+    // scan that the down phase needs run while other workgroups' rows are loading.
+    {
+      const uint8_t* x = (const uint8_t*)Ld->x;
+      const int nw2 = w < W ? (W - w + P - 1) / P : 0;
+      auto own_word = [&](int m) {
+        uint32_t u = 0;
+        for (int b = 0; b < B; ++b) u |= s_words[m * NB + b];
+        return u;
+      };
+      int own_k = 0;
+      for (int m = 0; m < nw2; ++m) own_k += __popc(own_word(m));
+      for (int e = wave; e < own_k; e += kWork) {
+        // entry e of the own list: word m, its rem-th set bit
+        int m = 0, rem = e;
+        uint32_t um = own_word(0);
+        while (rem >= __popc(um)) { rem -= __popc(um); um = own_word(++m); }
+        for (int i = 0; i < rem; ++i) um &= um - 1;
+        const int nid = 32 * (w + P * m) + __builtin_ctz(um);
+        const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
+        const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
+        // the bias goes out ahead of the row (loaded after the dot products it
+        // was one more round trip per row)
+        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
+        float za[NB], zl[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
+#pragma unroll
+        for (int u0 = 0; u0 < kU; u0 += kUP) {
+          // every load of the batch is issued before the first is used: chunk
+          // indices are clamped instead of branched on, so the compiler keeps
+          // them together and waits once
+          Raw<16> wa[kUP], wl[kUP], xq[kUP][NB];
+#pragma unroll
+          for (int u = 0; u < kUP; ++u) {
+            const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
+            wa[u] = load_raw<16>(ra + (size_t)c * 16);
+            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
+          }
+#pragma unroll
+          for (int u = 0; u < kUP; ++u) {
+            if (lane + (u0 + u) * kWave < nch1) {
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+                if (b < B) {
+                  dot_chunk<T>(wa[u].w, xq[u][b].w, za[b]);
+                  if (REGLU) dot_chunk<T>(wl[u].w, xq[u][b].w, zl[b]);
+                }
+            }
+          }
+        }
+        const float ta = wave_reduce_multi<NB>(za);
+        float v = fmaxf(ta + bias, 0.f);
+        if (REGLU) v *= wave_reduce_multi<NB>(zl);
+        if (reduce_owner<NB>(lane)) {
+          const int b = reduce_index<NB>(lane);
+          if (b < B) st_tagged(p.hact + (size_t)nid * B + b, tag, __float_as_uint(v));
+        }
+      }
+    }
     // thread o polls the union block of workgroup o (words o + P m) into s_uw
 #pragma unroll 1
     for (int o = tid; o < P; o += kNT) {
@@ -576,67 +640,15 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     lds_barrier();
 
 
-    {
-      const uint8_t* x = (const uint8_t*)Ld->x;
-      const int r0 = (int)(((long long)k * w) / P);
-      const int r1 = (int)(((long long)k * (w + 1)) / P);
-      for (int r = r0 + (wave < kWork ? wave : r1); r < r1; r += kWork) {
-        const int nid = in_lds ? s_nid[r] : rank_to_neuron(r, s_pref, s_uw, W);
-        if (lane == 0) Ld->idx[r] = nid;
-        const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
-        const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
-        // the bias goes out ahead of the row (loaded after the dot products it
-        // was one more round trip per row)
-        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
-        float za[NB], zl[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
-#pragma unroll
-        for (int u0 = 0; u0 < kU; u0 += kUP) {
-          // every load of the batch is issued before the first is used: chunk
-          // indices are clamped instead of branched on, so the compiler keeps
-          // them together and waits once
-          Raw<16> wa[kUP], wl[kUP], xq[kUP][NB];
-#pragma unroll
-          for (int u = 0; u < kUP; ++u) {
-            const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
-            wa[u] = load_raw<16>(ra + (size_t)c * 16);
-            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
-          }
-#pragma unroll
-          for (int u = 0; u < kUP; ++u) {
-            if (lane + (u0 + u) * kWave < nch1) {
-#pragma unroll
-              for (int b = 0; b < NB; ++b)
-                if (b < B) {
-                  dot_chunk<T>(wa[u].w, xq[u][b].w, za[b]);
-                  if (REGLU) dot_chunk<T>(wl[u].w, xq[u][b].w, zl[b]);
-                }
-            }
-          }
-        }
-        const float ta = wave_reduce_multi<NB>(za);
-        float v = fmaxf(ta + bias, 0.f);
-        if (REGLU) v *= wave_reduce_multi<NB>(zl);
-        if (reduce_owner<NB>(lane)) {
-          const int b = reduce_index<NB>(lane);
-          if (b < B) {
-            st_tagged(p.hact + (size_t)r * B + b, tag, __float_as_uint(v));
-            Ld->hact[(size_t)r * B + b] = v;
-          }
-        }
-      }
-    }
-
     // ---------------------------------------------------------------- phase D
     {
       // Down-phase geometry: workers are waves [0, kWork); lane group j = lane mod
       // nct (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct
       // walks the active rows.
       const int nct = p.cw / 8;
-      const int c0 = tile_of(w, P) * p.cw;
+      const int d_tile = tile_of(w, P);
+      const int d_tiles = (d + p.cw - 1) / p.cw;   // tiles that hold columns
+      const int c0 = d_tile * p.cw;
       const int d_j = lane & (nct - 1);
       const int d_rr = wave * (kWave / nct) + lane / nct;
       const int d_rs = kWork * (kWave / nct);
@@ -644,10 +656,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const bool d_ok = wave < kWork && d_col < d;
       const uint8_t* Wd = (const uint8_t*)Ld->Wd;
       Raw<16> wdv[kRD];
+      int nid[kRD];
       auto load_wd = [&](int rb) {                 // kRD rows at a time, rb < k
         // ranks past k are clamped to k - 1 (loaded, never used), so the loads
         // are issued back to back without branches
-        int nid[kRD];
         if (in_lds) {
 #pragma unroll
           for (int u = 0; u < kRD; ++u) nid[u] = s_nid[min(rb + u * d_rs, k - 1)];
@@ -671,7 +683,21 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           // entry u NB + b: activation of rank rb + u d_rs, token b
           poll_tagged_if<kRD * NB>(
               hv, [&](int i) { return i / NB < nrow && i % NB < B; },
-              [&](int i) { return p.hact + (size_t)(rb + (i / NB) * d_rs) * B + (i % NB); }, tag, p.err);
+              [&](int i) { return p.hact + (size_t)nid[i / NB] * B + (i % NB); }, tag, p.err);
+          // the list and the activations in rank order (outputs): rank r is
+          // written by the workgroup whose column tile is r mod the tile count
+          if (d_j == 0) {
+#pragma unroll
+            for (int u = 0; u < kRD; ++u) {
+              const int r = rb + u * d_rs;
+              if (u < nrow && r % d_tiles == d_tile) {
+                Ld->idx[r] = nid[u];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                  if (b < B) Ld->hact[(size_t)r * B + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+              }
+            }
+          }
 #pragma unroll
           for (int u = 0; u < kRD; ++u) {
             if (u < nrow) {
