@@ -60,15 +60,16 @@ __device__ __forceinline__ void st_tagged(unsigned long long* p, uint32_t tag, u
 __device__ __forceinline__ bool tag_ok(unsigned long long v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
 
 // Poll N tagged words (entries i with valid(i), addresses addr(i)) until all carry
-// `tag`.  Loads are issued as one batch, then only stale entries are reloaded.
-// Bounded: on timeout (or when another workgroup already failed) the error word is
-// set and whatever was read is returned.
+// `tag`.  Every addr(i), valid or not, must point into the caller's buffer: the
+// first loads are issued unconditionally as one batch (loads under per-entry
+// branches were each preceded by a wait for all memory, one round trip per word);
+// then only stale entries are reloaded.  Bounded: on timeout (or when another
+// workgroup already failed) the error word is set and whatever was read is returned.
 template <int N, class Valid, class Addr>
 __device__ __forceinline__ void poll_tagged_if(unsigned long long (&v)[N], Valid valid, Addr addr, uint32_t tag,
                                                uint32_t* err) {
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (valid(i)) v[i] = ld_agent64(addr(i));
+  for (int i = 0; i < N; ++i) v[i] = ld_agent64(addr(i));
   for (int spins = 0;; ++spins) {
     bool stale = false;
 #pragma unroll
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           // entry u NB + b: activation of rank rb + u d_rs, token b
           poll_tagged_if<kRD * NB>(
               hv, [&](int i) { return i / NB < nrow && i % NB < B; },
-              [&](int i) { return p.hact + (size_t)nid[i / NB] * B + (i % NB); }, tag, p.err);
+              [&](int i) { return p.hact + (size_t)nid[i / NB] * B + min(i % NB, B - 1); }, tag, p.err);
           // the list and the activations in rank order (outputs): rank r is
           // written by the workgroup whose column tile is r mod the tile count
           if (d_j == 0) {
