@@ -223,6 +223,7 @@ constexpr int kAW = 4;                   // waves [0, kAW): W1 rows
 constexpr int kCW = 7;                   // control wave; waves [kAW, kCW) stream W2
 constexpr int kWork = kNW;               // waves [0, kWork) take up and down rows
 
+
 // Weights of a layer that do not depend on its input, fetched before the layer
 // starts (behind the previous layer's barrier): the W1 row of each of waves 0..3
 // into registers, and the workgroup's W2 rows (mask words g = w, w + P, ...: 32
@@ -308,6 +309,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int kUP = (NB == 1 && !REGLU) ? kU : (NB == 1 || (NB == 2 && !REGLU)) ? 4 : 2;
   constexpr int kRD = 8 / NB;             // down rows per lane loaded together
   constexpr int kRB = TB <= 2 ? 8 : 4;    // score rows per lane per pass
+  // own up rows a workgroup takes before the union exchange: two rounds of the
+  // waves when a row is one load batch, one round otherwise
+  constexpr int kOwnCap = (kUP == kU ? 2 : 1) * kWork;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
@@ -523,12 +527,58 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     bool in_lds;                               // their list fits in LDS (s_nid)
     {
     SFX_PHASE_IDS;
+    // One up row: Wa (and Wl) row of neuron nid against the input, bias, activation,
+    // out tagged and indexed by neuron.
+    const uint8_t* x = (const uint8_t*)Ld->x;
+    auto up_row = [&](int nid) {
+      const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
+      const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
+      // the bias goes out ahead of the row (loaded after the dot products it
+      // was one more round trip per row)
+      const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
+      float za[NB], zl[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
+#pragma unroll
+      for (int u0 = 0; u0 < kU; u0 += kUP) {
+        // every load of the batch is issued before the first is used: chunk
+        // indices are clamped instead of branched on, so the compiler keeps
+        // them together and waits once
+        Raw<16> wa[kUP], wl[kUP], xq[kUP][NB];
+#pragma unroll
+        for (int u = 0; u < kUP; ++u) {
+          const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
+          wa[u] = load_raw<16>(ra + (size_t)c * 16);
+          if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kUP; ++u) {
+          if (lane + (u0 + u) * kWave < nch1) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              if (b < B) {
+                dot_chunk<T>(wa[u].w, xq[u][b].w, za[b]);
+                if (REGLU) dot_chunk<T>(wl[u].w, xq[u][b].w, zl[b]);
+              }
+          }
+        }
+      }
+      const float ta = wave_reduce_multi<NB>(za);
+      float v = fmaxf(ta + bias, 0.f);
+      if (REGLU) v *= wave_reduce_multi<NB>(zl);
+      if (reduce_owner<NB>(lane)) {
+        const int b = reduce_index<NB>(lane);
+        if (b < B) st_tagged(p.hact + (size_t)nid * B + b, tag, __float_as_uint(v));
+      }
+    };
     // Up rows first, for this workgroup's own active neurons: the union bits of its
-    // mask words w + P m (still in s_words), so no exchange is waited for.  The
-    // activations go out tagged and indexed by neuron; the union exchange and the
-    // scan that the down phase needs run while other workgroups' rows are loading.
+    // mask words w + P m (still in s_words), so no exchange is waited for; at most
+    // kOwnCap of them (two rounds of the waves).  A workgroup whose words are dense
+    // (co-activated groups of 32 are stored together) leaves the rest to the even
+    // split below, after the union exchange.
     {
-      const uint8_t* x = (const uint8_t*)Ld->x;
       const int nw2 = w < W ? (W - w + P - 1) / P : 0;
       auto own_word = [&](int m) {
         uint32_t u = 0;
@@ -537,54 +587,14 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       };
       int own_k = 0;
       for (int m = 0; m < nw2; ++m) own_k += __popc(own_word(m));
-      for (int e = wave; e < own_k; e += kWork) {
+      const int own_n = min(own_k, kOwnCap);
+      for (int e = wave; e < own_n; e += kWork) {
         // entry e of the own list: word m, its rem-th set bit
         int m = 0, rem = e;
         uint32_t um = own_word(0);
         while (rem >= __popc(um)) { rem -= __popc(um); um = own_word(++m); }
         for (int i = 0; i < rem; ++i) um &= um - 1;
-        const int nid = 32 * (w + P * m) + __builtin_ctz(um);
-        const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
-        const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
-        // the bias goes out ahead of the row (loaded after the dot products it
-        // was one more round trip per row)
-        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
-        float za[NB], zl[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) { za[b] = 0.f; zl[b] = 0.f; }
-#pragma unroll
-        for (int u0 = 0; u0 < kU; u0 += kUP) {
-          // every load of the batch is issued before the first is used: chunk
-          // indices are clamped instead of branched on, so the compiler keeps
-          // them together and waits once
-          Raw<16> wa[kUP], wl[kUP], xq[kUP][NB];
-#pragma unroll
-          for (int u = 0; u < kUP; ++u) {
-            const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
-            wa[u] = load_raw<16>(ra + (size_t)c * 16);
-            if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
-          }
-#pragma unroll
-          for (int u = 0; u < kUP; ++u) {
-            if (lane + (u0 + u) * kWave < nch1) {
-#pragma unroll
-              for (int b = 0; b < NB; ++b)
-                if (b < B) {
-                  dot_chunk<T>(wa[u].w, xq[u][b].w, za[b]);
-                  if (REGLU) dot_chunk<T>(wl[u].w, xq[u][b].w, zl[b]);
-                }
-            }
-          }
-        }
-        const float ta = wave_reduce_multi<NB>(za);
-        float v = fmaxf(ta + bias, 0.f);
-        if (REGLU) v *= wave_reduce_multi<NB>(zl);
-        if (reduce_owner<NB>(lane)) {
-          const int b = reduce_index<NB>(lane);
-          if (b < B) st_tagged(p.hact + (size_t)nid * B + b, tag, __float_as_uint(v));
-        }
+        up_row(32 * (w + P * m) + __builtin_ctz(um));
       }
     }
     // thread o polls the union block of workgroup o (words o + P m) into s_uw
@@ -609,7 +619,17 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     const uint32_t w0 = g0 < W ? s_uw[g0] : 0u;
     const uint32_t w1 = wpt == 2 && g0 + 1 < W ? s_uw[g0 + 1] : 0u;
     const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
-    uint32_t inc = cnt;
+    // the same scan also counts, per owner o = tid < P, its own entries past
+    // kOwnCap (the rows the even split below takes over): both counts fit in 16
+    // bits (k <= f <= 32 kMaxWords), so they are scanned packed in one word
+    uint32_t ovc = 0;
+    if (tid < P) {
+      uint32_t c = 0;
+      for (int g = tid; g < W; g += P) c += __popc(s_uw[g]);
+      ovc = c > (uint32_t)kOwnCap ? c - (uint32_t)kOwnCap : 0u;
+    }
+    const uint32_t pk = cnt | (ovc << 16);
+    uint32_t inc = pk;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const uint32_t n = __shfl_up(inc, o, kWave);
@@ -617,14 +637,18 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
     if (lane == kWave - 1) s_wt[wave] = inc;
     lds_barrier();
-    uint32_t before = 0, total = 0;
+    uint32_t before_pk = 0, total_pk = 0;
 #pragma unroll
     for (int v = 0; v < kNW; ++v) {
       const uint32_t t = s_wt[v];
-      if (v < wave) before += t;
-      total += t;
+      if (v < wave) before_pk += t;
+      total_pk += t;
     }
-    const uint32_t base = before + inc - cnt;
+    const uint32_t base_pk = before_pk + inc - pk;
+    uint32_t* s_ovp = reinterpret_cast<uint32_t*>(s_red);     // [P + 1] owner prefix, free in phase C
+    if (tid < P) s_ovp[tid] = base_pk >> 16;
+    if (tid == 0) s_ovp[P] = total_pk >> 16;
+    const uint32_t base = base_pk & 0xffffu, total = total_pk & 0xffffu;
     if (g0 < W) s_pref[g0] = base;
     if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
     if (tid == 0) s_pref[W] = total;
@@ -639,6 +663,25 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
     if (w == 0 && tid == 0) *Ld->count = k;
     lds_barrier();
+    // Own entries past kOwnCap of every workgroup (owner o: the set bits of words
+    // o + P m in order, from entry kOwnCap on), split evenly over the workgroups
+    // by the owner prefix s_ovp from the scan above.
+    {
+      const int nov = (int)s_ovp[P];             // overflow rows of all workgroups
+      const int q0 = (int)(((long long)nov * w) / P), q1 = (int)(((long long)nov * (w + 1)) / P);
+      for (int r = q0 + wave; r < q1; r += kWork) {
+        int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)s_ovp[mid] <= r) lo = mid; else hi = mid;
+        }
+        int m = 0, rem = kOwnCap + (r - (int)s_ovp[lo]);
+        uint32_t um = s_uw[lo];
+        while (rem >= __popc(um)) { rem -= __popc(um); um = s_uw[lo + P * (++m)]; }
+        for (int i = 0; i < rem; ++i) um &= um - 1;
+        up_row(32 * (lo + P * m) + __builtin_ctz(um));
+      }
+    }
 
 
     // ---------------------------------------------------------------- phase D
