@@ -6,8 +6,9 @@
 //
 // One 1024-thread workgroup per layer: thread g updates group g's score, builds a
 // 64-bit key (score bits << 32 | ~g) for candidates (score >= 0, so the bits order
-// like the values), a bitonic sort in LDS ranks the keys (score descending, then
-// group id ascending), and the first min(K, #candidates) become the hot set.
+// like the values), a bitonic sort ranks the keys (score descending, then group id
+// ascending; in-wave stages on registers, wider ones in LDS), and the first
+// min(K, #candidates) become the hot set.
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 
@@ -40,25 +41,43 @@ __global__ __launch_bounds__(kT) void k_tam(int G, const uint32_t* __restrict__ 
       key = ((unsigned long long)__float_as_uint(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)g);
     }
   }
-  s_key[g] = key;
   if (g < kT / 32) s_hot[g] = 0u;
   const int ncand = __syncthreads_count(cand);
 
-  // Bitonic sort, descending.
-  for (int k = 2; k <= kT; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int p = g ^ j;
-      if (p > g) {
-        const unsigned long long a = s_key[g], b = s_key[p];
-        const bool desc = (g & k) == 0;
-        if (desc ? (a < b) : (a > b)) {
-          s_key[g] = b;
-          s_key[p] = a;
-        }
-      }
+  // Bitonic sort of the first NP >= G keys, descending.  Exchanges between lanes
+  // of one wave (distance < 64) run on registers with shuffles; only the wider
+  // distances go through LDS, one barrier each.
+  int NP = 1;
+  while (NP < G) NP <<= 1;
+  for (int k = 2; k <= NP; k <<= 1) {
+    const bool desc = (g & k) == 0;
+    int j = k >> 1;
+    if (j >= kWave) {
+      s_key[g] = key;
       __syncthreads();
+      for (; j >= kWave; j >>= 1) {
+        const int p = g ^ j;
+        if (p > g) {
+          const unsigned long long a = s_key[g], b = s_key[p];
+          if (desc ? (a < b) : (a > b)) {
+            s_key[g] = b;
+            s_key[p] = a;
+          }
+        }
+        __syncthreads();
+      }
+      key = s_key[g];
+    }
+    for (; j > 0; j >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)key, j, kWave);
+      const uint32_t hi = __shfl_xor((uint32_t)(key >> 32), j, kWave);
+      const unsigned long long b = ((unsigned long long)hi << 32) | lo;
+      const bool lower = (g & j) == 0;        // lower index keeps the larger key when descending
+      key = (lower == desc) ? (key > b ? key : b) : (key < b ? key : b);
     }
   }
+  s_key[g] = key;
+  __syncthreads();
 
   const int kk = ncand < K ? ncand : K;
   if (g < K) {
