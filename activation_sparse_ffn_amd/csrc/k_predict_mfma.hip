@@ -90,60 +90,100 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
 }
 
 // ------------------------------------------------------------------ layer 2
-// Each wave owns one tile of 16 W2 rows and walks all h columns in 32-wide steps,
-// kSU steps in flight: per step one 16-byte W2 load and NT x pieces 16-byte piece
-// loads per lane (the pieces are small and shared by every wave: cache hits).
-constexpr int kSWB = 4;   // waves (row tiles) per workgroup
+// Each wave owns one tile of 16 W2 rows and walks the h columns in 32-wide steps,
+// kSU steps in flight: one 16-byte W2 load per lane and step.  The pieces (the B
+// operand, shared by every wave) are staged in LDS, KC columns at a time, by the
+// whole workgroup: read from memory by every wave at every step they tripled the
+// load requests and halved the W2 stream.
+constexpr int kSWB = 8;   // waves (row tiles) per workgroup
 constexpr int kSU = 4;
+
+template <class T, int NT>
+struct ScoreTile {
+  static constexpr int NP = Split<T>::pieces;
+  static constexpr int rows = NP * NT * 16;                       // piece rows in LDS
+  static constexpr int KC = rows <= 32 ? 2048 : rows <= 64 ? 1024 : rows <= 128 ? 512 : 256;   // columns per stage
+  static constexpr int KS = KC + 8;                               // halves per LDS row (16-byte skew)
+};
 
 template <class T, int NT>
 __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __restrict__ W2,
                                                              const uint16_t* __restrict__ hp,
                                                              float* __restrict__ scores, int B, int h, int f) {
-  constexpr int NP = Split<T>::pieces;
+  using G = ScoreTile<T, NT>;
+  constexpr int NP = G::NP;
   constexpr int NACC = Split<T>::accumulators;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  constexpr int KC = G::KC, KS = G::KS, NR = G::rows;
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[NR * KS];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = (blockIdx.x * kSWB + wave) * 16;
-  if (row0 >= f) return;
+  const bool active = row0 < f;                 // no early exit: the workgroup stages together
   const int r = min(row0 + (lane & 15), f - 1);
   const int kq = (lane >> 4) * 8;
-  const int nsteps = (h + 31) >> 5;
   const uint8_t* ar = W2 + (size_t)r * h * 2;
   const size_t tstride = (size_t)NT * 16 * h;
-  const uint16_t* br[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) br[n] = hp + (size_t)(n * 16 + (lane & 15)) * h;
   f32x4 acc[NACC][NT];
 #pragma unroll
   for (int q = 0; q < NACC; ++q)
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < nsteps; s0 += kSU) {
-    Raw<16> a[kSU], b[kSU][NT][NP];
+  for (int kc = 0; kc < h; kc += KC) {
+    const int cw = min(KC, h - kc);            // a multiple of 8: rows span multiples of 16 bytes
+    // stage piece rows (piece p, token t) columns [kc, kc + cw): 16 bytes per item,
+    // every item of a thread loaded before the first is stored
+    __syncthreads();                           // the previous stage is consumed
+    {
+      constexpr int IPT = (NR * (KC / 8) + kSWB * kWave - 1) / (kSWB * kWave);
+      const int per_row = cw >> 3, items = NR * per_row;
+      Raw<16> v[IPT];
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int c = min((s0 + u) * 32 + kq, h - 8);
-      a[u] = load_raw<16>(ar + (size_t)c * 2);
+      for (int q = 0; q < IPT; ++q) {
+        const int i = min(tid + q * kSWB * kWave, items - 1);
+        const int pr = i / per_row, c8 = i - pr * per_row;
+        const int p = pr / (NT * 16), t = pr - p * (NT * 16);
+        v[q] = load_raw<16>(hp + p * tstride + (size_t)t * h + kc + c8 * 8);
+      }
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) b[u][n][p] = load_raw<16>(br[n] + p * tstride + c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      if ((s0 + u) * 32 + kq >= h) a[u] = zero16();        // steps and columns past h add nothing
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int q = NACC == 1 ? 0 : p;
-          acc[q][n] = Mma<T>::run(a[u], b[u][n][p], acc[q][n]);
+      for (int q = 0; q < IPT; ++q) {
+        const int i = tid + q * kSWB * kWave;
+        if (i < items) {
+          const int pr = i / per_row, c8 = i - pr * per_row;
+          *reinterpret_cast<Raw<16>*>(s_p + pr * KS + c8 * 8) = v[q];
         }
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const int nst = (cw + 31) >> 5;
+      for (int s0 = 0; s0 < nst; s0 += kSU) {
+        Raw<16> a[kSU];
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+          const int c = min(kc + (s0 + u) * 32 + kq, h - 8);
+          a[u] = load_raw<16>(ar + (size_t)c * 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+          const int cl = (s0 + u) * 32 + kq;    // column within the stage
+          if (cl >= cw) a[u] = zero16();       // past the stage (or past h): adds nothing
+          const int clc = min(cl, cw - 8);     // read a staged column there (finite, times zero)
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              const Raw<16> bv = *reinterpret_cast<const Raw<16>*>(s_p + (p * NT * 16 + n * 16 + (lane & 15)) * KS + clc);
+              const int q = NACC == 1 ? 0 : p;
+              acc[q][n] = Mma<T>::run(a[u], bv, acc[q][n]);
+            }
+        }
+      }
     }
   }
+  if (!active) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int tok = n * 16 + (lane & 15);
