@@ -242,17 +242,19 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
 // a slice takes groups of 4 list entries g = s, s + S, ..., its four waves every
 // fourth of them, in batches of U groups: while a batch is multiplied the next
 // batch's rows and the batch after that's indices and activations are loading.
+// Up to 32 tokens the batch is sized so that two waves fit on each SIMD (one wave
+// per SIMD left the matrix cores idle while it waited for rows).
 constexpr int kMfmaTW = 128;
 
 template <class T, int NT>
-__global__ __launch_bounds__(kBlock) void k_down_mfma(const uint8_t* __restrict__ Wd,
+__global__ __launch_bounds__(kBlock, NT <= 2 ? 2 : 1) void k_down_mfma(const uint8_t* __restrict__ Wd,
                                                       const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ count, int kmax,
                                                       const float* __restrict__ hact, int B, int d, int f,
                                                       float* __restrict__ y, float* __restrict__ part,
                                                       uint32_t* __restrict__ tickets, int S, int ntiles) {
   constexpr int TW = kMfmaTW;
-  constexpr int U = NT <= 2 ? 8 : 4;
+  constexpr int U = NT <= 1 ? 8 : NT <= 2 ? 4 : 2;
   __shared__ f32x4 s_red[kWavesPerBlock - 1][8][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -173,6 +173,30 @@ def test_compact_crafted_scores():
         assert mtok[0, 3] and not mtok[1, 4] and mtok[2, 5] and not mtok[0, 6]
 
 
+@pytest.mark.parametrize("f,B,t", [(40001, 33, 2.0),       # ~54% union: three list windows, two token batches
+                                   (70000, 1, 10.0),       # empty list
+                                   (70000, 2, -1e30)])     # every neuron: nine windows, three words per thread
+def test_compact_long_lists(f, B, t):
+    """Lists longer than one LDS window, the empty list and the full list."""
+    g = torch.Generator().manual_seed(f + B)
+    s = torch.randn(B, f, generator=g).to(DEV)
+    W = (f + 31) // 32
+    tok = torch.zeros(B, W, dtype=torch.int32, device=DEV)
+    uni = torch.zeros(W, dtype=torch.int32, device=DEV)
+    idx = torch.full((f,), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = A.workspace(A.sfx_compact_ws(B, f))
+    say(f"compact long f={f} B={B} t={t}")
+    A.sfx_compact(s, t, uni, idx, cnt, ws, tok_bits=tok)
+    torch.cuda.synchronize()
+    mtok, muni, midx, mcnt = O.gate(s.cpu().double().numpy(), t)
+    assert np.array_equal(tok.cpu().numpy().view(np.uint32), O.pack_bits(mtok))
+    assert np.array_equal(uni.cpu().numpy().view(np.uint32), O.pack_bits(muni))
+    k = int(cnt.item())
+    assert k == mcnt and np.array_equal(idx[:k].cpu().numpy(), midx)
+    assert torch.all(idx[k:] == -7)
+
+
 def test_out_of_range_indices_are_inert():
     cfg = SCALED["C2s"]
     L = S.make_layer(cfg, 0, device=DEV)
