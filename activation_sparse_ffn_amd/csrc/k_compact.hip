@@ -3,12 +3,15 @@
 // pseudocode; Paper vs code, predictor threshold: a neuron whose score is below the
 // threshold is skipped).
 //
-// One kernel.  Every workgroup turns 1024 neurons x B tokens into mask words with
-// wave ballots (one 64-bit ballot = two 32-bit words = two groups of 32 neurons)
-// and ORs the tokens into the union word, which it writes through to the
-// coherence point.  The last workgroup to take a ticket prefix-sums the popcounts
-// of all union words and writes the index list and the count.  Nothing leaves the
-// device.
+// One kernel.  Every workgroup takes 1024 neurons and turns them x B tokens into
+// mask words with wave ballots (one 64-bit ballot = two 32-bit words = two groups
+// of 32 neurons), ORing the tokens into the union words.  Its active count goes
+// out as one word (count + 1, never zero); it reads the words of the workgroups
+// before it (one batch of loads, re-polled while any is still zero) and every
+// active neuron's thread writes it at prefix + rank, so the whole grid writes the
+// list in rank order (the last workgroup writing the whole list alone, one
+// scattered store per set bit, took 4-12 us).  The last workgroup to take the
+// closing ticket clears the count words and the ticket.  Nothing leaves the device.
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 
@@ -17,44 +20,24 @@ namespace {
 
 constexpr int kT = 1024;
 constexpr int kWaves = kT / kWave;
+constexpr int kSpin = 1 << 20;
 
-// Exclusive prefix sum of one value per thread over a 1024-thread block; also
-// returns the block total.  Wave-level shuffle scan, then a scan of the 16 wave
-// totals.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tot, uint32_t& total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
-  }
-  if (lane == kWave - 1) s_tot[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < kWaves ? s_tot[lane] : 0u;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const uint32_t n = __shfl_up(t, o, kWave);
-      if (lane >= o) t += n;
-    }
-    if (lane < kWaves) s_tot[kWaves + lane] = t;   // inclusive wave prefix
-  }
-  __syncthreads();
-  total = s_tot[2 * kWaves - 1];
-  const uint32_t before = wave > 0 ? s_tot[kWaves + wave - 1] : 0u;
-  return before + inc - v;
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ctl: [0] ticket, [1] error (nonzero: a count word did not arrive in time);
+// cnt: one word per workgroup.
 __global__ __launch_bounds__(kT) void k_compact(const float* __restrict__ scores, int B, int f, float t,
                                                 uint32_t* __restrict__ tok_bits, uint32_t* __restrict__ union_bits,
                                                 int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                uint32_t* __restrict__ ticket) {
-  __shared__ uint32_t s_tot[2 * kWaves];
+                                                uint32_t* __restrict__ ctl, uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t s_wc[kWaves];
+  __shared__ uint32_t s_red[kWaves];
   __shared__ int s_last;
   const int W = (f + 31) >> 5;
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
   const int n = blockIdx.x * kT + threadIdx.x;
   const int w0 = n >> 5;  // lanes 0 and 32 own words w0
   uint64_t uni = 0;
@@ -74,50 +57,78 @@ __global__ __launch_bounds__(kT) void k_compact(const float* __restrict__ scores
       }
     }
   }
-  if ((lane == 0 || lane == 32) && w0 < W) store_through(union_bits + w0, (uint32_t)(lane == 0 ? uni : (uni >> 32)));
+  if ((lane == 0 || lane == 32) && w0 < W) union_bits[w0] = (uint32_t)(lane == 0 ? uni : (uni >> 32));
 
+  // This workgroup's count and this wave's offset within it.
+  if (lane == 0) s_wc[wave] = (uint32_t)__popcll(uni);
+  __syncthreads();
+  uint32_t woff = 0, btot = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    const uint32_t c = s_wc[v];
+    btot += c;
+    woff += v < wave ? c : 0u;
+  }
+  if (threadIdx.x == 0) store_through(cnt + blockIdx.x, btot + 1u);
+
+  // Counts of the workgroups before this one: thread j reads workgroup j's word.
+  uint32_t part = 0;
+  for (int j0 = 0; j0 < (int)blockIdx.x; j0 += kT) {
+    const int j = j0 + (int)threadIdx.x;
+    const bool mine = j < (int)blockIdx.x;
+    uint32_t c = ld_agent(cnt + (mine ? j : 0));
+    for (int spins = 0; mine && c == 0u; ++spins) {
+      if (spins > kSpin) {
+        store_through(ctl + 1, 1u);
+        break;
+      }
+      c = ld_agent(cnt + j);
+    }
+    if (mine && c != 0u) part += c - 1u;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+  if (lane == 0) s_red[wave] = part;
+  __syncthreads();
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) prefix += s_red[v];
+
+  if ((uni >> lane) & 1ull) {
+    const uint32_t below = (uint32_t)__popcll(uni & ((1ull << lane) - 1ull));
+    idx[prefix + woff + below] = n;
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = (int32_t)(prefix + btot);
+
+  // Closing ticket, taken once this workgroup's count word has landed and its
+  // reads are done: the last one clears the count words and the ticket.
   wait_memory();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (take_ticket(ticket) == gridDim.x - 1);
+  if (threadIdx.x == 0) s_last = (take_ticket(ctl) == gridDim.x - 1);
   __syncthreads();
   if (!s_last) return;
-  acquire_agent();
-
-  // Last workgroup: exclusive scan of popcounts over all W words, `per`
-  // consecutive words per thread.
-  const int per = (W + kT - 1) / kT;
-  const int wb = threadIdx.x * per;
-  uint32_t cnt = 0;
-  for (int i = 0; i < per; ++i)
-    if (wb + i < W) cnt += __popc(union_bits[wb + i]);
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan(cnt, s_tot, total);
-  for (int i = 0; i < per; ++i) {
-    if (wb + i >= W) break;
-    uint32_t word = union_bits[wb + i];
-    while (word) {
-      idx[pos++] = ((wb + i) << 5) + __builtin_ctz(word);
-      word &= word - 1;
-    }
-  }
-  if (threadIdx.x == 0) {
-    *count = (int32_t)total;
-    *ticket = 0u;  // ready for the next call
-  }
+  for (int j = threadIdx.x; j < (int)gridDim.x; j += kT) store_through(cnt + j, 0u);
+  if (threadIdx.x == 0) store_through(ctl, 0u);
 }
+
+size_t cnt_offset() { return 256; }
 
 }  // namespace
 
+// control words | one count word per workgroup of 1024 neurons
 size_t compact_ws_bytes(int B, int f) {
-  (void)B; (void)f;
-  return 256;
+  (void)B;
+  const size_t blocks = ((size_t)f + kT - 1) / kT;
+  return cnt_offset() + ((blocks * 4 + 255) & ~(size_t)255);
 }
 
 hipError_t launch_compact(hipStream_t s, int B, int f, const float* scores, float t, uint32_t* tok_bits,
                           uint32_t* union_bits, int32_t* idx, int kmax, int32_t* count, void* ws) {
   (void)kmax;
   const int blocks = (f + kT - 1) / kT;
-  k_compact<<<dim3(blocks), dim3(kT), 0, s>>>(scores, B, f, t, tok_bits, union_bits, idx, count, (uint32_t*)ws);
+  uint32_t* ctl = (uint32_t*)ws;
+  uint32_t* cnt = (uint32_t*)((uint8_t*)ws + cnt_offset());
+  k_compact<<<dim3(blocks), dim3(kT), 0, s>>>(scores, B, f, t, tok_bits, union_bits, idx, count, ctl, cnt);
   return hipGetLastError();
 }
 

@@ -115,7 +115,11 @@ int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
  *              Entries from count on are left unchanged.
  *   kmax       capacity of idx; must be >= f, so the list cannot overflow.
  *   count      device int32 scalar, written.  It stays on the device.
- *   ws         >= sfx_compact_ws(B, f) bytes.
+ *   ws         >= sfx_compact_ws(B, f) bytes (256 + 4 per 1024 neurons, rounded
+ *              up to 256).  The workgroups hand their counts to each other through
+ *              it with bounded waits: a count that does not arrive within the bound
+ *              sets word 1 of the workspace nonzero instead of hanging, and the list
+ *              of that call is then undefined.
  * ------------------------------------------------------------------------------- */
 size_t sfx_compact_ws(int B, int f);
 int sfx_compact(void* stream, int B, int f, const float* scores, float threshold,

@@ -186,15 +186,17 @@ def test_compact_long_lists(f, B, t):
     idx = torch.full((f,), -7, dtype=torch.int32, device=DEV)
     cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
     ws = A.workspace(A.sfx_compact_ws(B, f))
-    say(f"compact long f={f} B={B} t={t}")
-    A.sfx_compact(s, t, uni, idx, cnt, ws, tok_bits=tok)
-    torch.cuda.synchronize()
     mtok, muni, midx, mcnt = O.gate(s.cpu().double().numpy(), t)
-    assert np.array_equal(tok.cpu().numpy().view(np.uint32), O.pack_bits(mtok))
-    assert np.array_equal(uni.cpu().numpy().view(np.uint32), O.pack_bits(muni))
-    k = int(cnt.item())
-    assert k == mcnt and np.array_equal(idx[:k].cpu().numpy(), midx)
-    assert torch.all(idx[k:] == -7)
+    for rep in range(2):                       # the control words are clear again after a call
+        say(f"compact long f={f} B={B} t={t} rep {rep}")
+        A.sfx_compact(s, t, uni, idx, cnt, ws, tok_bits=tok)
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy().view(np.uint32), O.pack_bits(mtok))
+        assert np.array_equal(uni.cpu().numpy().view(np.uint32), O.pack_bits(muni))
+        k = int(cnt.item())
+        assert k == mcnt and np.array_equal(idx[:k].cpu().numpy(), midx)
+        assert torch.all(idx[k:] == -7)
+        assert int(torch.count_nonzero(ws)) == 0
 
 
 def test_out_of_range_indices_are_inert():
