@@ -23,22 +23,45 @@ namespace sfx {
 namespace {
 
 // ------------------------------------------------------------------ layer 1
-// Workgroup = one tile of 16 W1 rows; its 16 waves take interleaved 32-wide k
-// steps (kHU in flight each); every wave's partial tile goes to LDS, and wave n
-// adds token tile n's partials in wave order, applies the ReLU and stores the
-// pieces (pad tokens past B store 0).
+// Workgroup = one tile of 16 W1 rows and one of S equal parts of the d walk; its
+// 16 waves take interleaved 32-wide k steps (kHU in flight each); every wave's
+// partial tile goes to LDS, and wave n adds token tile n's partials in wave order.
+// With S > 1 (fewer row tiles than compute units) each part stores its tile
+// write-through and takes the tile's ticket; the last part to arrive reads the S
+// tiles with agent-scope loads, adds them in part order, resets the ticket and
+// goes on as the only part would: ReLU, split, store the pieces (pad tokens past B
+// store 0).
 constexpr int kHW = 16;
 constexpr int kHU = 4;
+constexpr int kPredCUs = 256;   // split the d walk until the tiles reach this many workgroups
+constexpr int kMaxSplit = 4;
+
+__device__ __forceinline__ unsigned long long ld_agent64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int hidden_split(int h) {
+  const int tiles = (h + 15) / 16;
+  const int S = kPredCUs / tiles;
+  return S < 1 ? 1 : S > kMaxSplit ? kMaxSplit : S;
+}
 
 template <class T, int NT>
 __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __restrict__ x,
                                                             const uint8_t* __restrict__ W1,
-                                                            uint16_t* __restrict__ hp, int B, int d, int h) {
+                                                            uint16_t* __restrict__ hp, int B, int d, int h,
+                                                            int S, float* __restrict__ part,
+                                                            uint32_t* __restrict__ tickets) {
   constexpr int NP = Split<T>::pieces;
   __shared__ f32x4 s_acc[kHW][NT][kWave];
+  __shared__ int s_last;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * 16;
+  const int tiles = (h + 15) >> 4;
+  const int tile = blockIdx.x % tiles;
+  const int sp = blockIdx.x / tiles;            // part of the d walk
+  const int row0 = tile * 16;
   const int r = min(row0 + (lane & 15), h - 1);      // rows past h read row h - 1, never stored
   const int kq = (lane >> 4) * 8;
   const int nsteps = (d + 31) >> 5;
@@ -49,11 +72,15 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsteps; s0 += kHW * kHU) {
+  const int sb = (int)((long long)nsteps * sp / S);
+  const int se = (int)((long long)nsteps * (sp + 1) / S);
+  for (int s0 = sb + wave; s0 < se; s0 += kHW * kHU) {
     Raw<16> a[kHU], bx[kHU][NT];
 #pragma unroll
     for (int u = 0; u < kHU; ++u) {
-      const size_t off = (size_t)min((s0 + u * kHW) * 32 + kq, d - 8) * 2;
+      // a step of the next part re-reads this wave's first step (a cache hit)
+      const int st = s0 + u * kHW < se ? s0 + u * kHW : s0;
+      const size_t off = (size_t)min(st * 32 + kq, d - 8) * 2;
       a[u] = load_raw<16>(ar + off);
 #pragma unroll
       for (int n = 0; n < NT; ++n) bx[u][n] = load_raw<16>(xr[n] + off);
@@ -61,7 +88,8 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kHU; ++u) {
-      if ((s0 + u * kHW) * 32 + kq >= d) a[u] = zero16();   // steps and columns past d add nothing
+      // steps of the next part and columns past d add nothing
+      if (s0 + u * kHW >= se || (s0 + u * kHW) * 32 + kq >= d) a[u] = zero16();
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = Mma<T>::run(a[u], bx[u][n], acc[n]);
     }
@@ -69,10 +97,45 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
 #pragma unroll
   for (int n = 0; n < NT; ++n) s_acc[wave][n][lane] = acc[n];
   __syncthreads();
+  f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave < NT) {
+    t = s_acc[0][wave][lane];
+    for (int v = 1; v < kHW; ++v) t += s_acc[v][wave][lane];
+  }
+  if (S > 1) {
+    // part tile [tile][sp][n][lane] (16 bytes per lane)
+    auto slot = [&](int q) { return part + (((size_t)tile * S + q) * NT + wave) * kWave * 4 + lane * 4; };
+    if (wave < NT) {
+      store_through2(slot(sp), t[0], t[1]);
+      store_through2(slot(sp) + 2, t[2], t[3]);
+    }
+    wait_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = (take_ticket(tickets + tile) == (uint32_t)(S - 1));
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) tickets[tile] = 0u;   // ready for the next call
+    if (wave < NT) {
+      unsigned long long v[kMaxSplit][2];
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q) {
+        const float* pq = slot(min(q, S - 1));
+        v[q][0] = ld_agent64(pq);
+        v[q][1] = ld_agent64(pq + 2);
+      }
+      t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        if (q < S) {
+          t[0] += __uint_as_float((uint32_t)v[q][0]);
+          t[1] += __uint_as_float((uint32_t)(v[q][0] >> 32));
+          t[2] += __uint_as_float((uint32_t)v[q][1]);
+          t[3] += __uint_as_float((uint32_t)(v[q][1] >> 32));
+        }
+    }
+  }
   if (wave < NT) {
     const int n = wave;
-    f32x4 t = s_acc[0][n][lane];
-    for (int v = 1; v < kHW; ++v) t += s_acc[v][n][lane];
     // D layout: lane l holds rows 4 (l / 16) + i of the tile for token l % 16.
     const int tok = n * 16 + (lane & 15);
     const size_t tstride = (size_t)NT * 16 * h;   // one piece plane
@@ -200,9 +263,10 @@ __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __r
 
 template <class T, int NT>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-               uint16_t* hp, float* scores) {
-  k_hidden_mfma<T, NT><<<dim3((h + 15) / 16), dim3(kHW * kWave), 0, s>>>((const uint8_t*)x, (const uint8_t*)W1,
-                                                                           hp, B, d, h);
+               uint16_t* hp, float* scores, float* part, uint32_t* tickets) {
+  const int S = hidden_split(h);
+  k_hidden_mfma<T, NT><<<dim3(((h + 15) / 16) * S), dim3(kHW * kWave), 0, s>>>(
+      (const uint8_t*)x, (const uint8_t*)W1, hp, B, d, h, S, part, tickets);
   k_scores_mfma<T, NT><<<dim3((f + kSWB * 16 - 1) / (kSWB * 16)), dim3(kSWB * kWave), 0, s>>>(
       (const uint8_t*)W2, hp, scores, B, h, f);
   return hipGetLastError();
@@ -210,11 +274,14 @@ hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const v
 
 template <class T>
 hipError_t dispatch(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-                    uint16_t* hp, float* scores) {
-  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hp, scores);
-  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hp, scores);
-  return run<T, 4>(s, B, d, h, f, x, W1, W2, hp, scores);
+                    uint16_t* hp, float* scores, float* part, uint32_t* tickets) {
+  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
+  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
+  return run<T, 4>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
 }
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+int token_tiles(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
 
 }  // namespace
 
@@ -223,17 +290,28 @@ bool pred_mfma_eligible(int wdt, int B, int h, int f) {
   return (wdt == DT_F16 || wdt == DT_BF16) && B >= 8 && B <= 64;
 }
 
-// Bytes of the pieces buffer: pieces x (16 x token tiles) x h halves.
+// Pieces (pieces x 16 token-tile rows x h halves) | with S > 1 parts of the d
+// walk: one ticket per row tile | S partial tiles per row tile (fp32).
 size_t pred_mfma_ws_bytes(int wdt, int B, int h) {
   const int np = wdt == DT_BF16 ? Split<TBF16>::pieces : Split<TF16>::pieces;
-  const int nt = B <= 16 ? 1 : B <= 32 ? 2 : 4;
-  return (size_t)np * nt * 16 * h * sizeof(uint16_t);
+  const int nt = token_tiles(B);
+  const int tiles = (h + 15) / 16, S = hidden_split(h);
+  size_t n = up256((size_t)np * nt * 16 * h * sizeof(uint16_t));
+  if (S > 1) n += up256((size_t)tiles * 4) + (size_t)S * tiles * nt * 16 * 16 * sizeof(float);
+  return n;
 }
 
 hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
                             const void* W2, void* ws, float* scores) {
-  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, (uint16_t*)ws, scores);
-  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, (uint16_t*)ws, scores);
+  const int np = wdt == DT_BF16 ? Split<TBF16>::pieces : Split<TF16>::pieces;
+  const int tiles = (h + 15) / 16;
+  uint8_t* base = (uint8_t*)ws;
+  uint16_t* hp = (uint16_t*)base;
+  const size_t off_t = up256((size_t)np * token_tiles(B) * 16 * h * sizeof(uint16_t));
+  uint32_t* tickets = (uint32_t*)(base + off_t);
+  float* part = (float*)(base + off_t + up256((size_t)tiles * 4));
+  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
+  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
 }
 
 }  // namespace sfx

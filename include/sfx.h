@@ -93,8 +93,13 @@ int sfx_abi_version(void);
  * Rows: d*sizeof(wdt) and h*sizeof(wdt) must be multiples of 16 bytes.
  * From B = 8 on (fp16 / bf16) both layers run on the matrix cores; the second
  * takes the fp32 hidden as exact 16-bit pieces (two fp16 or three bf16 terms),
- * so scores keep fp32 accuracy.  The workspace then holds those pieces for
- * 16 * ceil(B / 16) tokens; below 8 tokens it holds the fp32 hidden [B][h].
+ * so scores keep fp32 accuracy.  With fp16 weights the hidden values must then
+ * stay below 65504 in magnitude (the fp16 range of the leading piece); bf16
+ * pieces cover the fp32 range.  The workspace then holds those pieces for 16, 32
+ * or 64 tokens (B <= 16, <= 32, <= 64) and, when h / 16 is below 256, the first
+ * layer's partial sums (its d walk is split over up to 4 workgroups per 16
+ * rows) with one control word per 16 rows; below 8 tokens it holds the fp32
+ * hidden [B][h].
  * ------------------------------------------------------------------------------- */
 size_t sfx_predict_ws(int wdt, int B, int d, int h, int f);
 int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
