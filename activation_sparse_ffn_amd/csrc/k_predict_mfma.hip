@@ -159,8 +159,10 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
 // staging barrier measured slower).  The pieces (the B
 // operand, shared by every wave) are staged in LDS, KC columns at a time, by the
 // whole workgroup: read from memory by every wave at every step they tripled the
-// load requests and halved the W2 stream.
-constexpr int kSWB = 8;   // waves (row tiles) per workgroup
+// load requests and halved the W2 stream.  With fewer than 256 workgroups of 8
+// row tiles (small f), two waves share a row tile (wpt = 2), taking alternate
+// batches of steps; the second adds its tile to the first through LDS.
+constexpr int kSWB = 8;   // waves per workgroup
 constexpr int kSU = 16;
 
 template <class T, int NT>
@@ -174,7 +176,8 @@ struct ScoreTile {
 template <class T, int NT>
 __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __restrict__ W2,
                                                              const uint16_t* __restrict__ hp,
-                                                             float* __restrict__ scores, int B, int h, int f) {
+                                                             float* __restrict__ scores, int B, int h, int f,
+                                                             int wpt) {
   using G = ScoreTile<T, NT>;
   constexpr int NP = G::NP;
   constexpr int NACC = Split<T>::accumulators;
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __r
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row0 = (blockIdx.x * kSWB + wave) * 16;
+  const int half = wave % wpt;                  // this wave's share of the tile's steps
+  const int row0 = (blockIdx.x * (kSWB / wpt) + wave / wpt) * 16;
   const bool active = row0 < f;                 // no early exit: the workgroup stages together
   const int r = min(row0 + (lane & 15), f - 1);
   const int kq = (lane >> 4) * 8;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __r
     __syncthreads();
     if (active) {
       const int nst = (cw + 31) >> 5;
-      for (int s0 = 0; s0 < nst; s0 += kSU) {
+      for (int s0 = half * kSU; s0 < nst; s0 += wpt * kSU) {
         Raw<16> a[kSU];
 #pragma unroll
         for (int u = 0; u < kSU; ++u) {
@@ -248,6 +252,25 @@ __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __r
       }
     }
   }
+  if (wpt > 1) {
+    // the staged pieces are consumed: the second wave of each tile parks its
+    // partial tile where they were, the first adds it
+    f32x4* s_red = reinterpret_cast<f32x4*>(s_p);
+    const int slot = (wave / wpt) * NACC * NT;
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int q = 0; q < NACC; ++q)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) s_red[(slot + q * NT + n) * kWave + lane] = acc[q][n];
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[q][n] += s_red[(slot + q * NT + n) * kWave + lane];
+  }
   if (!active) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -267,8 +290,11 @@ hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const v
   const int S = hidden_split(h);
   k_hidden_mfma<T, NT><<<dim3(((h + 15) / 16) * S), dim3(kHW * kWave), 0, s>>>(
       (const uint8_t*)x, (const uint8_t*)W1, hp, B, d, h, S, part, tickets);
-  k_scores_mfma<T, NT><<<dim3((f + kSWB * 16 - 1) / (kSWB * 16)), dim3(kSWB * kWave), 0, s>>>(
-      (const uint8_t*)W2, hp, scores, B, h, f);
+  const int rtiles = (f + 15) / 16;
+  const int wpt = (rtiles + kSWB - 1) / kSWB < kPredCUs ? 2 : 1;
+  const int per_wg = kSWB / wpt;
+  k_scores_mfma<T, NT><<<dim3((rtiles + per_wg - 1) / per_wg), dim3(kSWB * kWave), 0, s>>>(
+      (const uint8_t*)W2, hp, scores, B, h, f, wpt);
   return hipGetLastError();
 }
 
