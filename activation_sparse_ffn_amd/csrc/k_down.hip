@@ -412,6 +412,11 @@ Plan plan_for(int wdt, int B, int d, int kmax) {
     p.tw = kMfmaTW;
     p.ntiles = (d + p.tw - 1) / p.tw;
     int S = 2 * kTargetBlocks / p.ntiles;
+    // 8 slices measured best on 32 and 64 column tiles (LLaMA2-7B shape at 8 tokens:
+    // 16 slices 24.7 us, 8: 21.4; Falcon-40B shape: 4 slices 50.0 / 131.4 us at 8 /
+    // 32 tokens, 8: 48.5 / 125.6, 16: 59.8 / 141.4): beyond that the fixed-order
+    // sum of the partial tiles costs more than the shorter walks save.
+    if (p.ntiles >= 32 && S > 8) S = 8;
     if (S > kMaxSlices) S = kMaxSlices;
     const int groups = (kmax + 3) / 4;
     const int cap = (groups + kWavesPerBlock - 1) / kWavesPerBlock;   // >= one group per wave
