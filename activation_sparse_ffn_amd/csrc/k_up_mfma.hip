@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kUW * kWave) void k_up_mfma(const uint8_t* __restri
                                                         const int32_t* __restrict__ count, int kmax, int B,
                                                         int d, int f, float* __restrict__ hact) {
   constexpr int NA = REGLU ? 2 : 1;
-  constexpr int kUU = 4;                        // 32-column steps per wave in flight
+  constexpr int kUU = NT == 1 ? 8 : 4;          // 32-column steps per wave in flight (8 spills at 64 tokens)
   __shared__ f32x4 s_acc[kUW - 1][NA][MT][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
