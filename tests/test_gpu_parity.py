@@ -29,6 +29,10 @@ SCALED = {
     "C3s": S.scaled(S.CONFIGS["C3"], name="C3s", d=1032, f=2080, h=136),
     "C4s": S.scaled(S.CONFIGS["C4"], name="C4s", d=1056, f=2000, h=136),
     "C5s": S.scaled(S.CONFIGS["C5"], name="C5s", d=1032, f=4096, h=264),
+    # predictor layer 1 on the matrix cores with its d walk in 1 part (256 row
+    # tiles of 16) and in 3 parts (69 row tiles)
+    "C2h1": S.scaled(S.CONFIGS["C2"], name="C2h1", d=264, f=2080, h=4096),
+    "C2h3": S.scaled(S.CONFIGS["C2"], name="C2h3", d=1032, f=2080, h=1104),
 }
 
 
@@ -106,7 +110,8 @@ def test_full_size_layer(name, B):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name,B", [("C3s", 16), ("C3s", 32), ("C2s", 17), ("C2s", 64), ("C3s", 64)])
+@pytest.mark.parametrize("name,B", [("C3s", 16), ("C3s", 32), ("C2s", 17), ("C2s", 64), ("C3s", 64),
+                                    ("C2h1", 8), ("C2h3", 8), ("C2h3", 33)])
 def test_matrix_core_predictor(name, B):
     """B >= 16 runs both predictor layers on the matrix cores (hidden split into
     exact 16-bit pieces): scores must still sit within 1e-5 of fp64."""
