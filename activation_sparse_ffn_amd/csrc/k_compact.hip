@@ -12,6 +12,9 @@
 // list in rank order (the last workgroup writing the whole list alone, one
 // scattered store per set bit, took 4-12 us).  The last workgroup to take the
 // closing ticket clears the count words and the ticket.  Nothing leaves the device.
+// A workgroup waits only for workgroups of lower index, which publish before they
+// wait themselves; workgroups are dispatched in index order, so those are running
+// or done (the wait is bounded all the same).
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 
