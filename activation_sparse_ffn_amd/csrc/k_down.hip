@@ -230,8 +230,8 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
 }
 
 
-// ------------------------------------------------------------------ B >= 4
-// From 4 tokens on the products run on the matrix cores: v_mfma_f32_16x16x4_f32
+// ------------------------------------------------------------------ B >= 3
+// From 3 tokens on the products run on the matrix cores: v_mfma_f32_16x16x4_f32
 // (fp32 operands, so the fp32 activations are used as they are and the 16-bit
 // weights convert exactly).  A = 16 column slots x 4 list entries: lane l reads 16
 // bytes (8 consecutive columns) of entry l / 16's row at column slot l % 16, which
@@ -401,10 +401,11 @@ constexpr int lw_for(int nb) {
 
 struct Plan { int lw, cpl, tw, ntiles, S; bool mfma; };
 
-// From 4 tokens on (measured: LLaMA2-7B shape, separate calls, 4 tokens 76.2 -> 58.9 us
-// per layer-step with all three matrix-core kernels; 2 tokens 48.9 -> 54.4, 1 token
-// 35.8 -> 49.7, so below 4 the vector kernels stay).
-bool down_mfma_eligible(int wdt, int B) { return (wdt == DT_F16 || wdt == DT_BF16) && B >= 4 && B <= 64; }
+// From 3 tokens on (measured, separate calls, all three matrix-core kernels against
+// the vector ones: LLaMA2-7B shape 3 tokens 67.5 -> 56.7 us per layer-step, 4 tokens
+// 76.2 -> 58.9, OPT-6.7B shape 3 tokens 68.3 -> 53.0; at 2 tokens every vector kernel
+// was faster, LLaMA2-7B 48.9 against 54.4, at 1 token 35.8 against 49.7).
+bool down_mfma_eligible(int wdt, int B) { return (wdt == DT_F16 || wdt == DT_BF16) && B >= 3 && B <= 64; }
 
 Plan plan_for(int wdt, int B, int d, int kmax) {
   if (down_mfma_eligible(wdt, B)) {

@@ -6,7 +6,7 @@
 // read once and feeds B multiply-adds.  Layer 1 gives one wave per hidden row;
 // layer 2 gives each wave R rows of W2, so a lane keeps R 16-byte loads in flight
 // per chunk.  The hidden vector is kept in fp32 (workspace), never rounded to the
-// weight type.  From B = 4 on (fp16 / bf16) both layers are dense contractions
+// weight type.  From B = 3 on (fp16 / bf16) both layers are dense contractions
 // and run on the matrix cores (k_predict_mfma.hip).
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"

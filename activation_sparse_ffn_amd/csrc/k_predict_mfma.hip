@@ -1,6 +1,6 @@
-// Per-layer predictor on the matrix cores for B >= 4 tokens (PowerInfer page,
-// Method, per-layer predictor of §5.1).  From 4 tokens on, each predictor weight
-// feeds >= 4 multiply-adds and the two layers are dense contractions:
+// Per-layer predictor on the matrix cores for B >= 3 tokens (PowerInfer page,
+// Method, per-layer predictor of §5.1).  From 3 tokens on, each predictor weight
+// feeds >= 3 multiply-adds and the two layers are dense contractions:
 //
 //   layer 1   hidden[b][j] = max(sum_c W1[j][c] x[b][c], 0)       W1, x: fp16 / bf16
 //   layer 2   scores[b][i] = sum_j W2[i][j] hidden[b][j]           hidden: fp32
@@ -313,7 +313,7 @@ int token_tiles(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
 
 bool pred_mfma_eligible(int wdt, int B, int h, int f) {
   (void)h; (void)f;
-  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 4 && B <= 64;   // as down: from 4 tokens
+  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 3 && B <= 64;   // as down: from 3 tokens
 }
 
 // Pieces (pieces x 16 token-tile rows x h halves) | with S > 1 parts of the d

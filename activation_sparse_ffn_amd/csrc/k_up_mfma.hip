@@ -1,11 +1,11 @@
-// Gathered up / gate rows on the matrix cores for B >= 4 tokens (PowerInfer page,
+// Gathered up / gate rows on the matrix cores for B >= 3 tokens (PowerInfer page,
 // Method, neuron-aware operators of §5.4: only the rows of active neurons are read;
 // Paper vs code, activation functions: ReLU and ReGLU).
 //
 //   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0)                 ReLU
 //   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0) * (Wl[idx_j] . x_b)   ReGLU
 //
-// From 4 tokens on every row byte feeds >= 4 multiply-adds and the per-row input
+// From 3 tokens on every row byte feeds >= 3 multiply-adds and the per-row input
 // re-reads of the vector kernel dominate (pad tokens of the 16-token tile cost
 // nothing measurable: the kernel is bound by memory); here the gathered rows are the A operand
 // of v_mfma_f32_16x16x32 (16 list entries x 32 columns: lane l reads 16 bytes of
@@ -184,7 +184,7 @@ hipError_t dispatch(hipStream_t s, int act, int B, int d, int f, const void* x, 
 }  // namespace
 
 bool up_mfma_eligible(int wdt, int B, int d) {
-  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 4 && B <= 64 && d >= 8;   // as down: from 4 tokens
+  return (wdt == DT_F16 || wdt == DT_BF16) && B >= 3 && B <= 64 && d >= 8;   // as down: from 3 tokens
 }
 
 hipError_t launch_up_mfma(hipStream_t s, int wdt, int act, int B, int d, int f, const void* x, const void* Wa,

@@ -91,14 +91,14 @@ int sfx_abi_version(void);
  *   scores  [B][f] fp32, written.
  *   ws      >= sfx_predict_ws(wdt, B, d, h, f) bytes.
  * Rows: d*sizeof(wdt) and h*sizeof(wdt) must be multiples of 16 bytes.
- * From B = 4 on (fp16 / bf16) both layers run on the matrix cores; the second
+ * From B = 3 on (fp16 / bf16) both layers run on the matrix cores; the second
  * takes the fp32 hidden as exact 16-bit pieces (two fp16 or three bf16 terms),
  * so scores keep fp32 accuracy.  With fp16 weights the hidden values must then
  * stay below 65504 in magnitude (the fp16 range of the leading piece); bf16
  * pieces cover the fp32 range.  The workspace then holds those pieces for 16, 32
  * or 64 tokens (B <= 16, <= 32, <= 64) and, when h / 16 is below 256, the first
  * layer's partial sums (its d walk is split over up to 4 workgroups per 16
- * rows) with one control word per 16 rows; below 4 tokens it holds the fp32
+ * rows) with one control word per 16 rows; below 3 tokens it holds the fp32
  * hidden [B][h].
  * ------------------------------------------------------------------------------- */
 size_t sfx_predict_ws(int wdt, int B, int d, int h, int f);
@@ -149,7 +149,7 @@ int sfx_compact(void* stream, int B, int f, const float* scores, float threshold
  *                  [0, f)); count is read on the device and clamped to kmax; an
  *                  index outside [0, f) yields a zero activation.
  *   hact     [kmax][B] fp32; rows j < count are written, the rest are unchanged.
- * Q4 requires d % 32 == 0.  From B = 4 on, fp16 / bf16 rows are multiplied on the
+ * Q4 requires d % 32 == 0.  From B = 3 on, fp16 / bf16 rows are multiplied on the
  * matrix cores (exact 16-bit products, fp32 sums).
  * ------------------------------------------------------------------------------- */
 int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f,
@@ -167,7 +167,7 @@ int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f,
  * The neurons are split into slices; each slice's partial sum goes to the
  * workspace and the last slice to finish a column tile adds the partials in slice
  * order, so y is bitwise reproducible.  y is overwritten (zero when count = 0).
- * From B = 4 on, fp16 / bf16 rows are multiplied on the matrix cores in fp32
+ * From B = 3 on, fp16 / bf16 rows are multiplied on the matrix cores in fp32
  * (16x16x4 fp32 products, the activations used as they are).
  *
  *   Wd        [f][d] wdt, row = neuron (Q4: packed codes); Wd_scales as for Wa.

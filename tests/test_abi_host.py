@@ -117,15 +117,15 @@ def test_workspace_queries_are_monotone(lib):
     a = lib.sfx_sparse_down_ws(1, 1, 4096, 16384)
     b = lib.sfx_sparse_down_ws(1, 8, 4096, 16384)
     assert b > a
-    # below 4 tokens (and for fp32 weights) the fp32 hidden [B][h]; from 4 tokens on
+    # below 3 tokens (and for fp32 weights) the fp32 hidden [B][h]; from 3 tokens on
     # (fp16 / bf16) its exact 16-bit pieces for 16 tokens per matrix-core tile, and
     # with fewer than 256 row tiles of 16 the layer-1 walk is split in S <= 4 parts:
     # one ticket per tile and S fp32 partial tiles (16 rows x 16 tokens) per tile
-    assert lib.sfx_predict_ws(1, 3, 4096, 1024, 16384) == 3 * 1024 * 4
+    assert lib.sfx_predict_ws(1, 2, 4096, 1024, 16384) == 2 * 1024 * 4
     assert lib.sfx_predict_ws(0, 8, 4096, 1024, 16384) == 8 * 1024 * 4
     tiles, S = 1024 // 16, 4
     split = 256 + S * tiles * 16 * 16 * 4                 # tickets (64 words) + partials, per token tile
-    assert lib.sfx_predict_ws(1, 4, 4096, 1024, 16384) == 2 * 16 * 1024 * 2 + split
+    assert lib.sfx_predict_ws(1, 3, 4096, 1024, 16384) == 2 * 16 * 1024 * 2 + split
     assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == 2 * 16 * 1024 * 2 + split
     assert lib.sfx_predict_ws(2, 8, 4096, 1024, 16384) == 3 * 16 * 1024 * 2 + split
     assert lib.sfx_predict_ws(1, 17, 4096, 1024, 16384) == 2 * 32 * 1024 * 2 + 256 + 2 * (split - 256)

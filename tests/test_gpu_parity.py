@@ -76,7 +76,7 @@ def test_c1_true_relu_mask():
 
 
 @pytest.mark.parametrize("name,B", [("C2s", 1), ("C3s", 1), ("C3s", 3), ("C3s", 4), ("C3s", 8), ("C4s", 1),
-                                    ("C4s", 2), ("C2s", 4), ("C5s", 1), ("C5s", 8), ("C5s", 16), ("C5s", 32)])
+                                    ("C4s", 2), ("C2s", 2), ("C2s", 4), ("C5s", 1), ("C5s", 8), ("C5s", 16), ("C5s", 32)])
 def test_scaled_configs(name, B):
     cfg = SCALED[name]
     for layer in range(2):
