@@ -230,7 +230,10 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
  *   ws       >= sfx_ffn_step_ws(wdt, act, B, d, h, f) bytes, zero-filled before
  *            its first use, used on one device only.
  * Returns SFX_E_UNSUPPORTED for shapes the fused kernel is not built for; the
- * separate calls cover those.
+ * separate calls cover those.  From 3 tokens on, the separate calls (which then
+ * run on the matrix cores) measured faster than this kernel on MI355X (LLaMA2-7B
+ * shape at 4 tokens: 58.4 against 70.5 us per layer-step); at 1 and 2 tokens this
+ * kernel is the faster path.
  * ------------------------------------------------------------------------------- */
 typedef struct sfx_layer {
   const void* x;            /* [B][d] */
