@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--tam-lambda", type=float, default=0.9)
     p.add_argument("--tam-eps", type=float, default=0.01)
     p.add_argument("--separate", action="store_true", help="time the five separate calls per layer")
+    p.add_argument("--fused", action="store_true",
+                   help="time sfx_ffn_step where it supports the shape, also from 3 tokens on (by default the "
+                        "separate calls are timed there: on the matrix cores they measured faster)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the calibration of HBM byte counters")
     return p.parse_args()
@@ -150,7 +153,10 @@ def main():
     ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
     tam = TamState(L, G, tam_k, device=dev)
     tensors = [ly.tensors() for ly in layers]
-    fused = (not args.separate) and StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+    # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
+    # separate calls run on the matrix cores and measured faster (--fused forces it)
+    fused = (not args.separate) and (args.fused or B <= 2) and \
+        StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
 
     if fused:
         st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ubits)
