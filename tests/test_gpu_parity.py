@@ -252,13 +252,14 @@ def test_bitwise_determinism():
         assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("B", [2, 8])        # vector kernels; matrix cores (split layer 1, tickets)
+def test_graph_replay_matches_eager(B):
     """The layer-step captured in a HIP graph: every replay (new tokens copied into
     the static input between replays, eager work in between) equals eager."""
     cfg = SCALED["C5s"]
     L = S.make_layer(cfg, 0, device=DEV)
-    xs = _tokens(cfg, 0, 4, 2)
-    buf = StepBuffers(cfg.d, cfg.f, cfg.h, 2, cfg.wdtype, cfg.pdtype)
+    xs = _tokens(cfg, 0, 4, B)
+    buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype)
     x_static = xs[0].clone()
     eager = []
     for s in range(4):
@@ -275,7 +276,7 @@ def test_graph_replay_matches_eager():
     with torch.cuda.graph(graph):
         run_layer(buf, L.tensors(), x_static, L.threshold, cfg.act)
     for s in range(4):
-        say(f"graph replay {s}")
+        say(f"graph replay B={B} {s}")
         x_static.copy_(xs[s])
         graph.replay()
         torch.cuda.synchronize()
