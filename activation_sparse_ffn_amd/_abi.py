@@ -232,12 +232,63 @@ def sfx_ffn_step_ws(wdt: int, act: int, B: int, d: int, h: int, f: int) -> int:
     return load().sfx_ffn_step_ws(wdt, act, B, d, h, f)
 
 
-def layer_descriptors(layers, device=None) -> torch.Tensor:
+TORCH_OF = {SFX_F16: torch.float16, SFX_BF16: torch.bfloat16}
+
+
+def _check_layer(i: int, e: dict, B: int, d: int, h: int, f: int, wdt: int, act: int):
+    """Raise unless layer entry `e` holds what the fused kernel reads and writes:
+    the kernel cannot check device-resident descriptors, so a missing, short or
+    misaligned buffer must be caught here."""
+    W = (f + 31) // 32
+    wt = TORCH_OF.get(wdt)
+    if wt is None:
+        raise TypeError("fused step: weights must be fp16 or bf16")
+    need = ["x", "W1", "W2", "Wa", "Wd", "scores", "union_bits", "idx", "count", "hact", "y"]
+    if act == SFX_REGLU:
+        need.append("Wl")
+    for n in need:
+        if e.get(n) is None:
+            raise ValueError(f"layer {i}: '{n}' is required")
+    shapes = {"x": (B, d), "W1": (h, d), "W2": (f, h), "Wa": (f, d), "Wl": (f, d), "Wd": (f, d)}
+    for n, shp in shapes.items():
+        t = e.get(n)
+        if t is None:
+            continue
+        if t.dtype != wt:
+            raise TypeError(f"layer {i}: '{n}' is {t.dtype}, expected {wt}")
+        if tuple(t.shape) != shp:
+            raise ValueError(f"layer {i}: '{n}' has shape {tuple(t.shape)}, expected {shp}")
+    # outputs and the bias: dtype and at least the elements the kernel touches
+    sizes = {"ba": (torch.float32, f), "scores": (torch.float32, B * f), "hact": (torch.float32, f * B),
+             "y": (torch.float32, B * d), "tok_bits": ((torch.int32, torch.uint32), B * W),
+             "union_bits": ((torch.int32, torch.uint32), W), "idx": ((torch.int32,), f),
+             "count": ((torch.int32,), 1)}
+    for n, (dt, numel) in sizes.items():
+        t = e.get(n)
+        if t is None:
+            continue
+        dts = dt if isinstance(dt, tuple) else (dt,)
+        if t.dtype not in dts:
+            raise TypeError(f"layer {i}: '{n}' is {t.dtype}, expected {dts}")
+        if t.numel() < numel:
+            raise ValueError(f"layer {i}: '{n}' holds {t.numel()} elements, needs >= {numel}")
+    for n, t in e.items():
+        if not isinstance(t, torch.Tensor):
+            continue
+        align = 4 if n in ("tok_bits", "union_bits", "idx", "count", "ba") else 16
+        if t.data_ptr() % align != 0:
+            raise ValueError(f"layer {i}: '{n}' is not {align}-byte aligned")
+
+
+def layer_descriptors(layers, B: int, d: int, h: int, f: int, wdt: int, act, device=None) -> torch.Tensor:
     """Device array of `sfx_layer` descriptors.  `layers` is a list of dicts of
     tensors (x, W1, W2, Wa, ba, Wl, Wd, scores, tok_bits, union_bits, idx, count,
-    hact, y) plus a float `threshold`; missing optional entries are NULL."""
+    hact, y) plus a float `threshold`; missing optional entries (ba, Wl for ReLU,
+    tok_bits) are NULL.  Every entry is checked against the shape (B, d, h, f) first."""
+    a = ACTS[act] if isinstance(act, str) else int(act)
     arr = (SfxLayer * len(layers))()
     for i, e in enumerate(layers):
+        _check_layer(i, e, B, d, h, f, wdt, a)
         for name, _ in SfxLayer._fields_:
             if name in ("threshold", "reserved"):
                 continue

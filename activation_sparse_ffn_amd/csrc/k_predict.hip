@@ -14,7 +14,7 @@
 namespace sfx {
 
 hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
-                            const void* W2, void* ws, float* scores);
+                            const void* W2, void* ws, float* scores, uint32_t* range_flag);
 bool pred_mfma_eligible(int wdt, int B, int h, int f);
 size_t pred_mfma_ws_bytes(int wdt, int B, int h);
 
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const uint8_t* __restric
 
 template <class T, int NB>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
-               const void* W2, float* scores, float* hid, bool mfma, int wdt) {
-  if (mfma) return launch_pred_mfma(s, wdt, B, d, h, f, x, W1, W2, hid, scores);   // hid = the pieces buffer
+               const void* W2, float* scores, float* hid, bool mfma, int wdt, uint32_t* range_flag) {
+  if (mfma) return launch_pred_mfma(s, wdt, B, d, h, f, x, W1, W2, hid, scores, range_flag);   // hid = the pieces buffer
   dim3 blk(kBlock);
   k_pred_hidden<T, NB><<<dim3((h + kWavesPerBlock - 1) / kWavesPerBlock), blk, 0, s>>>(
       (const uint8_t*)x, (const uint8_t*)W1, hid, B, d, h);
@@ -165,35 +165,40 @@ hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const v
 
 template <class T>
 hipError_t dispatch_nb(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
-                       const void* W2, float* scores, float* hid, bool mfma, int wdt) {
+                       const void* W2, float* scores, float* hid, bool mfma, int wdt, uint32_t* flag) {
   switch (nb_class(B)) {
-    case 1: return run<T, 1>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case 2: return run<T, 2>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case 4: return run<T, 4>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case 8: return run<T, 8>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case 16: return run<T, 16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case 32: return run<T, 32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    default: return run<T, 64>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case 1: return run<T, 1>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case 2: return run<T, 2>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case 4: return run<T, 4>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case 8: return run<T, 8>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case 16: return run<T, 16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case 32: return run<T, 32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    default: return run<T, 64>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
   }
 }
 
 }  // namespace
 
+// control line (word 0: sticky fp16-range flag of the matrix-core path) | the fp32
+// hidden [B][h] (vector path) or the pieces, tickets and partial tiles (matrix cores)
+constexpr size_t kCtlBytes = 256;
+
 size_t predict_ws_bytes(int wdt, int B, int d, int h, int f) {
   (void)d;
   size_t hid = (size_t)B * h * sizeof(float);
   if (pred_mfma_eligible(wdt, B, h, f)) hid = pred_mfma_ws_bytes(wdt, B, h);
-  return (hid + 255) & ~(size_t)255;
+  return kCtlBytes + ((hid + 255) & ~(size_t)255);
 }
 
 hipError_t launch_predict(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x,
                           const void* W1, const void* W2, float* scores, void* ws) {
-  float* hid = (float*)ws;
+  uint32_t* flag = (uint32_t*)ws;
+  float* hid = (float*)((uint8_t*)ws + kCtlBytes);
   const bool mfma = pred_mfma_eligible(wdt, B, h, f);
   switch (wdt) {
-    case DT_F32: return dispatch_nb<TF32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case DT_F16: return dispatch_nb<TF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
-    case DT_BF16: return dispatch_nb<TBF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt);
+    case DT_F32: return dispatch_nb<TF32>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case DT_F16: return dispatch_nb<TF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
+    case DT_BF16: return dispatch_nb<TBF16>(s, B, d, h, f, x, W1, W2, scores, hid, mfma, wdt, flag);
     default: return hipErrorInvalidValue;
   }
 }

@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
                                                             const uint8_t* __restrict__ W1,
                                                             uint16_t* __restrict__ hp, int B, int d, int h,
                                                             int S, float* __restrict__ part,
-                                                            uint32_t* __restrict__ tickets) {
+                                                            uint32_t* __restrict__ tickets,
+                                                            uint32_t* __restrict__ range_flag) {
   constexpr int NP = Split<T>::pieces;
   __shared__ f32x4 s_acc[kHW][NT][kWave];
   __shared__ int s_last;
@@ -144,7 +145,11 @@ __global__ __launch_bounds__(kHW * kWave) void k_hidden_mfma(const uint8_t* __re
       const int row = row0 + (lane >> 4) * 4 + i;
       if (row < h) {
         uint16_t pc[NP];
-        Split<T>::run(tok < B ? fmaxf(t[i], 0.f) : 0.f, pc);
+        const float hv = tok < B ? fmaxf(t[i], 0.f) : 0.f;
+        // fp16 pieces: a hidden value past the fp16 range has no finite leading
+        // piece; the call's scores are then wrong, so the sticky flag records it
+        if (Split<T>::max_finite > 0.f && !(hv <= Split<T>::max_finite)) store_through(range_flag, 1u);
+        Split<T>::run(hv, pc);
 #pragma unroll
         for (int p = 0; p < NP; ++p) hp[p * tstride + (size_t)tok * h + row] = pc[p];
       }
@@ -286,10 +291,10 @@ __global__ __launch_bounds__(kSWB * kWave) void k_scores_mfma(const uint8_t* __r
 
 template <class T, int NT>
 hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-               uint16_t* hp, float* scores, float* part, uint32_t* tickets) {
+               uint16_t* hp, float* scores, float* part, uint32_t* tickets, uint32_t* range_flag) {
   const int S = hidden_split(h);
   k_hidden_mfma<T, NT><<<dim3(((h + 15) / 16) * S), dim3(kHW * kWave), 0, s>>>(
-      (const uint8_t*)x, (const uint8_t*)W1, hp, B, d, h, S, part, tickets);
+      (const uint8_t*)x, (const uint8_t*)W1, hp, B, d, h, S, part, tickets, range_flag);
   const int rtiles = (f + 15) / 16;
   const int wpt = (rtiles + kSWB - 1) / kSWB < kPredCUs ? 2 : 1;
   const int per_wg = kSWB / wpt;
@@ -300,10 +305,10 @@ hipError_t run(hipStream_t s, int B, int d, int h, int f, const void* x, const v
 
 template <class T>
 hipError_t dispatch(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1, const void* W2,
-                    uint16_t* hp, float* scores, float* part, uint32_t* tickets) {
-  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
-  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
-  return run<T, 4>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
+                    uint16_t* hp, float* scores, float* part, uint32_t* tickets, uint32_t* range_flag) {
+  if (B <= 16) return run<T, 1>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets, range_flag);
+  if (B <= 32) return run<T, 2>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets, range_flag);
+  return run<T, 4>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets, range_flag);
 }
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -328,7 +333,7 @@ size_t pred_mfma_ws_bytes(int wdt, int B, int h) {
 }
 
 hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x, const void* W1,
-                            const void* W2, void* ws, float* scores) {
+                            const void* W2, void* ws, float* scores, uint32_t* range_flag) {
   const int np = wdt == DT_BF16 ? Split<TBF16>::pieces : Split<TF16>::pieces;
   const int tiles = (h + 15) / 16;
   uint8_t* base = (uint8_t*)ws;
@@ -336,8 +341,8 @@ hipError_t launch_pred_mfma(hipStream_t s, int wdt, int B, int d, int h, int f, 
   const size_t off_t = up256((size_t)np * token_tiles(B) * 16 * h * sizeof(uint16_t));
   uint32_t* tickets = (uint32_t*)(base + off_t);
   float* part = (float*)(base + off_t + up256((size_t)tiles * 4));
-  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
-  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets);
+  if (wdt == DT_F16) return dispatch<TF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets, range_flag);
+  return dispatch<TBF16>(s, B, d, h, f, x, W1, W2, hp, scores, part, tickets, range_flag);
 }
 
 }  // namespace sfx

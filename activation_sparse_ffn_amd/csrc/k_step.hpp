@@ -818,6 +818,24 @@ hipError_t run_step(hipStream_t s, const StepParams& p, int act, int P) {
   return hipGetLastError();
 }
 
+// Workgroups of this instantiation that fit on one compute unit at once (registers,
+// LDS): the grid of one workgroup per compute unit is resident only when this is >= 1.
+template <class T, int NB, int DL>
+int blocks_per_cu(int act) {
+  int n = 0;
+  hipError_t e = act == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_step<T, NB, true, DL>, kNT, 0)
+                          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_step<T, NB, false, DL>, kNT, 0);
+  return e == hipSuccess ? n : 0;
+}
+template <class T>
+int step_blocks_per_cu(int act, int B) {
+  switch (nb_class(B)) {
+    case 1: return blocks_per_cu<T, 1, 1>(act);
+    case 2: return blocks_per_cu<T, 2, 1>(act);
+    default: return blocks_per_cu<T, 4, 1>(act);
+  }
+}
+
 // Built for d <= 4096 and B <= 4 (the register budget of 2 waves per SIMD holds
 // every phase without spilling there).
 template <class T>

@@ -6,4 +6,5 @@ hipError_t launch_step_bf16(hipStream_t s, const StepParams& p, int act, int P, 
   (void)DL;
   return step::dispatch_step<TBF16>(s, p, act, P);
 }
+int step_blocks_per_cu_bf16(int act, int B) { return step::step_blocks_per_cu<TBF16>(act, B); }
 }  // namespace sfx

@@ -6,4 +6,5 @@ hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, i
   (void)DL;
   return step::dispatch_step<TF16>(s, p, act, P);
 }
+int step_blocks_per_cu_f16(int act, int B) { return step::step_blocks_per_cu<TF16>(act, B); }
 }  // namespace sfx

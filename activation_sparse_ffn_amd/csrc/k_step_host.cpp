@@ -2,6 +2,8 @@
 // workspace and its launch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 #include "sfx_step.hpp"
@@ -10,6 +12,8 @@ namespace sfx {
 
 hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, int DL);
 hipError_t launch_step_bf16(hipStream_t s, const StepParams& p, int act, int P, int DL);
+int step_blocks_per_cu_f16(int act, int B);
+int step_blocks_per_cu_bf16(int act, int B);
 
 namespace {
 constexpr int kNT = 512, kW2Bytes = 131072, kRedFloats = 1024;
@@ -92,6 +96,25 @@ StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layer
   off += up256((size_t)g.P * p.us * 8);
   p.hact = (unsigned long long*)(base + off);
   return p;
+}
+
+// The persistent grid (one workgroup per compute unit) is only resident when one
+// workgroup of the instantiation fits on a compute unit.  Host-side occupancy query,
+// cached per device and instantiation.
+bool step_resident(int wdt, int act, int B) {
+  static std::atomic<int> cache[8][2][2][3];   // device, dtype, act, token class: 0 unknown, 1 yes, 2 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  const int nb = nb_class(B), ci = nb == 1 ? 0 : nb == 2 ? 1 : 2;
+  const int di = wdt == DT_BF16 ? 1 : 0;
+  std::atomic<int>* c = dev < 8 ? &cache[dev][di][act & 1][ci] : nullptr;
+  if (c != nullptr) {
+    const int v = c->load(std::memory_order_relaxed);
+    if (v != 0) return v == 1;
+  }
+  const int n = wdt == DT_BF16 ? step_blocks_per_cu_bf16(act, B) : step_blocks_per_cu_f16(act, B);
+  if (c != nullptr) c->store(n >= 1 ? 1 : 2, std::memory_order_relaxed);
+  return n >= 1;
 }
 
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,

@@ -181,6 +181,7 @@ size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f) {
   const int P = sfx::device_cu_count();
   if (P <= 0) return 0;
   if (!sfx::step_geometry(wdt, act, B, d, h, f, P).ok) return 0;
+  if (!sfx::step_resident(wdt, act, B)) return 0;
   return sfx::step_ws_bytes(B, h, f, P);
 }
 
@@ -195,6 +196,7 @@ int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int
   if (P <= 0) return SFX_E_DEVICE;
   const sfx::StepGeom g = sfx::step_geometry(wdt, act, B, d, h, f, P);
   if (!g.ok) return SFX_E_UNSUPPORTED;
+  if (!sfx::step_resident(wdt, act, B)) return SFX_E_UNSUPPORTED;
   const int w = check_ws(ws, ws_bytes, sfx::step_ws_bytes(B, h, f, P));
   if (w != SFX_OK) return w;
   return launch_status(sfx::launch_step((hipStream_t)stream, wdt, act, B, d, h, f, L, layers, ws, g));

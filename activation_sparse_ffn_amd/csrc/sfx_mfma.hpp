@@ -42,6 +42,7 @@ template <>
 struct Split<TF16> {
   static constexpr int pieces = 2;
   static constexpr int accumulators = 2;     // hi and lo are summed apart (lo is scaled)
+  static constexpr float max_finite = 65504.0f;   // largest value whose hi piece is finite
   __device__ __forceinline__ static void run(float v, uint16_t* out) {
     const _Float16 hi = (_Float16)v;
     const _Float16 lo = (_Float16)((v - (float)hi) * 2048.0f);
@@ -55,6 +56,7 @@ template <>
 struct Split<TBF16> {
   static constexpr int pieces = 3;
   static constexpr int accumulators = 1;     // the three pieces share one accumulator
+  static constexpr float max_finite = 0.0f;  // no limit: bf16 pieces cover the fp32 range
   __device__ __forceinline__ static void run(float v, uint16_t* out) {
     const __bf16 hi = (__bf16)v;
     const float r1 = v - (float)hi;

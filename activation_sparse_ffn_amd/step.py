@@ -31,6 +31,22 @@ class StepBuffers:
         self.ws_comp = A.workspace(A.sfx_compact_ws(B, f), dev)
         self.ws_down = A.workspace(A.sfx_sparse_down_ws(WDT_CODE[wdtype], B, d, self.kmax), dev)
 
+    def status(self) -> dict:
+        """Sticky status words of the workspaces (synchronises): the predictor's
+        fp16-range flag and the compaction's timeout word; nonzero means some call
+        since the last `clear_status` produced undefined results."""
+        return {"predict_range": int(self.ws_pred[:4].view(torch.int32).item()),
+                "compact_timeout": int(self.ws_comp[4:8].view(torch.int32).item())}
+
+    def clear_status(self):
+        self.ws_pred[:4].zero_()
+        self.ws_comp[4:8].zero_()
+
+    def check_status(self):
+        st = self.status()
+        if any(st.values()):
+            raise RuntimeError(f"libsfx status words set: {st}")
+
 
 def run_layer(buf: StepBuffers, layer, x: torch.Tensor, threshold: float, act: str,
               tok_bits: bool = True, stream=None):
@@ -112,7 +128,7 @@ class StackStep:
             e.update(wt)
             e["x"] = x
             entries.append(e)
-        return A.layer_descriptors(entries, self.device)
+        return A.layer_descriptors(entries, self.B, self.d, self.h, self.f, self.wdt, self.act, self.device)
 
     def run(self, descs: torch.Tensor, stream=None):
         A.sfx_ffn_step(self.wdt, self.act, self.B, self.d, self.h, self.f, descs, self.ws, stream=stream)
@@ -121,4 +137,14 @@ class StackStep:
         return torch.cat([b["count"] for b in self.bufs])
 
     def error_word(self) -> int:
+        """The fused kernel's sticky error word (synchronises): nonzero once a wait of
+        some launch on this workspace timed out."""
         return int(self.ws[:4].view(torch.int32).item())
+
+    def clear_error(self):
+        self.ws[:4].zero_()
+
+    def check_status(self):
+        e = self.error_word()
+        if e != 0:
+            raise RuntimeError(f"sfx_ffn_step: a grid wait timed out (error word {e})")

@@ -27,8 +27,9 @@
  *     of a weight matrix must span a multiple of 16 bytes.
  *   - Workspaces must be 256-byte aligned, at least as large as the matching
  *     *_ws() query, and zero-filled before their first use; each call leaves the
- *     control words it uses at zero again.  One workspace must not be used by two
- *     calls that may run at the same time.
+ *     control words it uses at zero again, except the sticky status words named
+ *     below, which stay set until the caller clears them.  One workspace must not
+ *     be used by two calls that may run at the same time.
  *   - Batch B (tokens per step) is 1..SFX_MAX_B.
  *   - The data passed to one call must not change until that call's kernels end.
  */
@@ -94,12 +95,17 @@ int sfx_abi_version(void);
  * From B = 3 on (fp16 / bf16) both layers run on the matrix cores; the second
  * takes the fp32 hidden as exact 16-bit pieces (two fp16 or three bf16 terms),
  * so scores keep fp32 accuracy.  With fp16 weights the hidden values must then
- * stay below 65504 in magnitude (the fp16 range of the leading piece); bf16
- * pieces cover the fp32 range.  The workspace then holds those pieces for 16, 32
+ * stay within 65504 in magnitude (the fp16 range of the leading piece); bf16
+ * pieces cover the fp32 range.  Below 3 tokens (and for fp32 weights) there is no
+ * such limit.
+ * Workspace: a 256-byte control line, then (from 3 tokens) the pieces for 16, 32
  * or 64 tokens (B <= 16, <= 32, <= 64) and, when h / 16 is below 256, the first
  * layer's partial sums (its d walk is split over up to 4 workgroups per 16
- * rows) with one control word per 16 rows; below 3 tokens it holds the fp32
- * hidden [B][h].
+ * rows) with one control word per 16 rows; below 3 tokens the fp32 hidden [B][h].
+ * Word 0 of the control line is a sticky range flag: the matrix-core path sets it
+ * nonzero when a hidden value is above 65504 (or NaN) with fp16 weights, and the
+ * scores of that call are then wrong (inf / NaN terms).  The library never clears
+ * it; the caller reads it after synchronising and writes zero to reset it.
  * ------------------------------------------------------------------------------- */
 size_t sfx_predict_ws(int wdt, int B, int d, int h, int f);
 int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
@@ -124,7 +130,9 @@ int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
  *              up to 256).  The workgroups hand their counts to each other through
  *              it with bounded waits: a count that does not arrive within the bound
  *              sets word 1 of the workspace nonzero instead of hanging, and the list
- *              of that call is then undefined.
+ *              of that call is then undefined.  Word 1 is sticky: the library never
+ *              clears it; the caller reads it after synchronising (nonzero = some
+ *              call since the last reset timed out) and writes zero to reset it.
  * ------------------------------------------------------------------------------- */
 size_t sfx_compact_ws(int B, int f);
 int sfx_compact(void* stream, int B, int f, const float* scores, float threshold,
@@ -217,10 +225,15 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
  * layer's input is read.  Same passages as those four calls.
  *
  * One persistent workgroup per compute unit; phases are separated by grid
- * barriers in the workspace, so the grid must be resident on the device (nothing
- * else running on it).  A barrier that does not complete within its bound sets
- * word 0 of the workspace nonzero instead of hanging, and the outputs of that call
- * are then undefined.
+ * barriers in the workspace, so the grid must be resident on the device: the call
+ * returns SFX_E_UNSUPPORTED when the occupancy query says one workgroup does not
+ * fit on a compute unit, and kernels of other streams running at the same time
+ * can still keep workgroups from starting.  A wait that does not complete within
+ * its bound sets word 0 of the workspace nonzero instead of hanging, and the
+ * outputs of that call are then undefined.  Word 0 is sticky: the library never
+ * clears it, and while it is set the waits of later calls on the workspace give
+ * up early (their outputs are undefined too).  The caller reads it after
+ * synchronising and writes zero to reset it.
  *
  *   wdt      SFX_F16 or SFX_BF16 (x, predictor and FFN rows).  act: ReLU / ReGLU.
  *   B        1..4.   d <= 4096, d and h multiples of 8, f <= 32768.

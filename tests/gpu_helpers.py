@@ -31,6 +31,7 @@ def gpu_layer_step(cfg, L, x: torch.Tensor, threshold=None, buf=None):
     t = L.threshold if threshold is None else threshold
     run_layer(buf, L.tensors(), x, t, cfg.act)
     torch.cuda.synchronize()
+    buf.check_status()
     k = int(buf.count.item())
     return {
         "scores": buf.scores.cpu().numpy(),

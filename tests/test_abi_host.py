@@ -48,7 +48,7 @@ ODD = P(0x10004)
 
 def test_predict_validation(lib):
     ws_n = lib.sfx_predict_ws(1, 1, 4096, 1024, 16384)
-    assert ws_n == 4096
+    assert ws_n == 256 + 4096                   # control line + fp32 hidden
     ws = P(0x20000)
     call = lambda **k: lib.sfx_predict(None, k.get("wdt", 1), k.get("B", 1), k.get("d", 4096), k.get("h", 1024),
                                        k.get("f", 16384), k.get("x", GOOD), GOOD, GOOD, k.get("s", GOOD),
@@ -117,20 +117,22 @@ def test_workspace_queries_are_monotone(lib):
     a = lib.sfx_sparse_down_ws(1, 1, 4096, 16384)
     b = lib.sfx_sparse_down_ws(1, 8, 4096, 16384)
     assert b > a
-    # below 3 tokens (and for fp32 weights) the fp32 hidden [B][h]; from 3 tokens on
-    # (fp16 / bf16) its exact 16-bit pieces for 16 tokens per matrix-core tile, and
-    # with fewer than 256 row tiles of 16 the layer-1 walk is split in S <= 4 parts:
-    # one ticket per tile and S fp32 partial tiles (16 rows x 16 tokens) per tile
-    assert lib.sfx_predict_ws(1, 2, 4096, 1024, 16384) == 2 * 1024 * 4
-    assert lib.sfx_predict_ws(0, 8, 4096, 1024, 16384) == 8 * 1024 * 4
+    # a 256-byte control line (the sticky fp16-range flag), then: below 3 tokens (and
+    # for fp32 weights) the fp32 hidden [B][h]; from 3 tokens on (fp16 / bf16) its
+    # exact 16-bit pieces for 16 tokens per matrix-core tile, and with fewer than
+    # 256 row tiles of 16 the layer-1 walk is split in S <= 4 parts: one ticket per
+    # tile and S fp32 partial tiles (16 rows x 16 tokens) per tile
+    ctl = 256
+    assert lib.sfx_predict_ws(1, 2, 4096, 1024, 16384) == ctl + 2 * 1024 * 4
+    assert lib.sfx_predict_ws(0, 8, 4096, 1024, 16384) == ctl + 8 * 1024 * 4
     tiles, S = 1024 // 16, 4
     split = 256 + S * tiles * 16 * 16 * 4                 # tickets (64 words) + partials, per token tile
-    assert lib.sfx_predict_ws(1, 3, 4096, 1024, 16384) == 2 * 16 * 1024 * 2 + split
-    assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == 2 * 16 * 1024 * 2 + split
-    assert lib.sfx_predict_ws(2, 8, 4096, 1024, 16384) == 3 * 16 * 1024 * 2 + split
-    assert lib.sfx_predict_ws(1, 17, 4096, 1024, 16384) == 2 * 32 * 1024 * 2 + 256 + 2 * (split - 256)
+    assert lib.sfx_predict_ws(1, 3, 4096, 1024, 16384) == ctl + 2 * 16 * 1024 * 2 + split
+    assert lib.sfx_predict_ws(1, 8, 4096, 1024, 16384) == ctl + 2 * 16 * 1024 * 2 + split
+    assert lib.sfx_predict_ws(2, 8, 4096, 1024, 16384) == ctl + 3 * 16 * 1024 * 2 + split
+    assert lib.sfx_predict_ws(1, 17, 4096, 1024, 16384) == ctl + 2 * 32 * 1024 * 2 + 256 + 2 * (split - 256)
     # 256 row tiles: no split
-    assert lib.sfx_predict_ws(1, 8, 4096, 4096, 16384) == 2 * 16 * 4096 * 2
+    assert lib.sfx_predict_ws(1, 8, 4096, 4096, 16384) == ctl + 2 * 16 * 4096 * 2
     assert lib.sfx_predict_ws(1, 0, 4096, 1024, 16384) == 0
 
 

@@ -285,3 +285,38 @@ def test_graph_replay_matches_eager(B):
         assert np.array_equal(buf.idx[:k].cpu().numpy(), eager[s]["idx"])
         assert np.array_equal(buf.y.cpu().numpy(), eager[s]["y"])
         _ = torch.randn(1000, device=DEV).sum().item()      # eager work between replays
+
+
+@pytest.mark.parametrize("B", [3, 1])
+def test_predict_fp16_range_flag(B):
+    """fp16 predictor with one hidden value far past 65504: from 3 tokens (matrix
+    cores, fp16 hi + lo pieces) the sticky range flag is set; at one token (vector
+    path, fp32 hidden) there is no limit, the flag stays clear and the scores match
+    fp64.  A normal input leaves the flag clear on both paths."""
+    d, h, f = 512, 64, 1024
+    g = torch.Generator(device="cpu").manual_seed(7)
+    x = torch.randn(B, d, generator=g, dtype=torch.float64)
+    W1 = torch.randn(h, d, generator=g, dtype=torch.float64) / d ** 0.5
+    W2 = torch.randn(f, h, generator=g, dtype=torch.float64) / h ** 0.5
+    x16, W216 = x.to(torch.float16), W2.to(torch.float16)
+    scores = torch.empty(B, f, dtype=torch.float32, device=DEV)
+    ws = A.workspace(A.sfx_predict_ws(A.SFX_F16, B, d, h, f))
+    for big in (False, True):
+        W1b = W1.clone()
+        if big:
+            # hidden row 5 of token 0 = 1000 * sum|x_0| ~ 4e5
+            W1b[5] = 1000.0 * torch.sign(x16[0].to(torch.float64))
+        W116 = W1b.to(torch.float16)
+        ws.zero_()
+        say(f"fp16 range flag B={B} big={big}")
+        A.sfx_predict(x16.to(DEV), W116.to(DEV), W216.to(DEV), scores, ws)
+        torch.cuda.synchronize()
+        flag = int(ws[:4].view(torch.int32).item())
+        if big and B >= 3:
+            assert flag != 0
+            continue
+        assert flag == 0
+        s64 = O.predict(x16.numpy().astype(np.float64), W116.numpy().astype(np.float64),
+                        W216.numpy().astype(np.float64))
+        err = np.max(np.abs(scores.cpu().numpy().astype(np.float64) - s64) / np.maximum(1.0, np.abs(s64)))
+        assert err <= 1e-5, err

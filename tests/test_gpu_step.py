@@ -28,8 +28,11 @@ def _outputs(st: StackStep, l: int):
             "count": k, "hact": b["hact"][:k].cpu().numpy(), "y": b["y"].cpu().numpy()}
 
 
-def _run_and_check(cfg, L, B, steps, layers=None):
+def _run_and_check(cfg, L, B, steps, layers=None, threshold=None, min_k=None):
     layers = layers or [S.make_layer(cfg, l, device=DEV) for l in range(L)]
+    if threshold is not None:
+        for ly in layers:
+            ly.threshold = threshold
     lnp = [layer_np(ly) for ly in layers]
     xs = [S.make_tokens(cfg, l, steps, B, device=DEV) for l in range(L)]
     assert StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
@@ -45,6 +48,8 @@ def _run_and_check(cfg, L, B, steps, layers=None):
             if s % 2 == 1:                     # tok_bits not requested this step: keep the last ones out
                 out["tok_bits"] = None
             r = check_step(cfg, lnp[l], S.storage_numpy(xs[l][s]), out, layers[l].threshold)
+            if min_k is not None:
+                assert r["count"] > min_k, r
             if l == 0:
                 say("   ", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in r.items()})
     return st
@@ -123,3 +128,70 @@ def test_fused_determinism_and_graph_replay():
             for key in ("idx", "hact", "y"):
                 assert np.array_equal(o[key], eager[s][l][key]), (s, l, key)
         _ = torch.randn(1000, device=DEV).sum().item()
+
+
+# Active lists longer than the LDS copy of the list (4920 entries: the down phase
+# then finds each rank's neuron from the union words) and W2 rows that do not fit
+# the 128 KB LDS region (d = 4096, h = 1024, f = 32768: 4 mask words = 256 KB of
+# W2 per workgroup, so the scores read W2 from memory).
+NID_CAP = 4920
+WIDE = S.scaled(S.CONFIGS["C2"], name="C2w", d=4096, f=32768, h=1024)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_fused_long_list_w2_from_memory(B):
+    # scores are N(0, 1/2): this threshold leaves ~20% of the neurons active per
+    # token (k ~ 6.5k at 1 token, ~19k for the union of 4)
+    t = float(np.float32(0.5951))
+    _run_and_check(WIDE, 2, B, 2, threshold=t, min_k=NID_CAP)
+    torch.cuda.empty_cache()
+
+
+def test_fused_long_list_w2_in_lds():
+    """OPT-6.7B shape (W2 rows in LDS) with every neuron active: 16384 > 4920."""
+    cfg = S.CONFIGS["C2"]
+    _run_and_check(cfg, 2, 1, 1, threshold=float("-inf"), min_k=NID_CAP)
+    torch.cuda.empty_cache()
+
+
+def test_fused_benchmark_launch():
+    """The launch the benchmark times: all 32 layers of the OPT-6.7B-shaped stack at
+    one token, union words in one [L][W] array, no per-token masks, two steps per
+    graph, replayed twice.  Every replay matches an eager run bit for bit, and
+    layers 0, 15 and 31 of the last step match the oracle."""
+    cfg = S.CONFIGS["C2"]
+    L, B, steps = cfg.layers, 1, 4
+    W = cfg.groups
+    say("benchmark launch: generating 32 layers")
+    layers = [S.make_layer(cfg, l, device=DEV) for l in range(L)]
+    xs = [S.make_tokens(cfg, l, steps, B, device=DEV) for l in range(L)]
+    ubits = torch.zeros(L, W, dtype=torch.int32, device=DEV)
+    st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, union_bits=ubits)
+    descs = [st.descriptors([xs[l][s] for l in range(L)], tok_bits=False) for s in range(steps)]
+    # eager reference of the last step
+    st.run(descs[steps - 1])
+    torch.cuda.synchronize()
+    st.check_status()
+    eager = [_outputs(st, l) for l in range(L)]
+    say("benchmark launch: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in (steps - 2, steps - 1):
+            st.run(descs[s])
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        st.check_status()
+        for l in range(L):
+            o = _outputs(st, l)
+            for key in ("scores", "union_bits", "idx", "hact", "y"):
+                assert np.array_equal(o[key], eager[l][key]), (rep, l, key)
+        assert np.array_equal(ubits.cpu().numpy()[L - 1], eager[L - 1]["union_bits"].view(np.int32))
+        _ = torch.randn(1000, device=DEV).sum().item()
+    for l in (0, 15, 31):
+        out = _outputs(st, l)
+        out["tok_bits"] = None
+        r = check_step(cfg, layer_np(layers[l]), S.storage_numpy(xs[l][steps - 1]), out, layers[l].threshold)
+        say(f"   layer {l}", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in r.items()})
+    del layers, st
+    torch.cuda.empty_cache()
