@@ -22,7 +22,8 @@ WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
-           "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step")
+           "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc")
+SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
 
 class SfxLayer(ctypes.Structure):
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_sparse_down_ws.argtypes = [I, I, I, I]
     lib.sfx_sparse_down.restype = I
     lib.sfx_sparse_down.argtypes = [P, I, I, I, I, P, P, P, P, I, P, P, P, Z]
+    lib.sfx_sparse_down_noalloc.restype = I
+    lib.sfx_sparse_down_noalloc.argtypes = [P, I, I, I, I, P, P, P, P, I, P, P]
     lib.sfx_tam_ws.restype = Z
     lib.sfx_tam_ws.argtypes = [I, I]
     lib.sfx_tam_update.restype = I
@@ -211,6 +214,20 @@ def sfx_sparse_down(Wd, idx, count, hact, y, ws, Wd_scales=None, stream=None):
     q = (_ptr(hact), _ptr(y), _ptr(ws))
     st = load().sfx_sparse_down(_stream(stream), wdt, B, d, f, *p, kmax, *q, ws.numel() if ws is not None else 0)
     _check(st, "sfx_sparse_down")
+
+
+def sfx_sparse_down_noalloc(Wd, idx, count, hact, y, Wd_scales=None, stream=None):
+    """sfx_sparse_down without a workspace: the library's static scratch is used
+    (shared by every call on the GPU, so calls must not overlap)."""
+    B, d = y.shape
+    f = Wd.shape[0]
+    wdt = _wdt_of(Wd)
+    kmax = idx.numel()
+    _need(y, torch.float32, "y")
+    _need(hact, torch.float32, "hact")
+    p = (_ptr(Wd), _ptr(Wd_scales), _ptr(idx), _ptr(count))
+    st = load().sfx_sparse_down_noalloc(_stream(stream), wdt, B, d, f, *p, kmax, _ptr(hact), _ptr(y))
+    _check(st, "sfx_sparse_down_noalloc")
 
 
 def sfx_tam_update(union_bits, lam, eps, K, score, hot_bits, entered_bits, left_bits, topk, topk_count,

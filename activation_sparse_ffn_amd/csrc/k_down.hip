@@ -11,6 +11,9 @@
 // writes one partial tile.  The last workgroup of a tile to finish (ticket in the
 // workspace) adds the S partials in slice order and writes y: no atomics on data,
 // and y is the same bit for bit on every run.
+#include <atomic>
+#include <mutex>
+
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 #include "sfx_mfma.hpp"
@@ -526,6 +529,41 @@ hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* 
       }
     default: return hipErrorInvalidValue;
   }
+}
+
+// ------------------------------------------------------------------ static scratch
+// Workspace of sfx_sparse_down_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Its device address is looked
+// up once per device (with that device current) and kept; host code uses only that
+// address, never the array's name.  The ticket words at its start are zero when the
+// module loads and every call leaves them at zero (the last workgroup of each
+// column tile resets its ticket), so each call starts from cleared tickets.
+static __device__ __align__(256) uint8_t scratch[kDownScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t down_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace sfx

@@ -71,6 +71,7 @@ const char* sfx_status_str(int status) {
     case SFX_E_LAUNCH: return "HIP reported a launch error";
     case SFX_E_UNSUPPORTED: return "combination not built";
     case SFX_E_DEVICE: return "no current HIP device";
+    case SFX_E_SCRATCH: return "needs more scratch than the static maximum (SFX_DOWN_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -156,6 +157,23 @@ int sfx_sparse_down(void* stream, int wdt, int B, int d, int f, const void* Wd, 
   if (w != SFX_OK) return w;
   return launch_status(sfx::launch_down((hipStream_t)stream, wdt, B, d, f, Wd, Wd_scales, idx, count, kmax,
                                         hact, y, ws));
+}
+
+int sfx_sparse_down_noalloc(void* stream, int wdt, int B, int d, int f, const void* Wd, const void* Wd_scales,
+                            const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || f < 1 || kmax < 1) return SFX_E_SHAPE;
+  if (!Wd || !idx || !count || !hact || !y) return SFX_E_NULL;
+  if (wdt == SFX_Q4G32 && !Wd_scales) return SFX_E_NULL;
+  if (!row_ok(wdt, d)) return wdt == SFX_Q4G32 ? SFX_E_SHAPE : SFX_E_ALIGN;
+  if (!aligned16(Wd) || !aligned16(hact) || !aligned16(y)) return SFX_E_ALIGN;
+  if (!sfx::down_supported(wdt, B)) return SFX_E_UNSUPPORTED;
+  const size_t need = sfx::down_ws_bytes(wdt, B, d, kmax);
+  if (need > sfx::kDownScratchBytes) return SFX_E_SCRATCH;
+  void* scratch = nullptr;
+  if (sfx::down_scratch(&scratch) != hipSuccess) return SFX_E_DEVICE;
+  return launch_status(sfx::launch_down((hipStream_t)stream, wdt, B, d, f, Wd, Wd_scales, idx, count, kmax,
+                                        hact, y, scratch));
 }
 
 // ------------------------------------------------------------------------------ TAM

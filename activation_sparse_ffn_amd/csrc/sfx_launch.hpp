@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/sfx.h"
+
 namespace sfx {
 
 int device_cu_count();  // cached per device; 0 if no device
@@ -29,6 +31,10 @@ hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* 
                        const void* Wd_s, const int32_t* idx, const int32_t* count, int kmax,
                        const float* hact, float* y, void* ws);
 bool down_supported(int wdt, int B);
+// Static scratch of the down kernel for callers that cannot allocate: its size, and
+// its device address on the current device (looked up on the first call per device).
+constexpr size_t kDownScratchBytes = SFX_DOWN_SCRATCH_BYTES;
+hipError_t down_scratch(void** ptr);
 
 size_t tam_ws_bytes(int G, int K);
 hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, float lambda,

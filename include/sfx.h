@@ -46,6 +46,7 @@ extern "C" {
 #define SFX_ABI_VERSION 1
 #define SFX_MAX_B 64
 #define SFX_MAX_GROUPS 1024
+#define SFX_DOWN_SCRATCH_BYTES ((size_t)17 << 20)   /* static scratch of sfx_sparse_down_noalloc */
 
 typedef enum {
   SFX_OK = 0,
@@ -56,7 +57,8 @@ typedef enum {
   SFX_E_WORKSPACE = -5,   /* workspace NULL, misaligned or smaller than the query */
   SFX_E_LAUNCH = -6,      /* HIP reported an error for an enqueued kernel */
   SFX_E_UNSUPPORTED = -7, /* the combination is valid but not built */
-  SFX_E_DEVICE = -8       /* no current HIP device could be queried */
+  SFX_E_DEVICE = -8,      /* no current HIP device could be queried */
+  SFX_E_SCRATCH = -9      /* the shape needs more than the library's static scratch */
 } sfx_status;
 
 typedef enum {
@@ -188,6 +190,23 @@ int sfx_sparse_down(void* stream, int wdt, int B, int d, int f,
                     const void* Wd, const void* Wd_scales,
                     const int32_t* idx, const int32_t* count, int kmax, const float* hact,
                     float* y, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_sparse_down_noalloc -- sfx_sparse_down for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments, same kernels, same y bit for bit, without `ws`.  The
+ * partial tiles and tickets live in a static device array of the library, one per
+ * GPU, of SFX_DOWN_SCRATCH_BYTES (17 MiB), held until the process ends; shapes
+ * whose sfx_sparse_down_ws exceeds it return SFX_E_SCRATCH before anything is
+ * enqueued (every fp16 / bf16 shape up to d = 8192 and 64 tokens fits).  The call allocates nothing (no hipMalloc, no library
+ * allocation); the first call on a device looks up the array's address there.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (other streams, or concurrent host threads) race and give undefined y.
+ * ------------------------------------------------------------------------------- */
+int sfx_sparse_down_noalloc(void* stream, int wdt, int B, int d, int f,
+                            const void* Wd, const void* Wd_scales,
+                            const int32_t* idx, const int32_t* count, int kmax, const float* hact,
+                            float* y);
 
 /* ---------------------------------------------------------------------------------
  * sfx_tam_update -- temporal activation momentum over groups of 32 neurons (KAIROX

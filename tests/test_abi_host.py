@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert A.abi_version() == 1
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert A.status_str(s) and A.status_str(s) != "unknown status"
     assert A.status_str(-99) == "unknown status"
 
@@ -142,3 +142,26 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         A.sfx_predict(x, torch.zeros(8, 64, dtype=torch.float16), torch.zeros(16, 8, dtype=torch.float16),
                       torch.zeros(1, 16), torch.zeros(256, dtype=torch.uint8))
+
+
+def test_down_noalloc_validation(lib):
+    """The no-allocation down call checks like sfx_sparse_down, and rejects a shape
+    whose workspace exceeds the static scratch before touching the device."""
+    E_SCRATCH = -9
+    call = lambda **k: lib.sfx_sparse_down_noalloc(None, k.get("wdt", 1), k.get("B", 1), k.get("d", 4096),
+                                                   16384, k.get("Wd", GOOD), None, GOOD, GOOD, 16384,
+                                                   k.get("hact", GOOD), GOOD)
+    assert call(wdt=7) == E_DTYPE
+    assert call(B=0) == E_SHAPE and call(B=65) == E_SHAPE
+    assert call(Wd=None) == E_NULL
+    assert call(hact=ODD) == E_ALIGN
+    assert call(wdt=3) == E_NULL                 # int4 needs its scales
+    big = 1 << 30                                # one ticket word per 128-column tile: 32 MiB
+    assert lib.sfx_sparse_down_ws(1, 3, big, 16384) > A.SFX_DOWN_SCRATCH_BYTES
+    assert call(B=3, d=big) == E_SCRATCH
+    assert A.status_str(E_SCRATCH).startswith("needs more scratch")
+    # every fp16 / bf16 shape up to d = 8192 and 64 tokens fits the scratch
+    for wdt in (1, 2):
+        for B in (1, 2, 3, 8, 16, 32, 64):
+            for d in (4096, 7168, 8192):
+                assert lib.sfx_sparse_down_ws(wdt, B, d, 32768) <= A.SFX_DOWN_SCRATCH_BYTES, (wdt, B, d)
