@@ -22,7 +22,8 @@ WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
-           "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc")
+           "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
+           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline")
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
 
@@ -34,7 +35,7 @@ class SfxLayer(ctypes.Structure):
                 ("Wd_scales", ctypes.c_void_p), ("threshold", ctypes.c_float), ("reserved", ctypes.c_int32),
                 ("scores", ctypes.c_void_p), ("tok_bits", ctypes.c_void_p), ("union_bits", ctypes.c_void_p),
                 ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("hact", ctypes.c_void_p),
-                ("y", ctypes.c_void_p)]
+                ("y", ctypes.c_void_p), ("xp", ctypes.c_void_p)]
 
 
 class SfxError(RuntimeError):
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
     lib.sfx_ffn_step.argtypes = [P, I, I, I, I, I, I, I, P, P, Z]
+    lib.sfx_ffn_pipeline_ws.restype = Z
+    lib.sfx_ffn_pipeline_ws.argtypes = [I, I, I, I, I, I]
+    lib.sfx_ffn_pipeline.restype = I
+    lib.sfx_ffn_pipeline.argtypes = [P, I, I, I, I, I, I, I, P, P, Z]
     _lib = lib
     return lib
 
@@ -266,7 +271,7 @@ def _check_layer(i: int, e: dict, B: int, d: int, h: int, f: int, wdt: int, act:
     for n in need:
         if e.get(n) is None:
             raise ValueError(f"layer {i}: '{n}' is required")
-    shapes = {"x": (B, d), "W1": (h, d), "W2": (f, h), "Wa": (f, d), "Wl": (f, d), "Wd": (f, d)}
+    shapes = {"x": (B, d), "xp": (B, d), "W1": (h, d), "W2": (f, h), "Wa": (f, d), "Wl": (f, d), "Wd": (f, d)}
     for n, shp in shapes.items():
         t = e.get(n)
         if t is None:
@@ -323,3 +328,18 @@ def sfx_ffn_step(wdt: int, act, B: int, d: int, h: int, f: int, descs: torch.Ten
     p = (_ptr(descs), _ptr(ws))
     st = load().sfx_ffn_step(_stream(stream), wdt, a, B, d, h, f, L, p[0], p[1], ws.numel())
     _check(st, "sfx_ffn_step")
+
+
+def sfx_ffn_pipeline_ws(wdt: int, act: int, B: int, d: int, h: int, f: int) -> int:
+    """Workspace bytes of the Live Pipeline step, 0 when the shape is not built for it."""
+    return load().sfx_ffn_pipeline_ws(wdt, act, B, d, h, f)
+
+
+def sfx_ffn_pipeline(wdt: int, act, B: int, d: int, h: int, f: int, descs: torch.Tensor, ws, stream=None):
+    """Every layer's step with layer l+1's predictor (on its input xp) overlapped with
+    layer l's FFN, in one launch."""
+    L = descs.numel() // ctypes.sizeof(SfxLayer)
+    a = ACTS[act] if isinstance(act, str) else int(act)
+    p = (_ptr(descs), _ptr(ws))
+    st = load().sfx_ffn_pipeline(_stream(stream), wdt, a, B, d, h, f, L, p[0], p[1], ws.numel())
+    _check(st, "sfx_ffn_pipeline")

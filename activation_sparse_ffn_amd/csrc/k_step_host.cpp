@@ -14,11 +14,16 @@ hipError_t launch_step_f16(hipStream_t s, const StepParams& p, int act, int P, i
 hipError_t launch_step_bf16(hipStream_t s, const StepParams& p, int act, int P, int DL);
 int step_blocks_per_cu_f16(int act, int B);
 int step_blocks_per_cu_bf16(int act, int B);
+hipError_t launch_pipe_f16(hipStream_t s, const StepParams& p, int act, int P);
+hipError_t launch_pipe_bf16(hipStream_t s, const StepParams& p, int act, int P);
+int pipe_blocks_per_cu_f16(int act, int B);
+int pipe_blocks_per_cu_bf16(int act, int B);
 
 namespace {
 constexpr int kNT = 512, kW2Bytes = 131072, kRedFloats = 1024;
 constexpr int kXBytes = 163840 - kW2Bytes - kRedFloats * 4 - 768;
 constexpr int kMaxWords = 1024;
+constexpr int kPrefBytes = (kMaxWords + 8) * 4, kUwBytes = kMaxWords * 4;
 }  // namespace
 
 StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
@@ -49,6 +54,21 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   g.cw = 8 * n;
   g.ok = true;
   (void)kNT;
+  return g;
+}
+
+// The Live Pipeline kernel: the fused step's shapes, with the scores of the owned
+// rows in half of the reduction scratch (the down sums use the other half) and the
+// hidden staged behind the list area of s_x, which stays live while it is read.
+StepGeom pipe_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
+  StepGeom g = step_geometry(wdt, act, B, d, h, f, P);
+  if (!g.ok) return g;
+  const int W = (f + 31) / 32;
+  const int nw2max = (W + P - 1) / P;
+  const int NB = nb_class(B);
+  const int TB = NB < 4 ? NB : 4;
+  if (32 * nw2max * NB > kRedFloats / 2) g.ok = false;
+  if (kPrefBytes + kUwBytes + 4LL * TB * h > kXBytes) g.ok = false;
   return g;
 }
 
@@ -115,6 +135,29 @@ bool step_resident(int wdt, int act, int B) {
   const int n = wdt == DT_BF16 ? step_blocks_per_cu_bf16(act, B) : step_blocks_per_cu_f16(act, B);
   if (c != nullptr) c->store(n >= 1 ? 1 : 2, std::memory_order_relaxed);
   return n >= 1;
+}
+
+bool pipe_resident(int wdt, int act, int B) {
+  static std::atomic<int> cache[8][2][2][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  const int nb = nb_class(B), ci = nb == 1 ? 0 : nb == 2 ? 1 : 2;
+  const int di = wdt == DT_BF16 ? 1 : 0;
+  std::atomic<int>* c = dev < 8 ? &cache[dev][di][act & 1][ci] : nullptr;
+  if (c != nullptr) {
+    const int v = c->load(std::memory_order_relaxed);
+    if (v != 0) return v == 1;
+  }
+  const int n = wdt == DT_BF16 ? pipe_blocks_per_cu_bf16(act, B) : pipe_blocks_per_cu_f16(act, B);
+  if (c != nullptr) c->store(n >= 1 ? 1 : 2, std::memory_order_relaxed);
+  return n >= 1;
+}
+
+hipError_t launch_pipe(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,
+                       void* ws, const StepGeom& g) {
+  const StepParams p = step_params(B, d, h, f, L, layers, ws, g);
+  if (wdt == DT_F16) return launch_pipe_f16(s, p, act, g.P);
+  return launch_pipe_bf16(s, p, act, g.P);
 }
 
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L, const LayerDesc* layers,

@@ -220,4 +220,31 @@ int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int
   return launch_status(sfx::launch_step((hipStream_t)stream, wdt, act, B, d, h, f, L, layers, ws, g));
 }
 
+// ------------------------------------------------------------------------------ Live Pipeline
+
+size_t sfx_ffn_pipeline_ws(int wdt, int act, int B, int d, int h, int f) {
+  const int P = sfx::device_cu_count();
+  if (P <= 0) return 0;
+  if (!sfx::pipe_geometry(wdt, act, B, d, h, f, P).ok) return 0;
+  if (!sfx::pipe_resident(wdt, act, B)) return 0;
+  return sfx::step_ws_bytes(B, h, f, P);
+}
+
+int sfx_ffn_pipeline(void* stream, int wdt, int act, int B, int d, int h, int f, int L, const sfx_layer* layers,
+                     void* ws, size_t ws_bytes) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1 || L < 1) return SFX_E_SHAPE;
+  if (!layers) return SFX_E_NULL;
+  if (!ws) return SFX_E_WORKSPACE;
+  const int P = sfx::device_cu_count();
+  if (P <= 0) return SFX_E_DEVICE;
+  const sfx::StepGeom g = sfx::pipe_geometry(wdt, act, B, d, h, f, P);
+  if (!g.ok) return SFX_E_UNSUPPORTED;
+  if (!sfx::pipe_resident(wdt, act, B)) return SFX_E_UNSUPPORTED;
+  const int w = check_ws(ws, ws_bytes, sfx::step_ws_bytes(B, h, f, P));
+  if (w != SFX_OK) return w;
+  return launch_status(sfx::launch_pipe((hipStream_t)stream, wdt, act, B, d, h, f, L, layers, ws, g));
+}
+
 }  // extern "C"

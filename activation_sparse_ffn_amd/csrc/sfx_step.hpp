@@ -37,6 +37,10 @@ constexpr int kFlagStride = SFX_FLAG_STRIDE;   // words between two workgroups' 
 size_t step_ws_bytes(int B, int h, int f, int P);
 StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layers, void* ws, const StepGeom& g);
 bool step_resident(int wdt, int act, int B);
+StepGeom pipe_geometry(int wdt, int act, int B, int d, int h, int f, int P);
+bool pipe_resident(int wdt, int act, int B);
+hipError_t launch_pipe(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L,
+                       const LayerDesc* layers, void* ws, const StepGeom& g);
 hipError_t launch_step(hipStream_t s, int wdt, int act, int B, int d, int h, int f, int L,
                        const LayerDesc* layers, void* ws, const StepGeom& g);
 

@@ -81,14 +81,17 @@ class TamState:
 
 
 class StackStep:
-    """All layers of a stack run by the fused multi-layer kernel (one launch per
-    step).  Each layer keeps its own output buffers.  `descriptors(inputs)` builds
-    the device descriptor array for a list of per-layer token tensors [B][d]; a
+    """All layers of a stack run by one fused multi-layer kernel per step: the exact
+    step (sfx_ffn_step) or, with `pipeline=True`, the Live Pipeline step
+    (sfx_ffn_pipeline: each layer's predictor scores its own predictor input).
+    Each layer keeps its own output buffers.  `descriptors(inputs, pred_inputs)`
+    builds the device descriptor array for lists of per-layer tensors [B][d]; a
     step is `run(descs)`."""
 
     def __init__(self, layers, d: int, f: int, h: int, B: int, wdtype: str, act: str, device="cuda",
-                 union_bits: torch.Tensor = None):
+                 union_bits: torch.Tensor = None, pipeline: bool = False):
         self.d, self.f, self.h, self.B, self.act = d, f, h, B, act
+        self.pipeline = pipeline
         self.wdt = WDT_CODE[wdtype]
         L = len(layers)
         W = (f + 31) // 32
@@ -108,30 +111,37 @@ class StackStep:
                               "y": torch.empty(B, d, dtype=torch.float32, device=dev)})
             self.weights.append({"W1": g("W1"), "W2": g("W2"), "Wa": g("Wa"), "ba": g("ba"), "Wl": g("Wl"),
                                  "Wd": g("Wd"), "threshold": float(g("threshold"))})
-        n = A.sfx_ffn_step_ws(self.wdt, A.ACTS[act], B, d, h, f)
+        wsq = A.sfx_ffn_pipeline_ws if pipeline else A.sfx_ffn_step_ws
+        n = wsq(self.wdt, A.ACTS[act], B, d, h, f)
         if n == 0:
-            raise A.SfxError(-7, "sfx_ffn_step_ws")
+            raise A.SfxError(-7, wsq.__name__)
         self.ws = A.workspace(n, dev)
 
     @staticmethod
-    def supported(d: int, f: int, h: int, B: int, wdtype: str, act: str) -> bool:
+    def supported(d: int, f: int, h: int, B: int, wdtype: str, act: str, pipeline: bool = False) -> bool:
         if wdtype not in ("f16", "bf16"):
             return False
-        return A.sfx_ffn_step_ws(WDT_CODE[wdtype], A.ACTS[act], B, d, h, f) > 0
+        wsq = A.sfx_ffn_pipeline_ws if pipeline else A.sfx_ffn_step_ws
+        return wsq(WDT_CODE[wdtype], A.ACTS[act], B, d, h, f) > 0
 
-    def descriptors(self, inputs, tok_bits: bool = True) -> torch.Tensor:
+    def descriptors(self, inputs, pred_inputs=None, tok_bits: bool = True) -> torch.Tensor:
+        """`inputs[l]` is layer l's FFN input; `pred_inputs[l]` its predictor input
+        (Live Pipeline only; None = the FFN input)."""
         entries = []
-        for b, wt, x in zip(self.bufs, self.weights, inputs):
+        pred_inputs = pred_inputs if pred_inputs is not None else [None] * len(inputs)
+        for b, wt, x, xp in zip(self.bufs, self.weights, inputs, pred_inputs):
             e = dict(b)
             if not tok_bits:
                 e["tok_bits"] = None
             e.update(wt)
             e["x"] = x
+            e["xp"] = xp
             entries.append(e)
         return A.layer_descriptors(entries, self.B, self.d, self.h, self.f, self.wdt, self.act, self.device)
 
     def run(self, descs: torch.Tensor, stream=None):
-        A.sfx_ffn_step(self.wdt, self.act, self.B, self.d, self.h, self.f, descs, self.ws, stream=stream)
+        call = A.sfx_ffn_pipeline if self.pipeline else A.sfx_ffn_step
+        call(self.wdt, self.act, self.B, self.d, self.h, self.f, descs, self.ws, stream=stream)
 
     def counts(self) -> torch.Tensor:
         return torch.cat([b["count"] for b in self.bufs])

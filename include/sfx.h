@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SFX_ABI_VERSION 1
+#define SFX_ABI_VERSION 2
 #define SFX_MAX_B 64
 #define SFX_MAX_GROUPS 1024
 #define SFX_DOWN_SCRATCH_BYTES ((size_t)17 << 20)   /* static scratch of sfx_sparse_down_noalloc */
@@ -287,11 +287,36 @@ typedef struct sfx_layer {
   int32_t* count;           /* device scalar */
   float* hact;              /* [>= f][B] */
   float* y;                 /* [B][d] */
+  const void* xp;           /* [B][d] predictor input of sfx_ffn_pipeline (NULL = x);
+                               sfx_ffn_step ignores it */
 } sfx_layer;
 
 size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f);
 int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int L,
                  const sfx_layer* layers, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_ffn_pipeline -- the fused step with the predictor one layer ahead (KAIROX page,
+ * Core method, item 2, Live Pipeline: the predictor of layer i + 1 runs on what is
+ * known when layer i starts, overlapped with layer i's FFN; Key observation 1:
+ * adjacent layers' hidden states have cosine similarity about 0.98).
+ *
+ * For each layer j, with its predictor input xp_j (descriptor field xp; NULL = x_j):
+ *   scores_j = W2_j relu(W1_j xp_j);  idx_j = ascending {i : scores_j[b][i] >= t_j
+ *   for some b};  hact = act(Wa_j[i] x_j + b_i);  y_j = sum_i hact Wd_j[i].
+ * Outputs and layouts are those of sfx_ffn_step.  The kernel computes layer 0's
+ * predictor first and then, while it gathers layer l's rows, layer l + 1's
+ * predictor; a caller pipelining a real model passes xp_{l+1} = x_l (the input of
+ * layer l, available when layer l starts) and, for layer 0, an input it has
+ * before the step starts (e.g. layer 0's input of the previous token).  The data
+ * behind every xp_j and x_j must be in place when the launch starts.
+ * Same shapes, workspace, residency rule and sticky error word (word 0) as
+ * sfx_ffn_step; shapes whose own-row scores or hidden staging do not fit the
+ * kernel's LDS split return SFX_E_UNSUPPORTED (sfx_ffn_pipeline_ws returns 0).
+ * ------------------------------------------------------------------------------- */
+size_t sfx_ffn_pipeline_ws(int wdt, int act, int B, int d, int h, int f);
+int sfx_ffn_pipeline(void* stream, int wdt, int act, int B, int d, int h, int f, int L,
+                     const sfx_layer* layers, void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,12 @@ Functions and the passages they follow:
                 Item 6 (§8): entering / leaving sets are set differences.
   dense_ffn     the dense layer the sparse step reproduces when every neuron with
                 a nonzero activation is in the active set (used only by the pins).
+  ffn_step      the four steps in order; with a separate predictor input xp it is
+                the Live Pipeline step of the KAIROX page (Core method, item 2): the
+                predictor of a layer scores an input known one layer earlier, the
+                FFN rows then run on the layer's own input.
+  mask_recall   share of the active neurons of one mask that another mask also
+                holds (KAIROX page, Prediction cost and quality: predictor recall).
 
 Readings where the pages leave a step open: the predictor has no biases; the
 hidden layer stays in full precision; a NaN score is inactive; the activated
@@ -170,14 +176,17 @@ def true_relu_idx(x, Wa, ba) -> np.ndarray:
     return np.flatnonzero((z > 0.0).any(axis=0)).astype(np.int32)
 
 
-def ffn_step(x, layer: dict, wdtype: str, pdtype: str, act: str, threshold: float):
+def ffn_step(x, layer: dict, wdtype: str, pdtype: str, act: str, threshold: float, xp=None):
     """One layer-step in the pages' order: predict -> gate -> up -> down.
-    `layer` holds storage arrays W1, W2, Wa, ba, Wd (and Wl, *_s scales).
+    `layer` holds storage arrays W1, W2, Wa, ba, Wd (and Wl, *_s scales).  The
+    predictor scores `xp` when given (the Live Pipeline's one-layer-ahead input),
+    else `x`; the up and down rows always use `x`.
     Returns a dict with scores, tok_mask, union, idx, count, hact, y."""
     x64 = decode(x, pdtype)
+    xp64 = x64 if xp is None else decode(xp, pdtype)
     W1 = decode(layer["W1"], pdtype)
     W2 = decode(layer["W2"], pdtype)
-    scores = predict(x64, W1, W2)
+    scores = predict(xp64, W1, W2)
     tok_mask, union, idx, count = gate(scores, threshold)
     Wa_r = rows(layer["Wa"], wdtype, idx, layer.get("Wa_s"))
     Wl_r = rows(layer["Wl"], wdtype, idx, layer.get("Wl_s")) if act == "reglu" else None
@@ -186,6 +195,14 @@ def ffn_step(x, layer: dict, wdtype: str, pdtype: str, act: str, threshold: floa
     y = sparse_down(rows(layer["Wd"], wdtype, idx, layer.get("Wd_s")), hact)
     return {"scores": scores, "tok_mask": tok_mask, "union": union, "idx": idx,
             "count": count, "hact": hact, "y": y}
+
+
+def mask_recall(predicted: np.ndarray, exact: np.ndarray) -> float:
+    """|predicted AND exact| / |exact| over boolean masks (1.0 when exact is empty)."""
+    predicted = np.asarray(predicted, dtype=bool)
+    exact = np.asarray(exact, dtype=bool)
+    n = int(exact.sum())
+    return 1.0 if n == 0 else float((predicted & exact).sum()) / n
 
 
 # ----------------------------------------------------------------------------- TAM

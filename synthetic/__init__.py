@@ -7,5 +7,5 @@ of the step's own arithmetic: no predictor, no gate, no sparse product, no TAM.
 Both the HIP path and the fp64 oracle consume what it produces.
 """
 from .configs import CONFIGS, FFNConfig, scaled  # noqa: F401
-from .gen import (Layer, make_layer, make_tokens, seed_for, storage_numpy,  # noqa: F401
-                  threshold_for, zipf_profile, quantize_q4)
+from .gen import (LAYER_COS, Layer, make_layer, make_layer_chain, make_tokens, seed_for,  # noqa: F401
+                  storage_numpy, threshold_for, zipf_profile, quantize_q4)

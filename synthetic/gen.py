@@ -199,6 +199,28 @@ def make_tokens(cfg: FFNConfig, layer: int, steps: int, B: int, device="cpu", ta
     return x.to(TORCH_DTYPE[cfg.pdtype]).contiguous()
 
 
+LAYER_COS = 0.98
+
+
+def make_layer_chain(cfg: FFNConfig, layers: int, steps: int, B: int, device="cpu", cos: float = LAYER_COS,
+                     tag: str = "chain"):
+    """FFN inputs of consecutive layers within each decode step, for the Live
+    Pipeline: layer 0 follows the configuration's token process (AR(1) over steps),
+    and x_{l+1} = cos x_l + sqrt(1 - cos^2) xi_l with fresh N(0, I) noise, so
+    adjacent layers' inputs have cosine similarity ~cos (KAIROX, Key observations,
+    observation 1: about 0.98) and unit variance.  Returns a list of `layers`
+    tensors [steps][B][d] in the predictor dtype."""
+    x = make_tokens(cfg, 0, steps, B, device=device, tag=f"{tag}/x0").to(torch.float64)
+    out = [x.to(TORCH_DTYPE[cfg.pdtype]).contiguous()]
+    c = math.sqrt(1.0 - cos * cos)
+    for l in range(1, layers):
+        g = _rng(cfg.name, l, f"{tag}/B{B}", device)
+        xi = torch.randn(steps, B, cfg.d, generator=g, dtype=torch.float64, device=device)
+        x = cos * x + c * xi
+        out.append(x.to(TORCH_DTYPE[cfg.pdtype]).contiguous())
+    return out
+
+
 def storage_numpy(t: torch.Tensor) -> np.ndarray:
     """Raw storage of a tensor as a host numpy array (bf16 as its uint16 bit pattern)."""
     t = t.detach().to("cpu").contiguous()

@@ -52,11 +52,13 @@ def rel_err(a, ref):
     return num / den if den > 0 else num
 
 
-def check_step(cfg, Lnp: dict, x_np: np.ndarray, out: dict, t: float, report: dict = None):
-    """Every comparison of one layer-step.  Returns a dict of measured errors."""
+def check_step(cfg, Lnp: dict, x_np: np.ndarray, out: dict, t: float, report: dict = None, xp_np=None):
+    """Every comparison of one layer-step (the predictor scores `xp_np` when given:
+    the Live Pipeline step).  Returns a dict of measured errors."""
     pd, wd = cfg.pdtype, cfg.wdtype
     x64 = O.decode(x_np, pd)
-    s64 = O.predict(x64, O.decode(Lnp["W1"], pd), O.decode(Lnp["W2"], pd))
+    xp64 = x64 if xp_np is None else O.decode(xp_np, pd)
+    s64 = O.predict(xp64, O.decode(Lnp["W1"], pd), O.decode(Lnp["W2"], pd))
     r = {}
 
     # (1) scores against fp64

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert A.abi_version() == 1
+    assert A.abi_version() == 2
     for s in range(-9, 1):
         assert A.status_str(s) and A.status_str(s) != "unknown status"
     assert A.status_str(-99) == "unknown status"

@@ -281,3 +281,33 @@ def test_tam_select_brute_force():
         assert (score[a] > score[b]) or (score[a] == score[b] and a < b)
     assert set(np.flatnonzero(ent)) == chosen - set(np.flatnonzero(prev))
     assert set(np.flatnonzero(left)) == set(np.flatnonzero(prev)) - chosen
+
+
+# ----------------------------------------------------------------------------- Live Pipeline
+
+def test_live_step_roles_of_the_two_inputs():
+    """ffn_step with a separate predictor input: the mask comes from xp, the
+    activations from x.  Identity predictor (h = d = f, W1 = W2 = I) so the scores
+    are relu(xp); identity up rows with zero bias so hact = relu(x); Wd rows are
+    powers of two so y is exact.  Worked by hand: xp = (1, -1, 2, 0.5), t = 0.75
+    -> active {0, 2}; x = (3, 4, -5, 6) -> hact = (3, 0); y = 3 Wd[0] + 0 Wd[2].
+    Swapping the roles of x and xp, or scoring x, changes idx and y."""
+    I = np.eye(4)
+    Wd = np.array([[1, 2, 0, 0], [0, 0, 4, 0], [8, 0, 0, 16], [0, 32, 0, 0]], float)
+    layer = {"W1": I, "W2": I, "Wa": I, "ba": np.zeros(4), "Wd": Wd}
+    xp = np.array([[1.0, -1.0, 2.0, 0.5]])
+    x = np.array([[3.0, 4.0, -5.0, 6.0]])
+    r = O.ffn_step(x, layer, "f32", "f32", "relu", 0.75, xp=xp)
+    assert r["idx"].tolist() == [0, 2] and r["count"] == 2
+    assert r["hact"][:, 0].tolist() == [3.0, 0.0]
+    assert r["y"][0].tolist() == [3.0, 6.0, 0.0, 0.0]
+    r_same = O.ffn_step(x, layer, "f32", "f32", "relu", 0.75)        # scores of x itself
+    assert r_same["idx"].tolist() == [0, 1, 3]
+    assert r_same["y"][0].tolist() == [3.0, 6.0 + 192.0, 16.0, 0.0]
+
+
+def test_mask_recall():
+    exact = np.array([1, 1, 0, 1, 0], bool)
+    assert O.mask_recall(np.array([1, 0, 1, 1, 0], bool), exact) == 2 / 3
+    assert O.mask_recall(exact, exact) == 1.0
+    assert O.mask_recall(np.zeros(5, bool), np.zeros(5, bool)) == 1.0

@@ -126,3 +126,19 @@ def test_planted_groups_coactivate():
     grp_active = m.reshape(m.shape[0], -1, 32).any(axis=2).mean()
     indep = 1 - (1 - m.mean()) ** 32
     assert grp_active < 0.6 * indep
+
+
+def test_layer_chain_cosine_and_variance():
+    """Adjacent layers' inputs have cosine ~0.98 and unit variance; layer 0 keeps
+    the AR(1) lag-1 correlation of the token process."""
+    cfg = S.scaled(S.CONFIGS["C2"], name="chain", d=4096, f=64, h=16)
+    xs = S.make_layer_chain(cfg, 3, 6, 2)
+    assert len(xs) == 3 and tuple(xs[1].shape) == (6, 2, 4096)
+    a, b = xs[0].double(), xs[1].double()
+    cos = (a * b).sum(-1) / (a.norm(dim=-1) * b.norm(dim=-1))
+    assert abs(float(cos.mean()) - S.LAYER_COS) < 0.005
+    assert abs(float(xs[2].double().var()) - 1.0) < 0.03
+    lag = (xs[0][1:].double() * xs[0][:-1].double()).mean()
+    assert abs(float(lag) - 0.9) < 0.03
+    again = S.make_layer_chain(cfg, 3, 6, 2)
+    assert all(torch.equal(u, v) for u, v in zip(xs, again))
