@@ -65,7 +65,7 @@ __device__ __forceinline__ bool tag_ok(unsigned long long v, uint32_t tag) { ret
 // branches were each preceded by a wait for all memory, one round trip per word);
 // then only stale entries are reloaded.  Bounded: on timeout (or when another
 // workgroup already failed) the error word is set and whatever was read is returned.
-template <int N, class Valid, class Addr>
+template <int N, class Valid, class Addr, int SL = 2>
 __device__ __forceinline__ void poll_tagged_if(unsigned long long (&v)[N], Valid valid, Addr addr, uint32_t tag,
                                                uint32_t* err) {
 #pragma unroll
@@ -81,7 +81,7 @@ __device__ __forceinline__ void poll_tagged_if(unsigned long long (&v)[N], Valid
     }
     // back off: many waves re-reading uncached words would otherwise crowd out
     // the loads that do the work
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(SL);
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if (valid(i) && !tag_ok(v[i], tag)) v[i] = ld_agent64(addr(i));

@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--fused", action="store_true",
                    help="time sfx_ffn_step where it supports the shape, also from 3 tokens on (by default the "
                         "separate calls are timed there: on the matrix cores they measured faster)")
+    p.add_argument("--pipeline", action="store_true",
+                   help="time the Live Pipeline step (sfx_ffn_pipeline): each layer's predictor scores the previous "
+                        "layer's input (layer 0: the previous token's), inputs of adjacent layers at cosine 0.98")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the calibration of HBM byte counters")
     return p.parse_args()
@@ -149,18 +152,29 @@ def main():
 
     print(f"[bench] generating {L} layers of {cfg.workload}", file=sys.stderr, flush=True)
     layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
-    xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
+    if args.pipeline:
+        xs = S.make_layer_chain(cfg, L, W + K, B, device=dev)
+    else:
+        xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
+
+    def pred_inputs(s):
+        return [xs[0][max(s - 1, 0)]] + [xs[l - 1][s] for l in range(1, L)]
     ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
     tam = TamState(L, G, tam_k, device=dev)
     tensors = [ly.tensors() for ly in layers]
     # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
     # separate calls run on the matrix cores and measured faster (--fused forces it)
-    fused = (not args.separate) and (args.fused or B <= 2) and \
-        StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+    fused = (not args.separate) and (args.fused or args.pipeline or B <= 2) and \
+        StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, pipeline=args.pipeline)
+    if args.pipeline and not fused:
+        print("bench.py: the Live Pipeline kernel does not take this shape", file=sys.stderr)
+        sys.exit(2)
 
     if fused:
-        st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ubits)
-        descs = [st.descriptors([xs[l][s] for l in range(L)], tok_bits=False) for s in range(W + K)]
+        st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ubits,
+                       pipeline=args.pipeline)
+        descs = [st.descriptors([xs[l][s] for l in range(L)], pred_inputs(s) if args.pipeline else None,
+                                tok_bits=False) for s in range(W + K)]
 
         def step(s):
             st.run(descs[s])
@@ -243,7 +257,8 @@ def main():
         dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
         per_launch = [sum(sum(kernel_bytes(cfg, B, int(k)).values()) for k in counts[i]) for i in range(R)]
         dom_bytes = float(np.mean(per_launch))
-        dom_name = "sfx_ffn_step (k_step, all layers of one decode step)"
+        dom_name = ("sfx_ffn_pipeline (k_pipe" if args.pipeline else "sfx_ffn_step (k_step") + \
+            ", all layers of one decode step)"
     else:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
         torch.cuda._sleep(int(2e8))
@@ -282,10 +297,10 @@ def main():
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "mean_active": round(float(counts.mean()), 1),
         "bytes_per_layer_step": round(step_bytes / L, 0),
-        "path": "fused" if fused else "separate",
+        "path": ("pipeline" if args.pipeline else "fused") if fused else "separate",
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic(cfg, B, L) if fused else None,
+                     "traffic": measured_traffic(cfg, B, L) if fused and not args.pipeline else None,
                      "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
                      "bytes_per_launch": round(dom_bytes), "launches": int(dur_ms.size)},
     }

@@ -111,7 +111,9 @@ def test_pipeline_threshold_extremes():
 def test_pipeline_without_xp_matches_exact_step_masks():
     """With no predictor inputs (xp = x) the pipeline scores exactly what the exact
     step scores: scores, masks and lists bit for bit (the same sums in the same
-    order); y agrees within the parity bar (its sums are grouped differently)."""
+    order); activations and y agree to fp32 rounding (their sums are grouped
+    differently: each up row is split over four waves, the down rows over row
+    slices and column bands)."""
     cfg = SMALL["C3s"]
     L, B = 3, 2
     layers = [S.make_layer(cfg, l, device=DEV) for l in range(L)]
@@ -124,9 +126,10 @@ def test_pipeline_without_xp_matches_exact_step_masks():
     torch.cuda.synchronize()
     for l in range(L):
         a, b = _outputs(ex, l), _outputs(pp, l)
-        for key in ("scores", "tok_bits", "union_bits", "idx", "hact"):
+        for key in ("scores", "tok_bits", "union_bits", "idx"):
             assert np.array_equal(a[key], b[key]), (l, key)
-        assert np.max(np.abs(a["y"] - b["y"])) <= 1e-5 * np.max(np.abs(a["y"]))
+        for key in ("hact", "y"):
+            assert np.max(np.abs(a[key] - b[key])) <= 1e-5 * np.max(np.abs(a[key])), (l, key)
 
 
 def test_pipeline_determinism_and_graph_replay():
