@@ -23,7 +23,7 @@ WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
            "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
-           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline")
+           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read")
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
 
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
     lib.sfx_ffn_step.argtypes = [P, I, I, I, I, I, I, I, P, P, Z]
+    lib.sfx_stream_read.restype = I
+    lib.sfx_stream_read.argtypes = [P, P, Z, P]
     lib.sfx_ffn_pipeline_ws.restype = Z
     lib.sfx_ffn_pipeline_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_pipeline.restype = I
@@ -343,3 +345,14 @@ def sfx_ffn_pipeline(wdt: int, act, B: int, d: int, h: int, f: int, descs: torch
     p = (_ptr(descs), _ptr(ws))
     st = load().sfx_ffn_pipeline(_stream(stream), wdt, a, B, d, h, f, L, p[0], p[1], ws.numel())
     _check(st, "sfx_ffn_pipeline")
+
+
+STREAM_READ_OUT_WORDS = 16384
+
+
+def sfx_stream_read(buf: torch.Tensor, out: torch.Tensor, stream=None):
+    """Measurement helper: read `buf` once (the streaming-read ceiling)."""
+    if out.numel() < STREAM_READ_OUT_WORDS or out.element_size() != 4:
+        raise ValueError("out must hold 16384 32-bit words")
+    st = load().sfx_stream_read(_stream(stream), _ptr(buf), buf.numel() * buf.element_size(), _ptr(out))
+    _check(st, "sfx_stream_read")

@@ -136,6 +136,10 @@ constexpr int kMaxP = 256;
 #define SFX_POLL_SLEEP 2
 #endif
 constexpr int kPollSleep = SFX_POLL_SLEEP;   // pause between flag polls, in units of 64 clocks
+#ifndef SFX_STEP_POLL_SLEEP
+#define SFX_STEP_POLL_SLEEP 2
+#endif
+constexpr int kStepPS = SFX_STEP_POLL_SLEEP;  // pause between polls of tagged words, x 64 clocks
 #ifndef SFX_TLB_WARM
 #define SFX_TLB_WARM 1
 #endif
@@ -428,7 +432,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           // block entry s NB + b holds row o + P s, token b
           unsigned long long hw[4 * NB];
           auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
-          poll_tagged_if<4 * NB>(hw, valid, [&](int i) { return p.hid + (size_t)o * kHidBlock + i; }, tag, p.err);
+          auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
+          poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kStepPS>(hw, valid, addr, tag, p.err);
 #pragma unroll
           for (int i = 0; i < 4 * NB; ++i)
             if (valid(i)) s_hid[(i % NB) * h + o + P * (i / NB)] = __uint_as_float((uint32_t)hw[i]);
@@ -605,7 +610,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       for (int m0 = 0; m0 < nw; m0 += 8) {
         unsigned long long uv[8];
         const int n = min(8, nw - m0);
-        poll_tagged<8>(uv, n, [&](int i) { return p.uni + (size_t)o * p.us + m0 + i; }, tag, p.err);
+        auto valid = [&](int i) { return i < n; };
+        auto addr = [&](int i) { return p.uni + (size_t)o * p.us + m0 + i; };
+        poll_tagged_if<8, decltype(valid), decltype(addr), kStepPS>(uv, valid, addr, tag, p.err);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (i < n) s_uw[o + P * (m0 + i)] = (uint32_t)uv[i];
@@ -725,9 +732,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           unsigned long long hv[kRD * NB];
           const int nrow = min(kRD, (k - rb + d_rs - 1) / d_rs);
           // entry u NB + b: activation of rank rb + u d_rs, token b
-          poll_tagged_if<kRD * NB>(
-              hv, [&](int i) { return i / NB < nrow && i % NB < B; },
-              [&](int i) { return p.hact + (size_t)nid[i / NB] * B + min(i % NB, B - 1); }, tag, p.err);
+          auto valid = [&](int i) { return i / NB < nrow && i % NB < B; };
+          auto addr = [&](int i) { return p.hact + (size_t)nid[i / NB] * B + min(i % NB, B - 1); };
+          poll_tagged_if<kRD * NB, decltype(valid), decltype(addr), kStepPS>(hv, valid, addr, tag, p.err);
           // the list and the activations in rank order (outputs): rank r is
           // written by the workgroup whose column tile is r mod the tile count
           if (d_j == 0) {

@@ -247,4 +247,13 @@ int sfx_ffn_pipeline(void* stream, int wdt, int act, int B, int d, int h, int f,
   return launch_status(sfx::launch_pipe((hipStream_t)stream, wdt, act, B, d, h, f, L, layers, ws, g));
 }
 
+// ------------------------------------------------------------------------------ measurement helper
+
+int sfx_stream_read(void* stream, const void* buf, size_t nbytes, uint32_t* out) {
+  if (nbytes < 16 || nbytes % 16 != 0) return SFX_E_SHAPE;
+  if (!buf || !out) return SFX_E_NULL;
+  if (!aligned16(buf) || !aligned4(out)) return SFX_E_ALIGN;
+  return launch_status(sfx::launch_stream_read((hipStream_t)stream, buf, nbytes, out));
+}
+
 }  // extern "C"

@@ -36,6 +36,9 @@ bool down_supported(int wdt, int B);
 constexpr size_t kDownScratchBytes = SFX_DOWN_SCRATCH_BYTES;
 hipError_t down_scratch(void** ptr);
 
+size_t stream_read_out_words();
+hipError_t launch_stream_read(hipStream_t s, const void* buf, size_t nbytes, uint32_t* out);
+
 size_t tam_ws_bytes(int G, int K);
 hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, float lambda,
                       float eps, int K, float* score, uint32_t* hot_bits, uint32_t* entered,

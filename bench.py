@@ -9,19 +9,25 @@ default workload is the OPT-6.7B-shaped ReLU stack (d=4096, f=16384, h=1024, fp1
 
 Prints one JSON line.  `value` = tokens/s per FFN layer = B * layers / step time,
 with every input resident in HBM when the timed region starts; the timed region
-is one replay of a HIP graph holding exactly K steps.
+is one replay of a HIP graph holding exactly K steps.  By default the line also
+carries: the LLaMA2-7B ReGLU stack at batch 1 (the 7B-shaped gate workload), the
+Live Pipeline step on both stacks with its mask recall, the streaming-read ceiling,
+and the fp64 oracle's CPU time (1 thread and all threads) on a sample of the
+timed steps together with the parity maxima of that sample.
 """
 import argparse
 import json
-import math
 import os
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sparse-FFN tokens/s per layer + effective HBM GB/s (% of peak) at batch 1"
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -34,8 +40,10 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="0 = the workload's layer count")
     p.add_argument("--roofline-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="only the selected workload (no second stack, Live Pipeline or streaming probe)")
     p.add_argument("--cpu-layers", type=int, default=4)
-    p.add_argument("--cpu-steps", type=int, default=64)
+    p.add_argument("--cpu-steps", type=int, default=24)
     p.add_argument("--tam-lambda", type=float, default=0.9)
     p.add_argument("--tam-eps", type=float, default=0.01)
     p.add_argument("--separate", action="store_true", help="time the five separate calls per layer")
@@ -43,11 +51,18 @@ def parse():
                    help="time sfx_ffn_step where it supports the shape, also from 3 tokens on (by default the "
                         "separate calls are timed there: on the matrix cores they measured faster)")
     p.add_argument("--pipeline", action="store_true",
-                   help="time the Live Pipeline step (sfx_ffn_pipeline): each layer's predictor scores the previous "
-                        "layer's input (layer 0: the previous token's), inputs of adjacent layers at cosine 0.98")
+                   help="time the Live Pipeline step (sfx_ffn_pipeline) as the headline: each layer's predictor "
+                        "scores the previous layer's input (layer 0: the previous token's), inputs of adjacent "
+                        "layers at cosine 0.98")
+    p.add_argument("--stream-probe", type=int, default=0, metavar="MIB",
+                   help="only run the streaming-read probe over MIB MiB (5 reads) and print its bandwidth")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the calibration of HBM byte counters")
     return p.parse_args()
+
+
+def say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def e_bytes(dt):
@@ -75,8 +90,7 @@ def kernel_bytes(cfg, B, k):
 
 
 STEP_SOURCES = ["k_step.hpp", "k_step_host.cpp", "sfx_step.hpp", "sfx_common.hpp", "k_step_f16.hip", "k_step_bf16.hip"]
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "k_step_traffic_opt6.7b_fp16_b1.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_step_traffic_opt6.7b_fp16_b1.txt")
 
 
 def measured_traffic(cfg, B, L):
@@ -90,7 +104,7 @@ def measured_traffic(cfg, B, L):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "activation_sparse_ffn_amd", "csrc")
+    csrc = os.path.join(ROOT, "activation_sparse_ffn_amd", "csrc")
     h = hashlib.sha256()
     for f in STEP_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
@@ -99,24 +113,296 @@ def measured_traffic(cfg, B, L):
     return int(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, layers_np, xs_np, B, steps):
-    """The fp64 oracle, unchanged, on a bounded sample of the same workload."""
-    from oracle import sfx_oracle as O
+def popcount32(t):
+    """Set bits per element of an int32 tensor (torch has no popcount)."""
+    import torch
+    u = t.to(torch.int64) & 0xFFFFFFFF
+    sh = torch.arange(32, device=t.device, dtype=torch.int64)
+    return ((u.unsqueeze(-1) >> sh) & 1).sum(-1)
+
+
+class Workload:
+    """One stack of synthetic layers and the step that is timed on it."""
+
+    def __init__(self, args, cfg, B, L, mode, dev):
+        import torch
+        import synthetic as S
+        from activation_sparse_ffn_amd import StackStep, StepBuffers, TamState, run_layer
+        self.cfg, self.B, self.L, self.mode = cfg, B, L, mode
+        W, K = args.warmup, args.steps
+        self.W, self.K = W, K
+        G = (cfg.f + 31) // 32
+        self.G = G
+        self.tam_k = max(1, G // 4) if cfg.tam is None else cfg.tam["K"]
+        self.tam_args = (args.tam_lambda, args.tam_eps)
+        say(f"generating {L} layers of {cfg.workload} ({mode}, batch {B})")
+        self.layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
+        if mode == "pipeline":
+            self.xs = S.make_layer_chain(cfg, L, W + K, B, device=dev)
+        else:
+            self.xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
+        self.ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
+        self.tam = TamState(L, G, self.tam_k, device=dev)
+        self.tensors = [ly.tensors() for ly in self.layers]
+        if mode in ("fused", "pipeline"):
+            self.st = StackStep(self.layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev,
+                                union_bits=self.ubits, pipeline=(mode == "pipeline"))
+            self.descs = [self.st.descriptors([self.xs[l][s] for l in range(L)],
+                                              self.pred_inputs(s) if mode == "pipeline" else None,
+                                              tok_bits=False) for s in range(W + K)]
+        else:
+            self.buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
+            self.run_layer = run_layer
+
+    def pred_inputs(self, s):
+        """Live Pipeline predictor inputs of step s: layer l > 0 scores the input of
+        layer l - 1, layer 0 the layer-0 input of the previous step."""
+        return [self.xs[0][max(s - 1, 0)]] + [self.xs[l - 1][s] for l in range(1, self.L)]
+
+    def launch(self, s):
+        """Everything but the TAM update for step s (the dominant kernel's launch on
+        the fused paths)."""
+        if self.mode in ("fused", "pipeline"):
+            self.st.run(self.descs[s])
+        else:
+            for l in range(self.L):
+                self.buf.union_bits = self.ubits[l]
+                self.run_layer(self.buf, self.tensors[l], self.xs[l][s], self.layers[l].threshold, self.cfg.act,
+                               tok_bits=False)
+
+    def step(self, s):
+        self.launch(s)
+        self.tam.update(self.ubits, *self.tam_args)
+
+    def counts_of(self, s):
+        import torch
+        if self.mode in ("fused", "pipeline"):
+            self.st.run(self.descs[s])
+            return self.st.counts().cpu().numpy()
+        cs = []
+        for l in range(self.L):
+            self.buf.union_bits = self.ubits[l]
+            self.run_layer(self.buf, self.tensors[l], self.xs[l][s], self.layers[l].threshold, self.cfg.act,
+                           tok_bits=False)
+            cs.append(self.buf.count.clone())
+        return torch.cat(cs).cpu().numpy()
+
+    def check_status(self):
+        if self.mode in ("fused", "pipeline"):
+            self.st.check_status()
+        else:
+            self.buf.check_status()
+
+
+def time_workload(wl, roofline_steps):
+    """Graph-captured timing of K steps, algorithmic bytes from the measured counts,
+    and per-launch HIP-event durations of the dominant kernel."""
+    import torch
+    from activation_sparse_ffn_amd import _abi as A
+    cfg, B, L, W, K = wl.cfg, wl.B, wl.L, wl.W, wl.K
+    wl.step(0)
+    torch.cuda.synchronize()
+    say(f"{wl.mode} path; capturing graphs")
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for s in range(W):
+            wl.step(s)
+    with torch.cuda.graph(g_timed):
+        for s in range(W, W + K):
+            wl.step(s)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    g_timed.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / K
+    say(f"timed {K} steps: {ms_total:.3f} ms")
+    wl.check_status()                 # sticky status words of every workspace the timed steps used
+
+    counts = np.zeros((K, L), dtype=np.int64)
+    for i, s in enumerate(range(W, W + K)):
+        counts[i] = wl.counts_of(s)
+    kb = [kernel_bytes(cfg, B, int(k)) for k in counts.reshape(-1)]
+    tam_bytes = L * wl.G * 16
+    step_bytes = sum(sum(v.values()) for v in kb) / K + tam_bytes
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # Dominant kernel: per-launch durations from HIP events bracketing each launch on
+    # the launch stream; every launch is queued behind a spin kernel so the events
+    # time the GPU, not the host.  Fused paths: the whole-stack kernel (all layers'
+    # bytes per launch).  Separate path: sfx_predict (the largest byte share).
+    R = min(roofline_steps, K)
+    torch.cuda.synchronize()
+    if wl.mode in ("fused", "pipeline"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+        torch.cuda._sleep(int(2e8))
+        for i, s in enumerate(range(W, W + R)):
+            evs[i][0].record()
+            wl.st.run(wl.descs[s])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        per_launch = [sum(sum(kernel_bytes(cfg, B, int(k)).values()) for k in counts[i]) for i in range(R)]
+        dom_bytes = float(np.mean(per_launch))
+        dom_name = ("sfx_ffn_pipeline (k_pipe" if wl.mode == "pipeline" else "sfx_ffn_step (k_step") + \
+            ", all layers of one decode step)"
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
+        torch.cuda._sleep(int(2e8))
+        i = 0
+        for s in range(W, W + R):
+            for l in range(L):
+                t = wl.tensors[l]
+                evs[i][0].record()
+                A.sfx_predict(wl.xs[l][s], t["W1"], t["W2"], wl.buf.scores, wl.buf.ws_pred)
+                evs[i][1].record()
+                i += 1
+        torch.cuda.synchronize()
+        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        dom_bytes = float(kernel_bytes(cfg, B, 0)["predict"])
+        dom_name = "sfx_predict (k_pred_hidden + k_pred_scores)"
+    dom_gbps = dom_bytes / (dur_ms.mean() * 1e-3) / 1e9
+    return {
+        "ms_step": ms_step, "counts": counts, "step_bytes": step_bytes, "gbps": gbps,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(cfg, B, L) if wl.mode == "fused" else None,
+                     "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3), "bytes_per_launch": round(dom_bytes),
+                     "launches": int(dur_ms.size)},
+    }
+
+
+def summary(wl, r):
+    return {"workload": wl.cfg.workload, "batch": wl.B, "layers": wl.L, "path": wl.mode,
+            "us_per_layer_step": round(r["ms_step"] * 1e3 / wl.L, 3),
+            "tokens_per_s_per_layer": round(wl.B * wl.L / (r["ms_step"] * 1e-3), 1),
+            "effective_GBps": round(r["gbps"], 1), "hbm_frac": round(r["gbps"] / PEAK_HBM_GBPS, 4),
+            "mean_active": round(float(r["counts"].mean()), 1), "roofline_frac": r["roofline"]["frac"]}
+
+
+def mask_recall(wl_pipe, dev, steps):
+    """Recall and precision of the Live Pipeline's union masks (predictor on the
+    previous layer's input) against the masks of the exact step (predictor on the
+    layer's own input), over every layer of `steps` timed steps."""
+    import torch
+    from activation_sparse_ffn_amd import StackStep
+    cfg, L, B = wl_pipe.cfg, wl_pipe.L, wl_pipe.B
+    ex_bits = torch.zeros(L, wl_pipe.G, dtype=torch.int32, device=dev)
+    ex = StackStep(wl_pipe.layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ex_bits)
+    hit = exact = pred = 0
+    for s in steps:
+        wl_pipe.st.run(wl_pipe.descs[s])
+        ex.run(ex.descriptors([wl_pipe.xs[l][s] for l in range(L)], tok_bits=False))
+        torch.cuda.synchronize()
+        hit += int(popcount32(wl_pipe.ubits & ex_bits).sum())
+        exact += int(popcount32(ex_bits).sum())
+        pred += int(popcount32(wl_pipe.ubits).sum())
+    ex.check_status()
+    return {"recall": round(hit / max(exact, 1), 4), "precision": round(hit / max(pred, 1), 4),
+            "predicted_active": pred, "exact_active": exact, "layer_steps": L * len(steps)}
+
+
+def stream_probe(dev, mib=2048, reps=5):
+    """Bandwidth of the streaming-read helper (sfx_stream_read) over `mib` MiB,
+    rotating over two buffers so reads come from HBM, not the 256 MB cache."""
+    import torch
+    from activation_sparse_ffn_amd import _abi as A
+    n = mib << 20
+    bufs = [torch.ones(n // 2, dtype=torch.float16, device=dev) for _ in range(2)]
+    out = torch.zeros(A.STREAM_READ_OUT_WORDS, dtype=torch.int32, device=dev)
+    A.sfx_stream_read(bufs[0], out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(reps):
+        A.sfx_stream_read(bufs[i % 2], out)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / reps
+    return {"kernel": "sfx_stream_read (k_stream_read)", "bytes": n, "us": round(us, 2),
+            "GBps": round(n / (us * 1e-6) / 1e9, 1)}
+
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    n = 0
-    t0 = time.perf_counter()
-    for li, Lnp in enumerate(layers_np):
-        for s in range(steps):
-            O.ffn_step(xs_np[li][s], Lnp, cfg.wdtype, cfg.pdtype, cfg.act, Lnp["threshold"])
-            n += 1
-    dt = time.perf_counter() - t0
-    return {"value": B * n / dt, "unit": "tokens/s/layer", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(layers_np)} layers x {steps} decode steps of the benchmark workload "
-                      f"(batch {B}), fp64 numpy oracle, {dt:.1f} s"}
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_and_parity(wl, nl, ns):
+    """The fp64 oracle, unchanged, on a bounded sample of the timed workload (nl
+    layers x ns timed steps), in a child process with 1 thread and with every host
+    core, thread counts set in its environment before numpy is imported.  The same
+    run recomputes the sample's parity maxima against the GPU's outputs for those
+    steps (an eager re-run of the timed steps, outside the timed region)."""
+    import torch
+    import synthetic.gen as SG
+    cfg, L = wl.cfg, wl.L
+    lsel = sorted(set(int(round(i * (L - 1) / max(nl - 1, 1))) for i in range(nl)))
+    arrays = {"wdtype": np.array(cfg.wdtype), "pdtype": np.array(cfg.pdtype), "act": np.array(cfg.act)}
+    for j in lsel:
+        for k, v in wl.tensors[j].items():
+            if k != "perm":
+                arrays[f"L{j}/{k}"] = SG.storage_numpy(v)
+    layer_of, thr = [], []
+    i = 0
+    for s in range(wl.W, wl.W + ns):
+        wl.launch(s)
+        torch.cuda.synchronize()
+        for j in lsel:
+            b = wl.st.bufs[j] if wl.mode in ("fused", "pipeline") else None
+            if b is None:
+                raise RuntimeError("the oracle sample needs a fused path")
+            kk = int(b["count"].item())
+            arrays[f"x{i}"] = SG.storage_numpy(wl.xs[j][s])
+            if wl.mode == "pipeline":
+                arrays[f"xp{i}"] = SG.storage_numpy(wl.pred_inputs(s)[j])
+            arrays[f"scores{i}"] = b["scores"].cpu().numpy()
+            arrays[f"idx{i}"] = b["idx"][:kk].cpu().numpy()
+            arrays[f"hact{i}"] = b["hact"][:kk].cpu().numpy()
+            arrays[f"y{i}"] = b["y"].cpu().numpy()
+            layer_of.append(j)
+            thr.append(wl.layers[j].threshold)
+            i += 1
+    arrays["layer_of"] = np.array(layer_of)
+    arrays["threshold"] = np.array(thr, dtype=np.float64)
+    ncores = len(os.sched_getaffinity(0))
+    runs = {}
+    with tempfile.TemporaryDirectory() as td:
+        src = os.path.join(td, "in.npz")
+        np.savez(src, **arrays)
+        for threads in (1, ncores):
+            env = dict(os.environ)
+            for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+                env[var] = str(threads)
+            say(f"oracle on {len(layer_of)} layer-steps, {threads} thread(s)")
+            out = subprocess.run([sys.executable, os.path.join(ROOT, "oracle", "time_oracle.py"), src,
+                                  os.path.join(td, "out.npz")], env=env, capture_output=True, text=True,
+                                 timeout=900)
+            if out.returncode != 0:
+                raise RuntimeError(f"oracle timing failed:\n{out.stderr[-2000:]}")
+            runs[threads] = json.loads(out.stdout.strip().splitlines()[-1])
+    n = len(layer_of)
+    rN, r1 = runs[ncores], runs[1]
+    sample = (f"{len(lsel)} layers ({', '.join(map(str, lsel))}) x {ns} timed decode steps of the benchmark "
+              f"workload (batch {wl.B}), fp64 numpy oracle unchanged: {rN['seconds']:.1f} s on {ncores} threads, "
+              f"{r1['seconds']:.1f} s on 1 thread")
+    base = {"value": round(wl.B * n / rN["seconds"], 3), "unit": "tokens/s/layer", "cores": ncores,
+            "kind": "oracle", "sample": sample, "single_thread_value": round(wl.B * n / r1["seconds"], 3),
+            "cpu_model": cpu_model()}
+    par = {k: rN[k] for k in ("score_err", "near_threshold", "mask_mismatch", "hact_rel", "y_rel", "y_rel_own_list")}
+    par.update({"layer_steps": n, "bar": {"score_err": 1e-5, "y_rel": 1e-3 if cfg.wdtype != "q4" else 2e-3,
+                                          "mask_mismatch": 0}})
+    return base, par
 
 
 def main():
@@ -137,152 +423,41 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
         return
     import synthetic as S
-    from activation_sparse_ffn_amd import StackStep, StepBuffers, TamState, run_layer
+    from activation_sparse_ffn_amd import StackStep
     from activation_sparse_ffn_amd import _abi as A
 
     A.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.stream_probe:
+        print(json.dumps(stream_probe(dev, args.stream_probe)), flush=True)
+        return
+
+    def mode_for(cfg, B, pipeline):
+        if pipeline:
+            if not StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, pipeline=True):
+                print("bench.py: the Live Pipeline kernel does not take this shape", file=sys.stderr)
+                sys.exit(2)
+            return "pipeline"
+        # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
+        # separate calls run on the matrix cores and measured faster (--fused forces it)
+        fused = (not args.separate) and (args.fused or B <= 2) and \
+            StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
+        return "fused" if fused else "separate"
+
     cfg = S.CONFIGS[args.config]
     B = args.batch
     L = args.layers or cfg.layers
-    K, W = args.steps, args.warmup
-    G = (cfg.f + 31) // 32
-    tam_k = max(1, G // 4) if cfg.tam is None else cfg.tam["K"]
-
-    print(f"[bench] generating {L} layers of {cfg.workload}", file=sys.stderr, flush=True)
-    layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
-    if args.pipeline:
-        xs = S.make_layer_chain(cfg, L, W + K, B, device=dev)
-    else:
-        xs = [S.make_tokens(cfg, l, W + K, B, device=dev) for l in range(L)]
-
-    def pred_inputs(s):
-        return [xs[0][max(s - 1, 0)]] + [xs[l - 1][s] for l in range(1, L)]
-    ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
-    tam = TamState(L, G, tam_k, device=dev)
-    tensors = [ly.tensors() for ly in layers]
-    # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
-    # separate calls run on the matrix cores and measured faster (--fused forces it)
-    fused = (not args.separate) and (args.fused or args.pipeline or B <= 2) and \
-        StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, pipeline=args.pipeline)
-    if args.pipeline and not fused:
-        print("bench.py: the Live Pipeline kernel does not take this shape", file=sys.stderr)
-        sys.exit(2)
-
-    if fused:
-        st = StackStep(layers, cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act, device=dev, union_bits=ubits,
-                       pipeline=args.pipeline)
-        descs = [st.descriptors([xs[l][s] for l in range(L)], pred_inputs(s) if args.pipeline else None,
-                                tok_bits=False) for s in range(W + K)]
-
-        def step(s):
-            st.run(descs[s])
-            tam.update(ubits, args.tam_lambda, args.tam_eps)
-
-        def counts_of(s):
-            st.run(descs[s])
-            return st.counts().cpu().numpy()
-    else:
-        buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
-
-        def step(s):
-            for l in range(L):
-                buf.union_bits = ubits[l]
-                run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
-            tam.update(ubits, args.tam_lambda, args.tam_eps)
-
-        def counts_of(s):
-            cs = []
-            for l in range(L):
-                buf.union_bits = ubits[l]
-                run_layer(buf, tensors[l], xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
-                cs.append(buf.count.clone())
-            return torch.cat(cs).cpu().numpy()
-
-    # eager pass (loads code objects), then capture the warmup and timed steps
-    step(0)
-    torch.cuda.synchronize()
-    print(f"[bench] {'fused' if fused else 'separate-call'} path; capturing graphs", file=sys.stderr, flush=True)
-    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_warm):
-        for s in range(W):
-            step(s)
-    with torch.cuda.graph(g_timed):
-        for s in range(W, W + K):
-            step(s)
-    torch.cuda.synchronize()
-
-    g_warm.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    g_timed.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / K
-    print(f"[bench] timed {K} steps: {ms_total:.3f} ms", file=sys.stderr, flush=True)
-    # sticky status words of every workspace the timed steps used: a timed-out wait
-    # or an out-of-range hidden value would make the step's outputs undefined
-    if fused:
-        st.check_status()
-    else:
-        buf.check_status()
-
-    # Active counts of the timed steps (deterministic: an eager re-run of the same steps).
-    counts = np.zeros((K, L), dtype=np.int64)
-    for i, s in enumerate(range(W, W + K)):
-        counts[i] = counts_of(s)
-    kb = [kernel_bytes(cfg, B, int(k)) for k in counts.reshape(-1)]
-    tam_bytes = L * G * 16
-    step_bytes = sum(sum(v.values()) for v in kb) / K + tam_bytes
-    gbps = step_bytes / (ms_step * 1e-3) / 1e9
-
-    # Dominant kernel: per-launch durations from HIP events bracketing each launch on
-    # the launch stream; every launch is queued behind a spin kernel so the events
-    # time the GPU, not the host.  Fused path: the whole-stack kernel (all layers'
-    # bytes per launch).  Separate path: sfx_predict (the largest byte share).
-    R = min(args.roofline_steps, K)
-    torch.cuda.synchronize()
-    if fused:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
-        torch.cuda._sleep(int(2e8))
-        for i, s in enumerate(range(W, W + R)):
-            evs[i][0].record()
-            st.run(descs[s])
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
-        per_launch = [sum(sum(kernel_bytes(cfg, B, int(k)).values()) for k in counts[i]) for i in range(R)]
-        dom_bytes = float(np.mean(per_launch))
-        dom_name = ("sfx_ffn_pipeline (k_pipe" if args.pipeline else "sfx_ffn_step (k_step") + \
-            ", all layers of one decode step)"
-    else:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * L)]
-        torch.cuda._sleep(int(2e8))
-        i = 0
-        for s in range(W, W + R):
-            for l in range(L):
-                t = tensors[l]
-                evs[i][0].record()
-                A.sfx_predict(xs[l][s], t["W1"], t["W2"], buf.scores, buf.ws_pred)
-                evs[i][1].record()
-                i += 1
-        torch.cuda.synchronize()
-        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
-        dom_bytes = float(kernel_bytes(cfg, B, 0)["predict"])
-        dom_name = "sfx_predict (k_pred_hidden + k_pred_scores)"
-    dom_gbps = dom_bytes / (dur_ms.mean() * 1e-3) / 1e9
-
+    wl = Workload(args, cfg, B, L, mode_for(cfg, B, args.pipeline), dev)
+    r = time_workload(wl, args.roofline_steps)
+    ms_step = r["ms_step"]
     result = {
         "metric": METRIC,
         "value": round(B * L / (ms_step * 1e-3), 1),
         "unit": "tokens/s/layer",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -290,32 +465,41 @@ def main():
         "dtype": cfg.wdtype,
         "data": "synthetic (seeded, generated on device)",
         "config": {"workload": cfg.workload, "batch": B, "layers": L, "d": cfg.d, "f": cfg.f, "h": cfg.h,
-                   "act": cfg.act, "density": cfg.density, "tam": {"lambda": args.tam_lambda,
-                                                                  "eps": args.tam_eps, "K": tam_k, "G": G}},
+                   "act": cfg.act, "density": cfg.density,
+                   "tam": {"lambda": args.tam_lambda, "eps": args.tam_eps, "K": wl.tam_k, "G": wl.G}},
         "us_per_layer_step": round(ms_step * 1e3 / L, 3),
-        "effective_GBps": round(gbps, 1),
-        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-        "mean_active": round(float(counts.mean()), 1),
-        "bytes_per_layer_step": round(step_bytes / L, 0),
-        "path": ("pipeline" if args.pipeline else "fused") if fused else "separate",
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 1),
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic(cfg, B, L) if fused and not args.pipeline else None,
-                     "avg_launch_us": round(float(dur_ms.mean()) * 1e3, 3),
-                     "bytes_per_launch": round(dom_bytes), "launches": int(dur_ms.size)},
+        "effective_GBps": round(r["gbps"], 1),
+        "hbm_frac": round(r["gbps"] / PEAK_HBM_GBPS, 4),
+        "mean_active": round(float(r["counts"].mean()), 1),
+        "bytes_per_layer_step": round(r["step_bytes"] / L, 0),
+        "path": wl.mode,
+        "roofline": r["roofline"],
     }
+    if not args.no_cpu_baseline and wl.mode in ("fused", "pipeline"):
+        base, par = cpu_baseline_and_parity(wl, min(args.cpu_layers, L), min(args.cpu_steps, args.steps))
+        result["cpu_baseline"] = base
+        result["parity_sample"] = par
+    del wl
+    torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
-        import synthetic.gen as SG
-        nl = min(args.cpu_layers, L)
-        ns = min(args.cpu_steps, K)
-        lnp, xnp = [], []
-        for l in range(nl):
-            d = {k: SG.storage_numpy(v) for k, v in tensors[l].items()}
-            d["threshold"] = layers[l].threshold
-            lnp.append(d)
-            xnp.append([SG.storage_numpy(xs[l][s]) for s in range(W, W + ns)])
-        result["cpu_baseline"] = cpu_baseline(cfg, lnp, xnp, B, ns)
+    if not args.no_extra and args.config == "C2" and B == 1 and not args.pipeline and not args.separate:
+        extra = {}
+        c3 = S.CONFIGS["C3"]
+        w3 = Workload(args, c3, 1, c3.layers, mode_for(c3, 1, False), dev)
+        extra["llama2_7b_reglu_b1"] = summary(w3, time_workload(w3, args.roofline_steps))
+        del w3
+        torch.cuda.empty_cache()
+        pipes = {}
+        for name, c in (("opt6.7b_b1", S.CONFIGS["C2"]), ("llama2_7b_reglu_b1", c3)):
+            wp = Workload(args, c, 1, c.layers, "pipeline", dev)
+            s = summary(wp, time_workload(wp, args.roofline_steps))
+            s["mask_recall"] = mask_recall(wp, dev, range(args.warmup, args.warmup + min(8, args.steps)))
+            pipes[name] = s
+            del wp
+            torch.cuda.empty_cache()
+        extra["live_pipeline"] = pipes
+        extra["stream_read_ceiling"] = stream_probe(dev)
+        result["extra"] = extra
 
     print(json.dumps(result), flush=True)
 

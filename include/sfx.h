@@ -318,6 +318,16 @@ size_t sfx_ffn_pipeline_ws(int wdt, int act, int B, int d, int h, int f);
 int sfx_ffn_pipeline(void* stream, int wdt, int act, int B, int d, int h, int f, int L,
                      const sfx_layer* layers, void* ws, size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------------
+ * sfx_stream_read -- measurement helper, not a step of the method.  Reads the nbytes
+ * of buf once with 16-byte loads (2048 workgroups of 512 threads, 8 loads in flight
+ * per thread) and writes 16384 uint32 checksums to out.  Its bandwidth is the
+ * streaming-read ceiling that the step kernels' achieved HBM bandwidth is compared
+ * with (PowerInfer page, Problem: batch-1 decode is bound by reading the weights).
+ *   nbytes  a multiple of 16, >= 16.   buf 16-byte aligned.   out [16384] uint32.
+ * ------------------------------------------------------------------------------- */
+int sfx_stream_read(void* stream, const void* buf, size_t nbytes, uint32_t* out);
+
 #ifdef __cplusplus
 }
 #endif

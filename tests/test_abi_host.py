@@ -165,3 +165,10 @@ def test_down_noalloc_validation(lib):
         for B in (1, 2, 3, 8, 16, 32, 64):
             for d in (4096, 7168, 8192):
                 assert lib.sfx_sparse_down_ws(wdt, B, d, 32768) <= A.SFX_DOWN_SCRATCH_BYTES, (wdt, B, d)
+
+
+def test_stream_read_validation(lib):
+    assert lib.sfx_stream_read(None, GOOD, 100, GOOD) == E_SHAPE      # not a multiple of 16
+    assert lib.sfx_stream_read(None, GOOD, 0, GOOD) == E_SHAPE
+    assert lib.sfx_stream_read(None, None, 4096, GOOD) == E_NULL
+    assert lib.sfx_stream_read(None, ODD, 4096, GOOD) == E_ALIGN
