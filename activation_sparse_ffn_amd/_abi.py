@@ -14,16 +14,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsfx.so")
 
 SFX_F32, SFX_F16, SFX_BF16, SFX_Q4G32 = 0, 1, 2, 3
-SFX_RELU, SFX_REGLU = 0, 1
+SFX_RELU, SFX_REGLU, SFX_RELU2 = 0, 1, 2
 SFX_MAX_B = 64
 SFX_MAX_GROUPS = 1024
-ACTS = {"relu": SFX_RELU, "reglu": SFX_REGLU}
+ACTS = {"relu": SFX_RELU, "reglu": SFX_REGLU, "relu2": SFX_RELU2}
 WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
            "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
-           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read")
+           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read", "sfx_predict_q4")
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
 
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
     lib.sfx_ffn_step.argtypes = [P, I, I, I, I, I, I, I, P, P, Z]
+    lib.sfx_predict_q4.restype = I
+    lib.sfx_predict_q4.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, Z]
     lib.sfx_stream_read.restype = I
     lib.sfx_stream_read.argtypes = [P, P, Z, P]
     lib.sfx_ffn_pipeline_ws.restype = Z
@@ -177,6 +179,24 @@ def sfx_predict(x, W1, W2, scores, ws, stream=None):
     ptrs = (_ptr(x), _ptr(W1), _ptr(W2), _ptr(scores), _ptr(ws))
     st = load().sfx_predict(_stream(stream), _wdt_of(x), B, d, h, f, *ptrs, ws.numel() if ws is not None else 0)
     _check(st, "sfx_predict")
+
+
+def sfx_predict_q4(x, W1, W1_scales, W2, W2_scales, scores, ws, stream=None):
+    """scores[B][f] = W2 relu(W1 x_b) with int4 W1 [h][d/2] / W2 [f][h/2] codes and
+    fp16 scales; x [B][d] fp16."""
+    B, d = x.shape
+    h, f = W1.shape[0], W2.shape[0]
+    if W1.shape[1] * 2 != d or W2.shape[1] * 2 != h or tuple(scores.shape) != (B, f):
+        raise ValueError("sfx_predict_q4: shape mismatch")
+    _need(x, torch.float16, "x")
+    _need(scores, torch.float32, "scores")
+    for t, n in ((W1, "W1"), (W2, "W2")):
+        _need(t, torch.uint8, n)
+    for t, n in ((W1_scales, "W1_scales"), (W2_scales, "W2_scales")):
+        _need(t, torch.float16, n)
+    p = (_ptr(x), _ptr(W1), _ptr(W1_scales), _ptr(W2), _ptr(W2_scales), _ptr(scores), _ptr(ws))
+    st = load().sfx_predict_q4(_stream(stream), B, d, h, f, *p, ws.numel() if ws is not None else 0)
+    _check(st, "sfx_predict_q4")
 
 
 def sfx_compact(scores, threshold, union_bits, idx, count, ws, tok_bits=None, stream=None):

@@ -1,9 +1,11 @@
 // Gathered up / gate rows of the active neurons (PowerInfer page, Method, neuron-
 // aware operators of §5.4: the operator reads only the rows of neurons marked
-// active; Paper vs code, activation functions: ReLU and ReGLU).
+// active; Paper vs code, activation functions: ReLU, ReGLU and squared ReLU).
 //
 //   hact[j][b] = act(Wa[idx_j] . x_b + ba[idx_j])        ReLU
 //   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0) * (Wl[idx_j] . x_b)   ReGLU
+//   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0)^2                    squared ReLU
+// (squared ReLU runs the ReLU instantiations with a wave-uniform `square` flag)
 //
 // A persistent grid of waves strides over the device-resident count; each wave
 // reads whole rows with coalesced 16-byte loads (a row is contiguous), keeps the
@@ -29,7 +31,8 @@ template <class T, int NB, bool REGLU>
 __global__ __launch_bounds__(kBlock) void k_up(const uint8_t* __restrict__ x, const uint8_t* __restrict__ Wa,
                                                const float* __restrict__ ba, const uint8_t* __restrict__ Wl,
                                                const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-                                               int kmax, int B, int d, int f, float* __restrict__ hact) {
+                                               int kmax, int B, int d, int f, float* __restrict__ hact,
+                                               int square) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * kWavesPerBlock;
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(kBlock) void k_up(const uint8_t* __restrict__ x, co
         if (b < B) {
           float a = ok ? fmaxf(za[b] + bias, 0.f) : 0.f;
           if (REGLU) a *= zl[b];
+          if (square) a *= a;
           hact[(size_t)j * B + b] = a;
         }
       }
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(kBlock) void k_up_q4(const uint8_t* __restrict__ x,
                                                   const uint16_t* __restrict__ Wa_s, const float* __restrict__ ba,
                                                   const uint8_t* __restrict__ Wl, const uint16_t* __restrict__ Wl_s,
                                                   const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-                                                  int kmax, int B, int d, int f, float* __restrict__ hact) {
+                                                  int kmax, int B, int d, int f, float* __restrict__ hact,
+                                                  int square) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * kWavesPerBlock;
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(kBlock) void k_up_q4(const uint8_t* __restrict__ x,
         if (b < B) {
           float a = ok ? fmaxf(za[b] + bias, 0.f) : 0.f;
           if (REGLU) a *= zl[b];
+          if (square) a *= a;
           hact[(size_t)j * B + b] = a;
         }
       }
@@ -246,10 +252,10 @@ hipError_t run(hipStream_t s, int act, int B, int d, int f, const void* x, const
   dim3 g(grid_blocks(kmax)), blk(kBlock);
   if (act == 1)
     k_up<T, NB, true><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, (const uint8_t*)Wl, idx,
-                                         count, kmax, B, d, f, hact);
+                                         count, kmax, B, d, f, hact, 0);
   else
     k_up<T, NB, false><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, nullptr, idx, count,
-                                          kmax, B, d, f, hact);
+                                          kmax, B, d, f, hact, act == 2 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -261,10 +267,10 @@ hipError_t run_q4(hipStream_t s, int act, int B, int d, int f, const void* x, co
   if (act == 1)
     k_up_q4<NB, true><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, (const uint16_t*)Wa_s, ba,
                                          (const uint8_t*)Wl, (const uint16_t*)Wl_s, idx, count, kmax, B, d,
-                                         f, hact);
+                                         f, hact, 0);
   else
     k_up_q4<NB, false><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, (const uint16_t*)Wa_s, ba,
-                                          nullptr, nullptr, idx, count, kmax, B, d, f, hact);
+                                          nullptr, nullptr, idx, count, kmax, B, d, f, hact, act == 2 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
 // Gathered up / gate rows on the matrix cores for B >= 3 tokens (PowerInfer page,
 // Method, neuron-aware operators of §5.4: only the rows of active neurons are read;
-// Paper vs code, activation functions: ReLU and ReGLU).
+// Paper vs code, activation functions: ReLU, ReGLU and squared ReLU).
 //
 //   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0)                 ReLU
 //   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0) * (Wl[idx_j] . x_b)   ReGLU
+//   hact[j][b] = max(Wa[idx_j] . x_b + ba[idx_j], 0)^2                    squared ReLU
 //
 // From 3 tokens on every row byte feeds >= 3 multiply-adds and the per-row input
 // re-reads of the vector kernel dominate (pad tokens of the 16-token tile cost
@@ -34,7 +35,8 @@ __global__ __launch_bounds__(kUW * kWave) void k_up_mfma(const uint8_t* __restri
                                                         const uint8_t* __restrict__ Wl,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ count, int kmax, int B,
-                                                        int d, int f, float* __restrict__ hact) {
+                                                        int d, int f, float* __restrict__ hact,
+                                                        int square) {
   constexpr int NA = REGLU ? 2 : 1;
   constexpr int kUU = NT == 1 ? 8 : 4;          // 32-column steps per wave in flight (8 spills at 64 tokens)
   __shared__ f32x4 s_acc[kUW - 1][NA][MT][NT][kWave];
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kUW * kWave) void k_up_mfma(const uint8_t* __restri
               if (b < B) {
                 float h = ok ? fmaxf(acc[0][m][n][e] + bias, 0.f) : 0.f;
                 if (REGLU) h *= acc[NA - 1][m][n][e];
+                if (square) h *= h;
                 hact[(size_t)j * B + b] = h;
               }
             }
@@ -164,10 +167,10 @@ hipError_t run(hipStream_t s, int act, int B, int d, int f, const void* x, const
   dim3 g(tiles < cap ? (tiles > 0 ? tiles : 1) : cap), blk(kUW * kWave);
   if (act == 1)
     k_up_mfma<T, NT, MT, true><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, (const uint8_t*)Wl,
-                                                  idx, count, kmax, B, d, f, hact);
+                                                  idx, count, kmax, B, d, f, hact, 0);
   else
     k_up_mfma<T, NT, MT, false><<<g, blk, 0, s>>>((const uint8_t*)x, (const uint8_t*)Wa, ba, nullptr, idx,
-                                                   count, kmax, B, d, f, hact);
+                                                   count, kmax, B, d, f, hact, act == 2 ? 1 : 0);
   return hipGetLastError();
 }
 

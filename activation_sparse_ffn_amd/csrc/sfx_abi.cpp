@@ -82,6 +82,7 @@ int sfx_abi_version(void) { return SFX_ABI_VERSION; }
 
 size_t sfx_predict_ws(int wdt, int B, int d, int h, int f) {
   if (B < 1 || B > SFX_MAX_B || h < 1) return 0;
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return 0;
   return sfx::predict_ws_bytes(wdt, B, d, h, f);
 }
 
@@ -96,6 +97,19 @@ int sfx_predict(void* stream, int wdt, int B, int d, int h, int f, const void* x
   if (w != SFX_OK) return w;
   return launch_status(
       sfx::launch_predict((hipStream_t)stream, wdt, B, d, h, f, x, W1, W2, scores, ws));
+}
+
+int sfx_predict_q4(void* stream, int B, int d, int h, int f, const void* x, const void* W1, const void* W1_scales,
+                   const void* W2, const void* W2_scales, float* scores, void* ws, size_t ws_bytes) {
+  if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1) return SFX_E_SHAPE;
+  if (d % 32 != 0 || h % 32 != 0) return SFX_E_SHAPE;
+  if (!x || !W1 || !W1_scales || !W2 || !W2_scales || !scores) return SFX_E_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || !aligned16(scores)) return SFX_E_ALIGN;
+  if (((uintptr_t)W1_scales & 1u) != 0 || ((uintptr_t)W2_scales & 1u) != 0) return SFX_E_ALIGN;
+  const int w = check_ws(ws, ws_bytes, sfx::predict_ws_bytes(SFX_Q4G32, B, d, h, f));
+  if (w != SFX_OK) return w;
+  return launch_status(
+      sfx::launch_predict_q4((hipStream_t)stream, B, d, h, f, x, W1, W1_scales, W2, W2_scales, scores, ws));
 }
 
 // ------------------------------------------------------------------------------ compact
@@ -124,7 +138,7 @@ int sfx_sparse_up(void* stream, int wdt, int act, int B, int d, int f, const voi
                   const void* Wa_scales, const float* ba, const void* Wl, const void* Wl_scales,
                   const int32_t* idx, const int32_t* count, int kmax, float* hact) {
   if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
-  if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
+  if (act != SFX_RELU && act != SFX_REGLU && act != SFX_RELU2) return SFX_E_DTYPE;
   if (B < 1 || B > SFX_MAX_B || d < 1 || f < 1 || kmax < 1) return SFX_E_SHAPE;
   if (!x || !Wa || !idx || !count || !hact) return SFX_E_NULL;
   if (act == SFX_REGLU && !Wl) return SFX_E_NULL;

@@ -15,6 +15,9 @@ size_t predict_ws_bytes(int wdt, int B, int d, int h, int f);
 hipError_t launch_predict(hipStream_t s, int wdt, int B, int d, int h, int f, const void* x,
                           const void* W1, const void* W2, float* scores, void* ws);
 
+hipError_t launch_predict_q4(hipStream_t s, int B, int d, int h, int f, const void* x, const void* W1,
+                             const void* W1_s, const void* W2, const void* W2_s, float* scores, void* ws);
+
 size_t compact_ws_bytes(int B, int f);
 hipError_t launch_compact(hipStream_t s, int B, int f, const float* scores, float t,
                           uint32_t* tok_bits, uint32_t* union_bits, int32_t* idx, int kmax,

@@ -7,6 +7,7 @@ from . import _abi as A
 
 TORCH_WDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 WDT_CODE = {"f32": A.SFX_F32, "f16": A.SFX_F16, "bf16": A.SFX_BF16, "q4": A.SFX_Q4G32}
+# `pdtype` of StepBuffers is the predictor's storage: "q4" selects the int4 predictor
 
 
 class StepBuffers:
@@ -53,7 +54,10 @@ def run_layer(buf: StepBuffers, layer, x: torch.Tensor, threshold: float, act: s
     """predict -> compact -> up -> down for one layer.  `layer` holds the device
     tensors W1, W2, Wa, ba, Wd (Wl, Wa_s, Wl_s, Wd_s when present)."""
     g = layer.get if isinstance(layer, dict) else (lambda k: getattr(layer, k, None))
-    A.sfx_predict(x, g("W1"), g("W2"), buf.scores, buf.ws_pred, stream=stream)
+    if g("W1_s") is not None:
+        A.sfx_predict_q4(x, g("W1"), g("W1_s"), g("W2"), g("W2_s"), buf.scores, buf.ws_pred, stream=stream)
+    else:
+        A.sfx_predict(x, g("W1"), g("W2"), buf.scores, buf.ws_pred, stream=stream)
     A.sfx_compact(buf.scores, threshold, buf.union_bits, buf.idx, buf.count, buf.ws_comp,
                   tok_bits=buf.tok_bits if tok_bits else None, stream=stream)
     A.sfx_sparse_up(x, g("Wa"), g("ba"), buf.idx, buf.count, buf.hact, act=act, Wa_scales=g("Wa_s"),

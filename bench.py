@@ -54,6 +54,8 @@ def parse():
                    help="time the Live Pipeline step (sfx_ffn_pipeline) as the headline: each layer's predictor "
                         "scores the previous layer's input (layer 0: the previous token's), inputs of adjacent "
                         "layers at cosine 0.98")
+    p.add_argument("--pred-q4", action="store_true",
+                   help="store the predictor (W1, W2) in int4 g32 with fp16 scales (separate calls)")
     p.add_argument("--stream-probe", type=int, default=0, metavar="MIB",
                    help="only run the streaming-read probe over MIB MiB (5 reads) and print its bandwidth")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -75,14 +77,21 @@ def row_bytes(cfg):
     return cfg.d * e_bytes(cfg.wdtype)
 
 
+def pred_weight_bytes(cfg):
+    """Bytes per predictor weight: the storage type's, or 1/2 + 2/32 for int4 g32
+    (codes and fp16 scales)."""
+    return 0.5 + 2.0 / 32 if cfg.pred_q4 else e_bytes(cfg.pdtype)
+
+
 def kernel_bytes(cfg, B, k):
     """Algorithmic bytes of one layer-step, per call (what the method must move)."""
     d, f, h = cfg.d, cfg.f, cfg.h
     ep = e_bytes(cfg.pdtype)
+    epw = pred_weight_bytes(cfg)
     na = 2 if cfg.act == "reglu" else 1
     er = row_bytes(cfg)
     return {
-        "predict": (h * d + f * h) * ep + B * d * ep + B * f * 4,
+        "predict": (h * d + f * h) * epw + B * d * ep + B * f * 4,
         "compact": B * f * 4 + (1 + B) * f / 8 + k * 4,
         "up": B * d * ep + k * 4 + na * k * er + k * 4 + B * k * 4,
         "down": k * 4 + B * k * 4 + k * er + B * d * 4,
@@ -151,7 +160,7 @@ class Workload:
                                               self.pred_inputs(s) if mode == "pipeline" else None,
                                               tok_bits=False) for s in range(W + K)]
         else:
-            self.buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype, device=dev)
+            self.buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pred_storage, device=dev)
             self.run_layer = run_layer
 
     def pred_inputs(self, s):
@@ -259,13 +268,18 @@ def time_workload(wl, roofline_steps):
             for l in range(L):
                 t = wl.tensors[l]
                 evs[i][0].record()
-                A.sfx_predict(wl.xs[l][s], t["W1"], t["W2"], wl.buf.scores, wl.buf.ws_pred)
+                if t.get("W1_s") is not None:
+                    A.sfx_predict_q4(wl.xs[l][s], t["W1"], t["W1_s"], t["W2"], t["W2_s"], wl.buf.scores,
+                                     wl.buf.ws_pred)
+                else:
+                    A.sfx_predict(wl.xs[l][s], t["W1"], t["W2"], wl.buf.scores, wl.buf.ws_pred)
                 evs[i][1].record()
                 i += 1
         torch.cuda.synchronize()
         dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
         dom_bytes = float(kernel_bytes(cfg, B, 0)["predict"])
-        dom_name = "sfx_predict (k_pred_hidden + k_pred_scores)"
+        dom_name = ("sfx_predict_q4 (k_pred_hidden_q4 + k_pred_scores_q4)" if cfg.pred_q4 else
+                    "sfx_predict (k_pred_hidden + k_pred_scores)")
     dom_gbps = dom_bytes / (dur_ms.mean() * 1e-3) / 1e9
     return {
         "ms_step": ms_step, "counts": counts, "step_bytes": step_bytes, "gbps": gbps,
@@ -441,11 +455,14 @@ def main():
             return "pipeline"
         # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
         # separate calls run on the matrix cores and measured faster (--fused forces it)
-        fused = (not args.separate) and (args.fused or B <= 2) and \
+        fused = (not args.separate) and (args.fused or B <= 2) and not cfg.pred_q4 and \
             StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
         return "fused" if fused else "separate"
 
     cfg = S.CONFIGS[args.config]
+    if args.pred_q4:
+        cfg = S.scaled(cfg, name=cfg.name, pred_q4=True,
+                       workload=cfg.workload + ", int4 g32 predictor")
     B = args.batch
     L = args.layers or cfg.layers
     wl = Workload(args, cfg, B, L, mode_for(cfg, B, args.pipeline), dev)

@@ -73,7 +73,8 @@ typedef enum {
 
 typedef enum {
   SFX_RELU = 0,  /* a = max(Wa_i . x + b_i, 0) */
-  SFX_REGLU = 1  /* a = max(Wa_i . x + b_i, 0) * (Wl_i . x)  (gate = Wa, linear = Wl) */
+  SFX_REGLU = 1, /* a = max(Wa_i . x + b_i, 0) * (Wl_i . x)  (gate = Wa, linear = Wl) */
+  SFX_RELU2 = 2  /* a = max(Wa_i . x + b_i, 0)^2  (squared ReLU; sfx_sparse_up only) */
 } sfx_act;
 
 /* Host: static text for a status code. */
@@ -115,6 +116,26 @@ int sfx_predict(void* stream, int wdt, int B, int d, int h, int f,
                 float* scores, void* ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------
+ * sfx_predict_q4 -- the same predictor with int4 weights (PowerInfer page, Method,
+ * §5.1; Pitfalls: the predictors are large -- for the OPT-30B-shaped layer at batch 1
+ * an fp16 predictor is most of the bytes a step reads; int4 cuts it by 3.6x).
+ *
+ *   hidden_b = max(W1 x_b, 0) (fp32),  scores_b = W2 hidden_b,  W = q * s
+ *
+ *   x          [B][d] binary16.
+ *   W1         [h][d/2] packed int4 codes, W1_scales [h][d/32] binary16 (the layout
+ *              of SFX_Q4G32); W2 [f][h/2] codes, W2_scales [f][h/32].
+ *   scores     [B][f] fp32, written.
+ *   ws         >= sfx_predict_ws(SFX_Q4G32, B, d, h, f) bytes: the control line,
+ *              then the fp32 hidden [B][h].
+ * d and h must be multiples of 32; scale arrays 2-byte aligned.  Vector kernels at
+ * every batch size (no fp16 range limit).
+ * ------------------------------------------------------------------------------- */
+int sfx_predict_q4(void* stream, int B, int d, int h, int f, const void* x,
+                   const void* W1, const void* W1_scales, const void* W2, const void* W2_scales,
+                   float* scores, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
  * sfx_compact -- threshold and compaction (PowerInfer page, Method, hybrid-execution
  * pseudocode: a neuron is computed when its score is >= the threshold; Paper vs code,
  * predictor threshold).  For B > 1 the active set is the union of the per-token sets.
@@ -144,12 +165,13 @@ int sfx_compact(void* stream, int B, int f, const float* scores, float threshold
 /* ---------------------------------------------------------------------------------
  * sfx_sparse_up -- gathered up (and gate) rows of the active neurons (PowerInfer page,
  * Method, neuron-aware operators of §5.4: only active rows are read; Paper vs code,
- * activation functions ReLU and ReGLU).  Every token computes every listed neuron.
+ * activation functions ReLU, ReGLU and squared ReLU).  Every token computes every
+ * listed neuron.
  *
  *   hact[j][b] = act(Wa[idx[j]] . x_b + ba[idx[j]])      for j < *count, b < B
  *
  *   wdt      storage of the FFN rows: SFX_F32, SFX_F16, SFX_BF16 or SFX_Q4G32.
- *   act      SFX_RELU or SFX_REGLU.
+ *   act      SFX_RELU, SFX_REGLU or SFX_RELU2.
  *   x        [B][d] in wdt (binary16 when wdt = SFX_Q4G32).
  *   Wa       [f][d] activated branch, row = neuron (Q4: packed codes).
  *   Wa_scales Q4 scales [f][d/32] binary16, else NULL.

@@ -14,11 +14,12 @@ Functions and the passages they follow:
                 batch, the active set is the union of the per-token sets.
   sparse_up     PowerInfer page, Method, neuron-aware operators (§5.4): only the
                 rows of active neurons are read; Paper vs code, activation
-                functions (ReLU, ReGLU).
+                functions (ReLU, ReGLU, squared ReLU).
   sparse_down   PowerInfer page, Method, hybrid-execution pseudocode: y is the sum
                 of the active neurons' contributions (the partial sums of the two
                 executors add up to it).
-  dequant_q4    int4 symmetric, group 32, fp16 scale: w = q * s.
+  dequant_q4    int4 symmetric, group 32, fp16 scale: w = q * s (FFN rows, and the
+                predictor's W1 / W2 when they are stored in int4).
   tam_update    KAIROX page, Core method, item 4 (TAM, §6): a group's score
                 accumulates when active and decays by lambda when not; candidates
                 exceed tau = (1 - lambda) + eps; the highest-scoring candidates fill
@@ -133,6 +134,7 @@ def sparse_up(x: np.ndarray, Wa_rows: np.ndarray, ba_rows, act: str, Wl_rows=Non
     """Activations of the active neurons.  x [B][d]; Wa_rows / Wl_rows [k][d] are the
     active rows (row j <-> neuron idx[j]); ba_rows [k] or None.
     ReLU:  a = max(Wa_i . x + b_i, 0).  ReGLU: a = max(Wa_i . x + b_i, 0) * (Wl_i . x).
+    Squared ReLU ('relu2'): a = max(Wa_i . x + b_i, 0)^2.
     Returns hact [k][B]."""
     x = np.atleast_2d(np.asarray(x, dtype=F64))
     z = Wa_rows @ x.T                            # (k, B)
@@ -141,6 +143,8 @@ def sparse_up(x: np.ndarray, Wa_rows: np.ndarray, ba_rows, act: str, Wl_rows=Non
     a = np.maximum(z, 0.0)
     if act == "reglu":
         a = a * (Wl_rows @ x.T)
+    elif act == "relu2":
+        a = a * a
     elif act != "relu":
         raise ValueError(act)
     return a
@@ -163,6 +167,8 @@ def dense_ffn(x, Wa, ba, Wd, act: str, Wl=None) -> np.ndarray:
     a = np.maximum(z, 0.0)
     if act == "reglu":
         a = a * (x @ Wl.T)
+    elif act == "relu2":
+        a = a * a
     return a @ Wd
 
 
@@ -176,6 +182,14 @@ def true_relu_idx(x, Wa, ba) -> np.ndarray:
     return np.flatnonzero((z > 0.0).any(axis=0)).astype(np.int32)
 
 
+def predictor_weights(layer: dict, pdtype: str):
+    """fp64 W1, W2 of a layer: decoded from `pdtype` storage, or dequantised when the
+    layer carries int4 predictor scales (W1_s, W2_s)."""
+    if layer.get("W1_s") is not None:
+        return dequant_q4(layer["W1"], layer["W1_s"]), dequant_q4(layer["W2"], layer["W2_s"])
+    return decode(layer["W1"], pdtype), decode(layer["W2"], pdtype)
+
+
 def ffn_step(x, layer: dict, wdtype: str, pdtype: str, act: str, threshold: float, xp=None):
     """One layer-step in the pages' order: predict -> gate -> up -> down.
     `layer` holds storage arrays W1, W2, Wa, ba, Wd (and Wl, *_s scales).  The
@@ -184,8 +198,7 @@ def ffn_step(x, layer: dict, wdtype: str, pdtype: str, act: str, threshold: floa
     Returns a dict with scores, tok_mask, union, idx, count, hact, y."""
     x64 = decode(x, pdtype)
     xp64 = x64 if xp is None else decode(xp, pdtype)
-    W1 = decode(layer["W1"], pdtype)
-    W2 = decode(layer["W2"], pdtype)
+    W1, W2 = predictor_weights(layer, pdtype)
     scores = predict(xp64, W1, W2)
     tok_mask, union, idx, count = gate(scores, threshold)
     Wa_r = rows(layer["Wa"], wdtype, idx, layer.get("Wa_s"))
@@ -219,9 +232,10 @@ def tam_select(score: np.ndarray, prev_hot: np.ndarray, tau: float, K: int):
     three sets as bool [G]."""
     score = np.asarray(score)
     G = score.shape[0]
-    cand = [g for g in range(G) if score[g] > tau]
-    order = sorted(cand, key=lambda g: (-score[g], g))
-    topk = np.asarray(order[:K], dtype=np.int32)
+    cand = np.flatnonzero(score > tau)
+    # rank: score descending, then group id ascending (lexsort sorts by its last key first)
+    order = cand[np.lexsort((cand, -score[cand]))]
+    topk = order[:K].astype(np.int32)
     hot = np.zeros(G, dtype=bool)
     hot[topk] = True
     prev_hot = np.asarray(prev_hot, dtype=bool)

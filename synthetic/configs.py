@@ -25,11 +25,18 @@ class FFNConfig:
     planted: bool          # co-activated groups of 32 planted in the predictor
     tam: Optional[dict] = None
     workload: str = ""
+    pred_q4: bool = False  # predictor W1 / W2 stored as int4 g32 (x stays fp16)
 
     @property
     def pdtype(self) -> str:
-        """Storage of the predictor weights and of x (q4 layers keep an f16 predictor)."""
-        return "f16" if self.wdtype == "q4" else self.wdtype
+        """Storage of x and, unless pred_q4, of the predictor weights (q4 layers keep
+        an fp16 x and, by default, an fp16 predictor)."""
+        return "f16" if (self.wdtype == "q4" or self.pred_q4) else self.wdtype
+
+    @property
+    def pred_storage(self) -> str:
+        """Storage of the predictor weights: 'q4' when pred_q4, else pdtype."""
+        return "q4" if self.pred_q4 else self.pdtype
 
     @property
     def groups(self) -> int:

@@ -117,8 +117,8 @@ def quantize_q4(w: torch.Tensor):
 class Layer:
     cfg: FFNConfig
     index: int
-    W1: torch.Tensor               # [h][d]  predictor layer 1 (pdtype)
-    W2: torch.Tensor               # [f][h]  predictor layer 2 (pdtype)
+    W1: torch.Tensor               # [h][d]  predictor layer 1 (pdtype; int4: uint8 [h][d/2])
+    W2: torch.Tensor               # [f][h]  predictor layer 2 (pdtype; int4: uint8 [f][h/2])
     Wa: torch.Tensor               # [f][d]  activated branch (row = neuron); q4: uint8 [f][d/2]
     ba: torch.Tensor               # [f]     fp32 bias of the activated branch
     Wd: torch.Tensor               # [f][d]  down projection, neuron-major; q4: uint8 [f][d/2]
@@ -129,10 +129,12 @@ class Layer:
     Wa_s: Optional[torch.Tensor] = None    # q4 scales [f][d/32] fp16
     Wl_s: Optional[torch.Tensor] = None
     Wd_s: Optional[torch.Tensor] = None
+    W1_s: Optional[torch.Tensor] = None    # int4 predictor scales [h][d/32], [f][h/32] fp16
+    W2_s: Optional[torch.Tensor] = None
 
     def tensors(self) -> Dict[str, torch.Tensor]:
         out = {}
-        for k in ("W1", "W2", "Wa", "ba", "Wd", "perm", "Wl", "Wa_s", "Wl_s", "Wd_s"):
+        for k in ("W1", "W2", "Wa", "ba", "Wd", "perm", "Wl", "Wa_s", "Wl_s", "Wd_s", "W1_s", "W2_s"):
             v = getattr(self, k)
             if v is not None:
                 out[k] = v
@@ -144,7 +146,7 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
     pdt = TORCH_DTYPE[cfg.pdtype]
     name = cfg.name
 
-    W1 = (_randn(_rng(name, layer, "W1", device), h, d, device) / math.sqrt(d)).to(pdt)
+    W1 = _randn(_rng(name, layer, "W1", device), h, d, device) / math.sqrt(d)
     if cfg.planted:
         groups = (f + 31) // 32
         u = _randn(_rng(name, layer, "blk", device), groups, h, device)
@@ -154,7 +156,12 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
         del u, v
     else:
         W2 = _randn(_rng(name, layer, "W2", device), f, h, device) / math.sqrt(h)
-    W2 = W2.to(pdt)
+    W1_s = W2_s = None
+    if cfg.pred_q4:
+        W1, W1_s = quantize_q4(W1)
+        W2, W2_s = quantize_q4(W2)
+    else:
+        W1, W2 = W1.to(pdt), W2.to(pdt)
 
     p = zipf_profile(f, cfg.density)
     ba = torch.from_numpy(ndtri(p)).to(torch.float32).to(device)
@@ -180,7 +187,7 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
     perm = torch.randperm(f, generator=g).to(torch.int32).to(device)
     return Layer(cfg=cfg, index=layer, W1=W1, W2=W2, Wa=Wa, ba=ba, Wd=Wd,
                  threshold=threshold_for(cfg.density), perm=perm, p=p,
-                 Wl=Wl, Wa_s=Wa_s, Wl_s=Wl_s, Wd_s=Wd_s)
+                 Wl=Wl, Wa_s=Wa_s, Wl_s=Wl_s, Wd_s=Wd_s, W1_s=W1_s, W2_s=W2_s)
 
 
 def make_tokens(cfg: FFNConfig, layer: int, steps: int, B: int, device="cpu", tag: str = "x") -> torch.Tensor:

@@ -27,7 +27,7 @@ def gpu_layer_step(cfg, L, x: torch.Tensor, threshold=None, buf=None):
     """Run predict -> compact -> up -> down on the GPU; return host copies."""
     B = x.shape[0]
     if buf is None:
-        buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pdtype)
+        buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pred_storage)
     t = L.threshold if threshold is None else threshold
     run_layer(buf, L.tensors(), x, t, cfg.act)
     torch.cuda.synchronize()
@@ -58,7 +58,7 @@ def check_step(cfg, Lnp: dict, x_np: np.ndarray, out: dict, t: float, report: di
     pd, wd = cfg.pdtype, cfg.wdtype
     x64 = O.decode(x_np, pd)
     xp64 = x64 if xp_np is None else O.decode(xp_np, pd)
-    s64 = O.predict(xp64, O.decode(Lnp["W1"], pd), O.decode(Lnp["W2"], pd))
+    s64 = O.predict(xp64, *O.predictor_weights(Lnp, pd))
     r = {}
 
     # (1) scores against fp64

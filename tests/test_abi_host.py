@@ -80,7 +80,7 @@ def test_up_validation(lib):
     call = lambda **k: lib.sfx_sparse_up(None, k.get("wdt", 1), k.get("act", 0), k.get("B", 1), k.get("d", 4096),
                                          1000, GOOD, GOOD, k.get("sa"), None, k.get("wl"), k.get("sl"),
                                          GOOD, GOOD, 1000, GOOD)
-    assert call(act=2) == E_DTYPE
+    assert call(act=3) == E_DTYPE                # 0 ReLU, 1 ReGLU, 2 squared ReLU
     assert call(wdt=4) == E_DTYPE
     assert call(act=1) == E_NULL                # ReGLU needs the linear branch
     assert call(wdt=3) == E_NULL                # int4 needs scales
@@ -172,3 +172,18 @@ def test_stream_read_validation(lib):
     assert lib.sfx_stream_read(None, GOOD, 0, GOOD) == E_SHAPE
     assert lib.sfx_stream_read(None, None, 4096, GOOD) == E_NULL
     assert lib.sfx_stream_read(None, ODD, 4096, GOOD) == E_ALIGN
+
+
+def test_predict_q4_validation(lib):
+    ws_n = lib.sfx_predict_ws(3, 1, 7168, 1536, 28672)
+    assert ws_n == 256 + 1536 * 4
+    call = lambda **k: lib.sfx_predict_q4(None, k.get("B", 1), k.get("d", 7168), k.get("h", 1536), 28672,
+                                          GOOD, k.get("W1", GOOD), k.get("s1", GOOD), GOOD, GOOD, GOOD,
+                                          P(0x20000), k.get("wsn", ws_n))
+    assert call(d=7160) == E_SHAPE             # d and h multiples of 32
+    assert call(h=1540) == E_SHAPE
+    assert call(B=0) == E_SHAPE
+    assert call(W1=None) == E_NULL and call(s1=None) == E_NULL
+    assert call(W1=ODD) == E_ALIGN
+    assert call(s1=P(0x10001)) == E_ALIGN
+    assert call(wsn=ws_n - 1) == E_WORKSPACE

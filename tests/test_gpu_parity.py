@@ -320,3 +320,59 @@ def test_predict_fp16_range_flag(B):
                         W216.numpy().astype(np.float64))
         err = np.max(np.abs(scores.cpu().numpy().astype(np.float64) - s64) / np.maximum(1.0, np.abs(s64)))
         assert err <= 1e-5, err
+
+
+# squared ReLU (activation functions of the PowerInfer page's code notes) on the
+# vector kernels (1 token, int4 rows) and the matrix cores (3 tokens)
+RELU2 = {
+    "C2r": S.scaled(S.CONFIGS["C2"], name="C2r", act="relu2", d=1032, f=3000, h=136),
+    "C4r": S.scaled(S.CONFIGS["C4"], name="C4r", act="relu2", d=1056, f=2000, h=136),
+}
+
+
+@pytest.mark.parametrize("name,B", [("C2r", 1), ("C2r", 3), ("C2r", 8), ("C4r", 1)])
+def test_squared_relu(name, B):
+    cfg = RELU2[name]
+    L = S.make_layer(cfg, 0, device=DEV)
+    Lnp = layer_np(L)
+    xs = _tokens(cfg, 0, 2, B)
+    for step in range(2):
+        say(f"squared relu {name} B={B} step {step}")
+        out, _ = gpu_layer_step(cfg, L, xs[step])
+        r = check_step(cfg, Lnp, S.storage_numpy(xs[step]), out, L.threshold)
+        assert np.all(out["hact"] >= 0)
+
+
+# int4 g32 predictor (W1, W2 as codes + fp16 scales) on the OPT-30B recipe
+PQ4 = {
+    "C4q": S.scaled(S.CONFIGS["C4"], name="C4q", pred_q4=True, d=1056, f=2000, h=160),
+    "C2q": S.scaled(S.CONFIGS["C2"], name="C2q", pred_q4=True, d=1024, f=3008, h=128),
+}
+
+
+@pytest.mark.parametrize("name,B", [("C4q", 1), ("C4q", 2), ("C4q", 8), ("C2q", 1), ("C2q", 5)])
+def test_int4_predictor(name, B):
+    cfg = PQ4[name]
+    L = S.make_layer(cfg, 0, device=DEV)
+    assert L.W1.dtype == torch.uint8 and L.W1_s is not None
+    Lnp = layer_np(L)
+    xs = _tokens(cfg, 0, 2, B)
+    for step in range(2):
+        say(f"int4 predictor {name} B={B} step {step}")
+        out, _ = gpu_layer_step(cfg, L, xs[step])
+        check_step(cfg, Lnp, S.storage_numpy(xs[step]), out, L.threshold)
+
+
+def test_int4_predictor_full_size():
+    """OPT-30B shape, int4 rows and int4 predictor (30 MB instead of 110 MB of
+    predictor per layer-step), batch 1."""
+    cfg = S.scaled(S.CONFIGS["C4"], name="C4", pred_q4=True)
+    L = S.make_layer(cfg, 0, device=DEV)
+    Lnp = layer_np(L)
+    xs = _tokens(cfg, 0, 2, 1)
+    for step in range(2):
+        say(f"int4 predictor full size step {step}")
+        out, _ = gpu_layer_step(cfg, L, xs[step])
+        r = check_step(cfg, Lnp, S.storage_numpy(xs[step]), out, L.threshold)
+        say("   ", r)
+    torch.cuda.empty_cache()

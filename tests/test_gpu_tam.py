@@ -60,28 +60,50 @@ def test_tam_hand_fixture():
         assert np.flatnonzero(_bits_to_bool(st.left[0].cpu().numpy(), g["G"])).tolist() == step["left"]
 
 
+def _unpack(words, G):
+    """[L][ceil(G/32)] bit words -> bool [L][G] (bit g % 32 of word g / 32)."""
+    w = np.asarray(words).view(np.uint32).astype(np.uint64)
+    bits = (w[:, :, None] >> np.arange(32, dtype=np.uint64)) & 1
+    return bits.reshape(w.shape[0], -1)[:, :G].astype(bool)
+
+
 @pytest.mark.parametrize("lam", [0.8, 0.9, 0.95])
 def test_tam_random_bits_60_layers(lam):
-    """60 layers x 1024 groups, K = 256, 64 steps of seeded random group activity
-    with persistence (active groups stay active with probability 0.8)."""
-    L, G, K, eps = 60, 1024, 256, 0.01
+    """The Falcon-40B workload's TAM: 60 layers x 1024 groups, K = 256, 512 steps
+    of seeded random group activity with persistence (active groups stay active
+    with probability 0.8), every layer of every step against the oracle."""
+    L, G, K, eps, steps = 60, 1024, 256, 0.01, 512
     rng = np.random.default_rng(int(lam * 100))
     st = TamState(L, G, K)
     score64 = np.zeros((L, G))
     prev_hot = np.zeros((L, G), bool)
     act = rng.random((L, G)) < 0.2
     tau32 = _tau32(lam, eps)
-    for step in range(64):
+    worst = 0.0
+    for step in range(steps):
         keep = rng.random((L, G)) < 0.8
         act = np.where(act, keep, rng.random((L, G)) < 0.05)
         words = np.where(act, rng.integers(1, 2 ** 32, size=(L, G), dtype=np.uint64), 0).astype(np.uint32)
         u = torch.from_numpy(words.view(np.int32)).to(DEV)
-        say(f"tam lambda={lam} step {step}")
+        if step % 64 == 0:
+            say(f"tam lambda={lam} step {step}")
         st.update(u, lam, eps)
         torch.cuda.synchronize()
+        s_gpu = st.score.cpu().numpy()
+        topk_gpu, cnt_gpu = st.topk.cpu().numpy(), st.topk_count.cpu().numpy()
+        hot_gpu, ent_gpu, left_gpu = (_unpack(t.cpu().numpy(), G) for t in (st.hot, st.entered, st.left))
         for l in range(L):
             score64[l], _, _, _, _ = O.tam_update(score64[l], prev_hot[l], words[l], lam, eps, K)
-            prev_hot[l] = _check_layer(st, l, G, K, prev_hot[l], score64[l], tau32)
+            worst = max(worst, float(np.max(np.abs(s_gpu[l].astype(np.float64) - score64[l]))))
+            topk, hot, ent, left = O.tam_select(s_gpu[l].astype(np.float64), prev_hot[l], tau32, K)
+            n = int(cnt_gpu[l])
+            assert n == topk.size and np.array_equal(topk_gpu[l, :n], topk), (step, l)
+            assert np.all(topk_gpu[l, n:K] == -1)
+            assert np.array_equal(hot_gpu[l], hot) and np.array_equal(ent_gpu[l], ent), (step, l)
+            assert np.array_equal(left_gpu[l], left), (step, l)
+            prev_hot[l] = hot
+    say(f"   max |s_gpu - s64| over {steps} steps: {worst:.2e}")
+    assert worst <= 1e-5
 
 
 def test_tam_on_real_union_bits():

@@ -168,7 +168,7 @@ def _rand_layer(rng, d, f, act):
     return Wa, ba, Wd, Wl
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
 def test_all_ones_mask_equals_dense(act):
     """Every neuron active -> sparse up/down equals the dense FFN (np.matmul on the
     whole matrices), rel <= 1e-12."""
@@ -311,3 +311,35 @@ def test_mask_recall():
     assert O.mask_recall(np.array([1, 0, 1, 1, 0], bool), exact) == 2 / 3
     assert O.mask_recall(exact, exact) == 1.0
     assert O.mask_recall(np.zeros(5, bool), np.zeros(5, bool)) == 1.0
+
+
+# ----------------------------------------------------------------------------- squared ReLU, int4 predictor
+
+def test_squared_relu_hand_values():
+    """sparse_up with 'relu2': z = (2, -1, 0.5) for one token -> (4, 0, 0.25); a
+    missing square, a square before the ReLU ((-1)^2 = 1) or a dropped bias fail."""
+    x = np.array([[1.0, 2.0]])
+    Wa = np.array([[1.0, 0.0], [0.0, -1.0], [0.5, 0.0]])
+    ba = np.array([1.0, 1.0, 0.0])
+    h = O.sparse_up(x, Wa, ba, "relu2")
+    assert h[:, 0].tolist() == [4.0, 0.0, 0.25]
+
+
+def test_predictor_weights_int4():
+    """An int4 predictor is used dequantised: codes 0x8F (-1, -8) and 0x70 (0, 7)
+    with scale 0.5 per 32 columns; the scores of a one-hot input pick the column."""
+    d, h, f = 32, 32, 32
+    W1q = np.zeros((h, d // 2), np.uint8)
+    W1q[0, 0] = 0x8F                       # W1[0][0] = -1 * 0.5, W1[0][1] = -8 * 0.5
+    W1q[1, 1] = 0x70                       # W1[1][2] = 0, W1[1][3] = 7 * 0.5
+    W1s = np.full((h, d // 32), 0.5, np.float16)
+    W2q = np.zeros((f, h // 2), np.uint8)
+    W2q[5, 0] = 0x10                       # W2[5][1] = 1 * 2
+    W2s = np.full((f, h // 32), 2.0, np.float16)
+    layer = {"W1": W1q, "W1_s": W1s, "W2": W2q, "W2_s": W2s}
+    W1, W2 = O.predictor_weights(layer, "f16")
+    assert W1[0, 0] == -0.5 and W1[0, 1] == -4.0 and W1[1, 3] == 3.5 and W1[1, 2] == 0.0
+    x = np.zeros((1, d))
+    x[0, 3] = 2.0                          # hidden[1] = relu(3.5 * 2) = 7, hidden[0] = 0
+    s = O.predict(x, W1, W2)
+    assert s[0, 5] == 14.0 and np.count_nonzero(s) == 1
