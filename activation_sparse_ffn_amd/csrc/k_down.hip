@@ -233,6 +233,105 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ Wd,
 }
 
 
+// ------------------------------------------------------------------ B <= 2, 16-bit rows
+// Column tiles without partial sums: workgroup t owns columns [CW t, CW t + CW) of
+// y and reads that segment of every listed row (CW / 8 lanes per row, 256 / (CW /
+// 8) row slots per workgroup, kCU rows per slot in flight), so y is written by its
+// owner after a fixed-order sum over the slots: two dependent round trips
+// (indices and activations, then the row segments) instead of the slices' five
+// (plus write-through partials, a ticket and the last workgroup's reduction).
+// Tiles are numbered so that the four tiles sharing a 128-byte line of a row run
+// on one XCD (workgroups are dispatched round-robin over the 8 XCDs).
+// CW = 16 columns (32-byte segments) up to d = 4096; 32 columns (64-byte segments,
+// half as many workgroups) above.
+template <class T, int NB, int CW>
+__global__ __launch_bounds__(kBlock) void k_down_cols(const uint8_t* __restrict__ Wd,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ count, int kmax,
+                                                      const float* __restrict__ hact, int B, int d, int f,
+                                                      float* __restrict__ y, int ntiles) {
+  constexpr int kLPR = CW / 8;            // lanes per row
+  constexpr int kColSlots = kBlock / kLPR;
+  constexpr int kCU = NB == 1 ? 16 : 8;   // rows per slot in flight
+  constexpr int kColW = CW;
+  __shared__ float s_sum[kWavesPerBlock][kLPR][NB][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int w = blockIdx.x, P = gridDim.x;
+  const int tile = (P % 8 == 0 && P == ntiles) ? (w & 7) * (P >> 3) + (w >> 3) : w;
+  const int half = threadIdx.x & (kLPR - 1);
+  const int slot = threadIdx.x / kLPR;
+  const int col = tile * kColW + half * 8;
+  const bool cok = col < d;
+  const size_t rb = (size_t)d * 2;
+  const size_t cb = (size_t)(cok ? col : 0) * 2;
+  const int k = min(*count, kmax);
+  float acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+  for (int r0 = slot; r0 < k; r0 += kColSlots * kCU) {
+    int nid[kCU];
+    float hv[kCU][NB];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int r = min(r0 + u * kColSlots, k - 1);
+      nid[u] = idx[r];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) hv[u][b] = hact[(size_t)r * B + min(b, B - 1)];
+    }
+    Raw<16> wv[kCU];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int i = (unsigned)nid[u] < (unsigned)f ? nid[u] : 0;
+      wv[u] = load_raw<16>(Wd + (size_t)i * rb + cb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      if (r0 + u * kColSlots < k && (unsigned)nid[u] < (unsigned)f) {
+        float wf[8];
+        unpack<T, 4>(wv[u].w, wf);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < B) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(hv[u][b], wf[e], acc[b][e]);
+          }
+      }
+    }
+  }
+  // sum the slots: lanes of one column chunk within the wave (fixed butterfly
+  // over the lane bits above the chunk), then the four waves in order
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[b][e];
+#pragma unroll
+      for (int o = kLPR; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+      acc[b][e] = v;
+    }
+  if (lane < kLPR) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_sum[wave][lane][b][e] = acc[b][e];
+  }
+  __syncthreads();
+  if (threadIdx.x < kLPR * NB * 8) {
+    const int hh = threadIdx.x / (NB * 8), rem = threadIdx.x % (NB * 8), b = rem / 8, e = rem % 8;
+    const int c = tile * kColW + hh * 8 + e;
+    if (b < B && c < d) {
+      float t = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWavesPerBlock; ++v) t += s_sum[v][hh][b][e];
+      y[(size_t)b * d + c] = t;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ B >= 3
 // From 3 tokens on the products run on the matrix cores: v_mfma_f32_16x16x4_f32
 // (fp32 operands, so the fp32 activations are used as they are and the 16-bit
@@ -404,6 +503,9 @@ constexpr int lw_for(int nb) {
 
 struct Plan { int lw, cpl, tw, ntiles, S; bool mfma; };
 
+// 16-bit rows at 1-2 tokens take the column-tile kernel (no workspace).
+bool cols_eligible(int B) { return B <= 2; }
+
 // From 3 tokens on (measured, separate calls, all three matrix-core kernels against
 // the vector ones: LLaMA2-7B shape 3 tokens 67.5 -> 56.7 us per layer-step, 4 tokens
 // 76.2 -> 58.9, OPT-6.7B shape 3 tokens 68.3 -> 53.0; at 2 tokens every vector kernel
@@ -483,6 +585,20 @@ template <class T>
 hipError_t dispatch(hipStream_t s, const Plan& p, int B, int d, int f, const void* Wd, const void* Wd_s,
                     const int32_t* idx, const int32_t* count, int kmax, const float* hact, float* y, void* ws) {
   if constexpr (T::bytes == 2) {
+    if (cols_eligible(B)) {
+      const bool wide = d > 4096;
+      const int cw = wide ? 32 : 16;
+      const int ntiles = (d + cw - 1) / cw;
+      const uint8_t* W = (const uint8_t*)Wd;
+      if (B == 1) {
+        if (wide) k_down_cols<T, 1, 32><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, idx, count, kmax, hact, B, d, f, y, ntiles);
+        else k_down_cols<T, 1, 16><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, idx, count, kmax, hact, B, d, f, y, ntiles);
+      } else {
+        if (wide) k_down_cols<T, 2, 32><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, idx, count, kmax, hact, B, d, f, y, ntiles);
+        else k_down_cols<T, 2, 16><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, idx, count, kmax, hact, B, d, f, y, ntiles);
+      }
+      return hipGetLastError();
+    }
     if (p.mfma) {
       if (B <= 16) return run_mfma<T, 1>(s, p, B, d, f, Wd, idx, count, kmax, hact, y, ws);
       if (B <= 32) return run_mfma<T, 2>(s, p, B, d, f, Wd, idx, count, kmax, hact, y, ws);

@@ -220,6 +220,7 @@ size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f) {
 int sfx_ffn_step(void* stream, int wdt, int act, int B, int d, int h, int f, int L, const sfx_layer* layers,
                  void* ws, size_t ws_bytes) {
   if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act == SFX_RELU2) return SFX_E_UNSUPPORTED;   // squared ReLU: the separate calls
   if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
   if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1 || L < 1) return SFX_E_SHAPE;
   if (!layers) return SFX_E_NULL;
@@ -247,6 +248,7 @@ size_t sfx_ffn_pipeline_ws(int wdt, int act, int B, int d, int h, int f) {
 int sfx_ffn_pipeline(void* stream, int wdt, int act, int B, int d, int h, int f, int L, const sfx_layer* layers,
                      void* ws, size_t ws_bytes) {
   if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act == SFX_RELU2) return SFX_E_UNSUPPORTED;   // squared ReLU: the separate calls
   if (act != SFX_RELU && act != SFX_REGLU) return SFX_E_DTYPE;
   if (B < 1 || B > SFX_MAX_B || d < 1 || h < 1 || f < 1 || L < 1) return SFX_E_SHAPE;
   if (!layers) return SFX_E_NULL;

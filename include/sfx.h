@@ -276,7 +276,8 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
  * up early (their outputs are undefined too).  The caller reads it after
  * synchronising and writes zero to reset it.
  *
- *   wdt      SFX_F16 or SFX_BF16 (x, predictor and FFN rows).  act: ReLU / ReGLU.
+ *   wdt      SFX_F16 or SFX_BF16 (x, predictor and FFN rows).  act: ReLU / ReGLU
+ *            (squared ReLU returns SFX_E_UNSUPPORTED; sfx_sparse_up takes it).
  *   B        1..4.   d <= 4096, d and h multiples of 8, f <= 32768.
  *   L        number of layers; `layers` is a DEVICE array of L descriptors
  *            (caller-owned, unchanged until the kernel ends).  Each layer's idx
