@@ -10,4 +10,5 @@ from ._abi import (SFX_BF16, SFX_F16, SFX_F32, SFX_MAX_B, SFX_MAX_GROUPS, SFX_Q4
                    sfx_tam_update, sfx_tam_ws, status_str, workspace)
 from ._abi import layer_descriptors, sfx_ffn_step, sfx_ffn_step_ws  # noqa: F401
 from ._abi import sfx_ffn_pipeline, sfx_ffn_pipeline_ws, sfx_sparse_down_noalloc  # noqa: F401
-from .step import StackStep, StepBuffers, TamState, run_layer  # noqa: F401
+from ._abi import sfx_hot_update, sfx_topk_now_update  # noqa: F401
+from .step import HotRegion, StackStep, StepBuffers, TamState, TopKNowState, run_layer  # noqa: F401

@@ -23,7 +23,9 @@ WDT = {torch.float32: SFX_F32, torch.float16: SFX_F16, torch.bfloat16: SFX_BF16}
 EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict", "sfx_compact_ws",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
            "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
-           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read", "sfx_predict_q4")
+           "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read", "sfx_predict_q4",
+           "sfx_topk_now_update", "sfx_hot_update")
+HOT_MAX_MATS = 8
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
 
@@ -81,6 +83,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_tam_ws.argtypes = [I, I]
     lib.sfx_tam_update.restype = I
     lib.sfx_tam_update.argtypes = [P, I, I, P, F, F, I, P, P, P, P, P, P, P, Z]
+    lib.sfx_topk_now_update.restype = I
+    lib.sfx_topk_now_update.argtypes = [P, I, I, P, I, P, P, P, P, P]
+    lib.sfx_hot_update.restype = I
+    lib.sfx_hot_update.argtypes = [P, I, I, I, P, P, P, P, P, P, I, P, P, P]
     lib.sfx_ffn_step_ws.restype = Z
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
@@ -267,6 +273,33 @@ def sfx_tam_update(union_bits, lam, eps, K, score, hot_bits, entered_bits, left_
     st = load().sfx_tam_update(_stream(stream), L, G, _ptr(union_bits), float(lam), float(eps), int(K), *p,
                                ws.numel() if ws is not None else 0)
     _check(st, "sfx_tam_update")
+
+
+def sfx_topk_now_update(union_bits, K, hot_bits, entered_bits, left_bits, topk, topk_count, stream=None):
+    """The Top-K reload rule on this step's activity alone (no score state).
+    union_bits [L][G], bit sets [L][ceil(G/32)], topk [L][K], topk_count [L]."""
+    L, G = union_bits.shape
+    st = load().sfx_topk_now_update(_stream(stream), L, G, _ptr(union_bits), int(K), _ptr(hot_bits),
+                                    _ptr(entered_bits), _ptr(left_bits), _ptr(topk) if K > 0 else None,
+                                    _ptr(topk_count))
+    _check(st, "sfx_topk_now_update")
+
+
+def sfx_hot_update(G, K, entered_bits, left_bits, slot_of, group_of, copies, ncopies, group_bytes=(),
+                   src=None, dst=None, stream=None):
+    """Hot-region slots and the copy of entering groups for L layers.
+    entered_bits / left_bits [L][ceil(G/32)], slot_of [L][G], group_of [L][K],
+    copies [L][K][2], ncopies [L] (int32 device tensors); group_bytes: host sizes
+    of one group per matrix; src / dst: device int64 tensors [L][nmat] of
+    matrix addresses (None when group_bytes is empty)."""
+    L = entered_bits.shape[0]
+    nmat = len(group_bytes)
+    gb = (ctypes.c_size_t * max(nmat, 1))(*[int(v) for v in group_bytes])
+    st = load().sfx_hot_update(_stream(stream), L, int(G), int(K), _ptr(entered_bits), _ptr(left_bits),
+                               _ptr(slot_of), _ptr(group_of), _ptr(copies), _ptr(ncopies), nmat,
+                               gb if nmat > 0 else None, _ptr(src) if nmat > 0 else None,
+                               _ptr(dst) if nmat > 0 else None)
+    _check(st, "sfx_hot_update")
 
 
 # ------------------------------------------------------------------------- fused step

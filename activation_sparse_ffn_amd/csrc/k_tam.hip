@@ -9,6 +9,11 @@
 // like the values), a bitonic sort ranks the keys (score descending, then group id
 // ascending; in-wave stages on registers, wider ones in LDS), and the first
 // min(K, #candidates) become the hot set.
+//
+// The same ranking also serves a reload rule without memory (the Top-K reload the
+// KAIROX page compares TAM with, Experiments: strategies and ablations): the key is
+// the number of the group's neurons active in this step's union mask, every group
+// with at least one is a candidate, and no score is kept.
 #include "sfx_common.hpp"
 #include "sfx_launch.hpp"
 
@@ -17,6 +22,7 @@ namespace {
 
 constexpr int kT = 1024;
 
+template <bool kNow>
 __global__ __launch_bounds__(kT) void k_tam(int G, const uint32_t* __restrict__ union_bits, float lambda,
                                             float tau, int K, float* __restrict__ score,
                                             uint32_t* __restrict__ hot_bits, uint32_t* __restrict__ entered,
@@ -31,7 +37,13 @@ __global__ __launch_bounds__(kT) void k_tam(int G, const uint32_t* __restrict__ 
 
   unsigned long long key = 0ull;
   int cand = 0;
-  if (g < G) {
+  if (g < G && kNow) {
+    const uint32_t n = (uint32_t)__popc(union_bits[(size_t)l * G + g]);
+    if (n > 0u) {
+      cand = 1;
+      key = ((unsigned long long)n << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)g);
+    }
+  } else if (g < G) {
     const float a = union_bits[(size_t)l * G + g] != 0u ? 1.0f : 0.0f;
     float s = score[(size_t)l * G + g];
     s = fmaf(lambda, s, one_minus * a);
@@ -110,8 +122,15 @@ hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, f
                       int K, float* score, uint32_t* hot_bits, uint32_t* entered, uint32_t* left,
                       int32_t* topk, int32_t* topk_count) {
   const float tau = (1.0f - lambda) + eps;
-  k_tam<<<dim3(L), dim3(kT), 0, s>>>(G, union_bits, lambda, tau, K, score, hot_bits, entered, left, topk,
-                                     topk_count);
+  k_tam<false><<<dim3(L), dim3(kT), 0, s>>>(G, union_bits, lambda, tau, K, score, hot_bits, entered, left, topk,
+                                            topk_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_now(hipStream_t s, int L, int G, const uint32_t* union_bits, int K, uint32_t* hot_bits,
+                           uint32_t* entered, uint32_t* left, int32_t* topk, int32_t* topk_count) {
+  k_tam<true><<<dim3(L), dim3(kT), 0, s>>>(G, union_bits, 0.f, 0.f, K, nullptr, hot_bits, entered, left, topk,
+                                           topk_count);
   return hipGetLastError();
 }
 

@@ -207,6 +207,48 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits, float
                                        entered_bits, left_bits, topk, topk_count));
 }
 
+int sfx_topk_now_update(void* stream, int L, int G, const uint32_t* union_bits, int K, uint32_t* hot_bits,
+                        uint32_t* entered_bits, uint32_t* left_bits, int32_t* topk, int32_t* topk_count) {
+  if (L < 1 || G < 1 || G > SFX_MAX_GROUPS || K < 0 || K > G) return SFX_E_SHAPE;
+  if (!union_bits || !hot_bits || !entered_bits || !left_bits || !topk_count) return SFX_E_NULL;
+  if (K > 0 && !topk) return SFX_E_NULL;
+  return launch_status(sfx::launch_topk_now((hipStream_t)stream, L, G, union_bits, K, hot_bits, entered_bits,
+                                            left_bits, topk, topk_count));
+}
+
+// ------------------------------------------------------------------------------ hot region
+
+int sfx_hot_update(void* stream, int L, int G, int K, const uint32_t* entered_bits, const uint32_t* left_bits,
+                   int32_t* slot_of, int32_t* group_of, int32_t* copies, int32_t* ncopies, int nmat,
+                   const size_t* group_bytes, const void* const* src, void* const* dst) {
+  if (L < 1 || G < 1 || G > SFX_MAX_GROUPS || K < 1 || K > G) return SFX_E_SHAPE;
+  if (L > sfx::kHotMaxLayers) return SFX_E_SHAPE;
+  if (nmat < 0 || nmat > sfx::kHotMaxMats) return SFX_E_SHAPE;
+  if (!entered_bits || !left_bits || !slot_of || !group_of || !copies || !ncopies) return SFX_E_NULL;
+  if (!aligned4(entered_bits) || !aligned4(left_bits) || !aligned4(slot_of) || !aligned4(group_of) ||
+      !aligned4(copies) || !aligned4(ncopies))
+    return SFX_E_ALIGN;
+  sfx::HotMats mats{};
+  mats.n = nmat;
+  if (nmat > 0) {
+    if (!group_bytes || !src || !dst) return SFX_E_NULL;
+    if (((uintptr_t)src & 7u) || ((uintptr_t)dst & 7u)) return SFX_E_ALIGN;
+    int64_t chunks = 0;
+    for (int m = 0; m < nmat; ++m) {
+      if (group_bytes[m] == 0 || (group_bytes[m] & 15u)) return SFX_E_SHAPE;
+      mats.group_bytes[m] = group_bytes[m];
+      mats.chunk_off[m] = (int)chunks;
+      chunks += (int64_t)((group_bytes[m] + sfx::kHotChunk - 1) / sfx::kHotChunk);
+      if (chunks > (int64_t)(1 << 20)) return SFX_E_SHAPE;      // 16 GiB per group
+    }
+    mats.chunk_off[nmat] = (int)chunks;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = sfx::launch_hot_assign(st, L, G, K, entered_bits, left_bits, slot_of, group_of, copies, ncopies);
+  if (e == hipSuccess && nmat > 0) e = sfx::launch_hot_copy(st, L, K, mats, src, dst, copies, ncopies);
+  return launch_status(e);
+}
+
 // ------------------------------------------------------------------------------ fused step
 
 size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f) {

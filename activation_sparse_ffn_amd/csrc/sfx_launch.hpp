@@ -46,5 +46,20 @@ size_t tam_ws_bytes(int G, int K);
 hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, float lambda,
                       float eps, int K, float* score, uint32_t* hot_bits, uint32_t* entered,
                       uint32_t* left, int32_t* topk, int32_t* topk_count);
+hipError_t launch_topk_now(hipStream_t s, int L, int G, const uint32_t* union_bits, int K, uint32_t* hot_bits,
+                           uint32_t* entered, uint32_t* left, int32_t* topk, int32_t* topk_count);
+
+constexpr int kHotMaxMats = 8;
+constexpr int kHotMaxLayers = 1024;
+constexpr int kHotChunk = 16384;         // bytes per work item of the copy kernel
+struct HotMats {
+  int n;                                 // matrices per layer, 0..kHotMaxMats
+  size_t group_bytes[kHotMaxMats];       // bytes of one group's rows in matrix m
+  int chunk_off[kHotMaxMats + 1];        // first chunk of matrix m; chunk_off[n] = chunks per group
+};
+hipError_t launch_hot_assign(hipStream_t s, int L, int G, int K, const uint32_t* entered, const uint32_t* left,
+                             int32_t* slot_of, int32_t* group_of, int32_t* copies, int32_t* ncopies);
+hipError_t launch_hot_copy(hipStream_t s, int L, int K, const HotMats& mats, const void* const* src,
+                           void* const* dst, const int32_t* copies, const int32_t* ncopies);
 
 }  // namespace sfx

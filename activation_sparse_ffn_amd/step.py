@@ -84,6 +84,65 @@ class TamState:
                          self.topk, self.topk_count, stream=stream)
 
 
+class TopKNowState:
+    """Hot sets of L layers chosen by the Top-K reload rule on each step's activity
+    alone (same bit-set layout as TamState, no scores)."""
+
+    def __init__(self, L: int, G: int, K: int, device="cuda"):
+        HW = (G + 31) // 32
+        self.L, self.G, self.K = L, G, K
+        self.hot = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.entered = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.left = torch.zeros(L, HW, dtype=torch.int32, device=device)
+        self.topk = torch.full((L, max(K, 1)), -1, dtype=torch.int32, device=device)
+        self.topk_count = torch.zeros(L, dtype=torch.int32, device=device)
+
+    def update(self, union_bits: torch.Tensor, stream=None):
+        A.sfx_topk_now_update(union_bits, self.K, self.hot, self.entered, self.left, self.topk,
+                              self.topk_count, stream=stream)
+
+
+class HotRegion:
+    """Contiguous hot region of K group slots per layer for a list of matrices per
+    layer (`mats[l][m]`: a device tensor whose first dimension is the f neurons,
+    G groups of 32 rows).  `update(entered, left)` frees the slots of leaving
+    groups and copies the entering groups' rows into free slots; `region[l][m]`
+    holds K groups of matrix m, slot s = group `group_of[l][s]`."""
+
+    def __init__(self, mats, G: int, K: int, device="cuda"):
+        L = len(mats)
+        self.L, self.G, self.K = L, G, K
+        dev = torch.device(device)
+        self.slot_of = torch.full((L, G), -1, dtype=torch.int32, device=dev)
+        self.group_of = torch.full((L, K), -1, dtype=torch.int32, device=dev)
+        self.copies = torch.zeros(L, K, 2, dtype=torch.int32, device=dev)
+        self.ncopies = torch.zeros(L, dtype=torch.int32, device=dev)
+        nmat = len(mats[0]) if L else 0
+        self.group_bytes = []
+        self.region = []
+        for l, ms in enumerate(mats):
+            if len(ms) != nmat:
+                raise ValueError("every layer needs the same matrices")
+            row = []
+            for m, t in enumerate(ms):
+                if t.shape[0] != 32 * G or not t.is_contiguous():
+                    raise ValueError(f"layer {l} matrix {m}: need a contiguous tensor of {32 * G} rows")
+                gb = t.numel() * t.element_size() // G
+                if l == 0:
+                    self.group_bytes.append(gb)
+                elif gb != self.group_bytes[m]:
+                    raise ValueError(f"layer {l} matrix {m}: group size differs from layer 0")
+                row.append(torch.zeros((32 * K,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev))
+            self.region.append(row)
+        self.src = torch.tensor([[t.data_ptr() for t in ms] for ms in mats], dtype=torch.int64, device=dev)
+        self.dst = torch.tensor([[t.data_ptr() for t in r] for r in self.region], dtype=torch.int64, device=dev)
+        self._mats = mats                      # keeps the sources alive
+
+    def update(self, entered: torch.Tensor, left: torch.Tensor, stream=None):
+        A.sfx_hot_update(self.G, self.K, entered, left, self.slot_of, self.group_of, self.copies,
+                         self.ncopies, self.group_bytes, self.src, self.dst, stream=stream)
+
+
 class StackStep:
     """All layers of a stack run by one fused multi-layer kernel per step: the exact
     step (sfx_ffn_step) or, with `pipeline=True`, the Live Pipeline step

@@ -58,6 +58,8 @@ def parse():
                    help="store the predictor (W1, W2) in int4 g32 with fp16 scales (separate calls)")
     p.add_argument("--stream-probe", type=int, default=0, metavar="MIB",
                    help="only run the streaming-read probe over MIB MiB (5 reads) and print its bandwidth")
+    p.add_argument("--churn", action="store_true",
+                   help="only the hot-region churn study (Falcon-40B-shaped layers, TAM vs Top-K)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the calibration of HBM byte counters")
     return p.parse_args()
@@ -342,6 +344,85 @@ def stream_probe(dev, mib=2048, reps=5):
             "GBps": round(n / (us * 1e-6) / 1e9, 1)}
 
 
+def hot_region_churn(dev, L=4, B=1, steps=512):
+    """Churn of the hot region on the Falcon-40B-shaped layers (1024 groups of 32,
+    K = 256 hot slots, 512 AR(1) decode steps): the layers' own union masks feed
+    TAM at each lambda and the Top-K rule on the current step alone; each rule
+    keeps its own hot region of W_up, bias and W_down group rows (sfx_hot_update).
+    Reports groups and bytes copied per layer-step, the copy kernel's time and
+    bandwidth, and how many of a step's active neurons fall in groups the rule
+    made hot at the step before."""
+    import torch
+    import synthetic as S
+    from activation_sparse_ffn_amd import HotRegion, StepBuffers, TamState, TopKNowState, run_layer
+    cfg = S.CONFIGS["C5"]
+    G, K, eps = cfg.groups, cfg.tam["K"], cfg.tam["eps"]
+    say(f"hot-region churn: generating {L} layers of {cfg.workload}")
+    layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
+    xs = [S.make_tokens(cfg, l, steps, B, device=dev) for l in range(L)]
+    ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
+    bufs = [StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pred_storage, device=dev, union_bits=ubits[l])
+            for l in range(L)]
+    mats = [[ly.Wa, ly.ba, ly.Wd] for ly in layers]
+    rules = [("tam", lam) for lam in cfg.tam["lambdas"]] + [("topk_now", None)]
+    states, regions = [], []
+    for kind, lam in rules:
+        states.append(TamState(L, G, K, device=dev) if kind == "tam" else TopKNowState(L, G, K, device=dev))
+        regions.append(HotRegion(mats, G, K, device=dev))
+    group_bytes = sum(regions[0].group_bytes)
+    n_rules = len(rules)
+    copied = torch.zeros(n_rules, dtype=torch.int64, device=dev)
+    covered = torch.zeros(n_rules, dtype=torch.int64, device=dev)
+    active = torch.zeros((), dtype=torch.int64, device=dev)
+    shifts = torch.arange(32, device=dev, dtype=torch.int64)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+           for _ in range(n_rules)]
+    for s in range(steps):
+        for l in range(L):
+            run_layer(bufs[l], layers[l].tensors(), xs[l][s], layers[l].threshold, cfg.act, tok_bits=False)
+        cnt = popcount32(ubits)                                        # [L][G] active neurons per group
+        if s > 0:
+            active += cnt.sum()
+        for r, (kind, lam) in enumerate(rules):
+            st, hr = states[r], regions[r]
+            if s > 0:                                                  # hot set chosen at the step before
+                hot = ((st.hot.to(torch.int64).unsqueeze(-1) >> shifts) & 1).reshape(L, -1)[:, :G]
+                covered[r] += (cnt * hot).sum()
+            if kind == "tam":
+                st.update(ubits, lam, eps)
+            else:
+                st.update(ubits)
+            evs[r][s][0].record()
+            hr.update(st.entered, st.left)
+            evs[r][s][1].record()
+            copied[r] += hr.ncopies.sum()
+        if s % 128 == 0:
+            say(f"hot-region churn: step {s}")
+    torch.cuda.synchronize()
+    for b in bufs:
+        b.check_status()
+    out = {"workload": cfg.workload, "layers": L, "batch": B, "steps": steps, "groups": G, "K": K,
+           "group_bytes": group_bytes, "rules": {}}
+    tot_active = int(active.item())
+    for r, (kind, lam) in enumerate(rules):
+        n = int(copied[r].item())
+        us = np.array([a.elapsed_time(b) for a, b in evs[r]]) * 1e3
+        name = f"tam_lambda_{lam}" if kind == "tam" else "topk_current_step"
+        out["rules"][name] = {
+            "groups_copied_per_layer_step": round(n / (L * steps), 3),
+            "MB_copied_per_layer_step": round(n * group_bytes / (L * steps) / 1e6, 3),
+            "next_step_coverage": round(int(covered[r].item()) / max(tot_active, 1), 4),
+            "copy_us_per_step": round(float(us.mean()), 2),
+            "copy_GBps": round(2 * n * group_bytes / max(float(us.sum()) * 1e-6, 1e-12) / 1e9, 1),
+        }
+    base = out["rules"]["topk_current_step"]["groups_copied_per_layer_step"]
+    for name, v in out["rules"].items():
+        if name.startswith("tam"):
+            v["topk_copies_over_tam"] = round(base / v["groups_copied_per_layer_step"], 3) \
+                if v["groups_copied_per_layer_step"] > 0 else None
+    return out
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -446,6 +527,9 @@ def main():
     if args.stream_probe:
         print(json.dumps(stream_probe(dev, args.stream_probe)), flush=True)
         return
+    if args.churn:
+        print(json.dumps(hot_region_churn(dev)), flush=True)
+        return
 
     def mode_for(cfg, B, pipeline):
         if pipeline:
@@ -516,6 +600,8 @@ def main():
             torch.cuda.empty_cache()
         extra["live_pipeline"] = pipes
         extra["stream_read_ceiling"] = stream_probe(dev)
+        extra["tam_hot_region"] = hot_region_churn(dev)
+        torch.cuda.empty_cache()
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)

@@ -11,6 +11,7 @@
  *   sfx_sparse_up    hact   = act(Wa[i] x + b_i) (ReLU / ReGLU) active rows only
  *   sfx_sparse_down  y      = sum_j hact_j Wd[idx_j]            active rows only
  *   sfx_tam_update   per-group momentum score and hot set       once per step, all layers
+ *   sfx_hot_update   hot region slots + copy of entering groups  once per step, all layers
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a caller-owned DEVICE pointer unless the comment
@@ -258,6 +259,63 @@ int sfx_tam_update(void* stream, int L, int G, const uint32_t* union_bits,
                    float* score, uint32_t* hot_bits, uint32_t* entered_bits,
                    uint32_t* left_bits, int32_t* topk, int32_t* topk_count,
                    void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_topk_now_update -- the reload rule TAM is compared with (KAIROX page,
+ * Experiments: strategies and ablations, static TAM against Top-K): the hot set is
+ * the groups most active in this step alone, with no memory of earlier steps.
+ *
+ *   n_g   = popcount(union_bits[l][g])                    neurons of g active now
+ *   cand  = { g : n_g > 0 }
+ *   topk  = first min(K, |cand|) of cand ranked by n desc, then g asc
+ *   hot'  = topk;  entered = hot' & ~hot;  left = hot & ~hot'
+ *
+ * Arguments as sfx_tam_update without the score state (L, G, K, union_bits,
+ * hot_bits, entered_bits, left_bits, topk, topk_count).  Same error behaviour.
+ * ------------------------------------------------------------------------------- */
+int sfx_topk_now_update(void* stream, int L, int G, const uint32_t* union_bits, int K,
+                        uint32_t* hot_bits, uint32_t* entered_bits, uint32_t* left_bits,
+                        int32_t* topk, int32_t* topk_count);
+
+/* ---------------------------------------------------------------------------------
+ * sfx_hot_update -- keeps the hot set's groups in a contiguous hot region of K group
+ * slots per layer and copies only the groups that enter it (KAIROX page, Core
+ * method: item 3, weights of co-active neurons stored together so that a group
+ * moves as one contiguous block; item 4, the hot set fills the capacity; item 6,
+ * only the set difference moves).  On one GPU the copy stands in for the reload a
+ * CPU-GPU system pays, and its bytes measure the churn of the rule that chose the
+ * hot set.  One call updates L layers:
+ *
+ *   1. each group g in left_bits frees its slot: group_of[slot_of[g]] = -1,
+ *      slot_of[g] = -1;
+ *   2. the free slots F (group_of[s] == -1), ascending, go to the groups E of
+ *      entered_bits, ascending: slot_of[E_i] = F_i, group_of[F_i] = E_i, and
+ *      copies[l][i] = {E_i, F_i}, for i < ncopies[l] = min(|E|, |F|);
+ *   3. for every copy and every matrix m < nmat, group_bytes[m] bytes move from
+ *      src[l][m] + E_i * group_bytes[m] to dst[l][m] + F_i * group_bytes[m].
+ *
+ * When entered_bits / left_bits come from one sequence of hot sets of at most K
+ * groups (sfx_tam_update or sfx_topk_now_update with the same K), every entering
+ * group finds a slot and group_of lists exactly the hot set.  Otherwise entering
+ * groups past the free slots get slot -1 and no copy.
+ *
+ *   L, G, K        layers (1..1024), groups per layer (1..SFX_MAX_GROUPS), slots (1..G).
+ *   entered_bits, left_bits  [L][ceil(G/32)] uint32 (bit g % 32 of word g / 32).
+ *   slot_of        [L][G] int32 state, in/out (start at -1).
+ *   group_of       [L][K] int32 state, in/out (start at -1).
+ *   copies         [L][K][2] int32, written (entries past ncopies[l] untouched).
+ *   ncopies        [L] int32, written.
+ *   nmat           matrices per layer, 0..8 (0: slots only, no copy).
+ *   group_bytes    host array [nmat]: bytes of one group in matrix m, a positive
+ *                  multiple of 16 (at most 16 GiB summed over the matrices).
+ *   src, dst       device arrays [L * nmat] of device pointers (16-byte aligned):
+ *                  matrix m of layer l holds G groups (src) and K groups (dst).
+ * ------------------------------------------------------------------------------- */
+int sfx_hot_update(void* stream, int L, int G, int K,
+                   const uint32_t* entered_bits, const uint32_t* left_bits,
+                   int32_t* slot_of, int32_t* group_of, int32_t* copies, int32_t* ncopies,
+                   int nmat, const size_t* group_bytes,
+                   const void* const* src, void* const* dst);
 
 /* ---------------------------------------------------------------------------------
  * sfx_ffn_step -- the whole step for L layers in one launch: for each layer in order,

@@ -25,6 +25,12 @@ Functions and the passages they follow:
                 exceed tau = (1 - lambda) + eps; the highest-scoring candidates fill
                 the capacity K.  Item 3 (§5.2): decisions are per group of 32.
                 Item 6 (§8): entering / leaving sets are set differences.
+  topk_now_update  KAIROX page, Experiments, strategies and ablations: the Top-K
+                reload rule TAM is compared with -- the groups most active in this
+                step alone (count of active neurons), no memory.
+  hot_assign, hot_copy  KAIROX page, Core method, items 3 and 6: a contiguous hot
+                region of K group slots; leaving groups free their slots and only
+                entering groups are copied in.
   dense_ffn     the dense layer the sparse step reproduces when every neuron with
                 a nonzero activation is in the active set (used only by the pins).
   ffn_step      the four steps in order; with a separate predictor input xp it is
@@ -254,3 +260,53 @@ def tam_update(score: np.ndarray, prev_hot: np.ndarray, union_words: np.ndarray,
     score = lam * np.asarray(score, dtype=F64) + (1.0 - lam) * a
     topk, hot, entered, left = tam_select(score, prev_hot, tam_tau(lam, eps), K)
     return score, topk, hot, entered, left
+
+
+def topk_now_update(prev_hot: np.ndarray, union_words: np.ndarray, K: int):
+    """The Top-K reload rule TAM is compared with (KAIROX page, Experiments:
+    strategies and ablations): hot = the K groups with the most active neurons in
+    this step's union mask (at least one), ranked by that count descending, then
+    group id ascending; no memory of earlier steps.
+    Returns (topk int32, hot, entered, left)."""
+    w = np.ascontiguousarray(union_words, dtype=np.uint32)
+    count = np.unpackbits(w.view(np.uint8)).reshape(-1, 32).sum(axis=1)     # popcount per word
+    cand = np.flatnonzero(count > 0)
+    order = cand[np.lexsort((cand, -count[cand]))]
+    topk = order[:K].astype(np.int32)
+    hot = np.zeros(w.shape[0], dtype=bool)
+    hot[topk] = True
+    prev_hot = np.asarray(prev_hot, dtype=bool)
+    return topk, hot, hot & ~prev_hot, prev_hot & ~hot
+
+
+# ----------------------------------------------------------------------------- hot region
+
+def hot_assign(slot_of: np.ndarray, group_of: np.ndarray, entered: np.ndarray, left: np.ndarray):
+    """Slot bookkeeping of the hot region of one layer (KAIROX page, Core method:
+    item 3, a group moves as one contiguous block; item 6, only the set difference
+    moves).  slot_of [G] / group_of [K] int (-1 = none) are updated in place:
+    leaving groups free their slots; then the entering groups in ascending order
+    take the free slots in ascending order.  Returns the copies [(group, slot)]."""
+    for g in np.flatnonzero(left):
+        s = int(slot_of[g])
+        if s >= 0:
+            group_of[s] = -1
+        slot_of[g] = -1
+    free = [s for s in range(group_of.shape[0]) if group_of[s] < 0]
+    copies = []
+    for i, g in enumerate(np.flatnonzero(entered)):
+        if i < len(free):
+            slot_of[g] = free[i]
+            group_of[free[i]] = g
+            copies.append((int(g), free[i]))
+        else:
+            slot_of[g] = -1
+    return copies
+
+
+def hot_copy(region: np.ndarray, src: np.ndarray, copies):
+    """Applies the copies to one matrix's hot region: slot s of `region` (32 rows
+    per group, any row width) receives group g's 32 rows of `src`."""
+    for g, s in copies:
+        region[32 * s:32 * s + 32] = src[32 * g:32 * g + 32]
+    return region

@@ -187,3 +187,28 @@ def test_predict_q4_validation(lib):
     assert call(W1=ODD) == E_ALIGN
     assert call(s1=P(0x10001)) == E_ALIGN
     assert call(wsn=ws_n - 1) == E_WORKSPACE
+
+
+def test_topk_now_validation(lib):
+    call = lambda **k: lib.sfx_topk_now_update(None, k.get("L", 1), k.get("G", 1024), GOOD, k.get("K", 256),
+                                               GOOD, GOOD, GOOD, k.get("topk", GOOD), k.get("cnt", GOOD))
+    assert call(G=1025) == E_SHAPE and call(G=0) == E_SHAPE and call(L=0) == E_SHAPE
+    assert call(K=1025) == E_SHAPE and call(K=-1) == E_SHAPE
+    assert call(topk=None) == E_NULL and call(cnt=None) == E_NULL
+
+
+def test_hot_update_validation(lib):
+    sizes = (ctypes.c_size_t * 3)(4096, 128, 1536)
+    bad = (ctypes.c_size_t * 3)(4096, 8, 1536)             # 8 is not a multiple of 16
+    zero = (ctypes.c_size_t * 3)(4096, 0, 1536)
+
+    def call(**k):
+        return lib.sfx_hot_update(None, k.get("L", 2), k.get("G", 1024), k.get("K", 256), GOOD, GOOD,
+                                  k.get("slot", GOOD), GOOD, GOOD, GOOD, k.get("nmat", 3), k.get("gb", sizes),
+                                  k.get("src", GOOD), k.get("dst", GOOD))
+    assert call(K=0) == E_SHAPE and call(K=1025) == E_SHAPE and call(G=1025) == E_SHAPE
+    assert call(nmat=9) == E_SHAPE and call(nmat=-1) == E_SHAPE
+    assert call(gb=bad) == E_SHAPE and call(gb=zero) == E_SHAPE
+    assert call(slot=None) == E_NULL and call(src=None) == E_NULL and call(gb=None) == E_NULL
+    assert call(slot=P(0x10002)) == E_ALIGN
+    assert call(dst=P(0x10004)) == E_ALIGN                  # the pointer arrays need 8-byte alignment

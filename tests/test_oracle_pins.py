@@ -343,3 +343,80 @@ def test_predictor_weights_int4():
     x[0, 3] = 2.0                          # hidden[1] = relu(3.5 * 2) = 7, hidden[0] = 0
     s = O.predict(x, W1, W2)
     assert s[0, 5] == 14.0 and np.count_nonzero(s) == 1
+
+
+# ----------------------------------------------------------------------------- Top-K rule, hot region
+
+def test_topk_now_hand_case():
+    """topk_now_update ranks by the number of active neurons this step (popcount
+    of the union word), ties by group id, and needs at least one active neuron.
+    Words (1, 0b111, 0, 0b11, 0b101): counts (1, 3, 0, 2, 2) -> K = 3 picks
+    (1, 3, 4); a ranking by 'any active' (ids 0, 1, 3) or by word value (1, 4, 3)
+    fails.  Previous hot {0, 3} -> entered {1, 4}, left {0}."""
+    w = np.array([1, 0b111, 0, 0b11, 0b101], np.uint32)
+    prev = np.array([1, 0, 0, 1, 0], bool)
+    topk, hot, ent, left = O.topk_now_update(prev, w, 3)
+    assert topk.tolist() == [1, 3, 4]
+    assert np.flatnonzero(ent).tolist() == [1, 4] and np.flatnonzero(left).tolist() == [0]
+    topk, hot, _, _ = O.topk_now_update(prev, np.zeros(5, np.uint32), 3)
+    assert topk.size == 0 and not hot.any()
+    topk, _, _, _ = O.topk_now_update(prev, np.full(5, 0xFFFFFFFF, np.uint32), 2)
+    assert topk.tolist() == [0, 1]
+
+
+def test_hot_assign_hand_case():
+    """hot_assign over three hand-worked steps with K = 3 slots and G = 6:
+    step 1 enters {4, 1} -> 1 takes slot 0, 4 slot 1; step 2 enters {0, 5} and
+    {1} leaves -> free slots (0, 2) go to 0 and 5; step 3: {4} leaves, {2}
+    enters -> slot 1.  A descending fill, a free list that is not ascending, or a
+    leaving group that keeps its slot all fail."""
+    G, K = 6, 3
+    slot_of = np.full(G, -1)
+    group_of = np.full(K, -1)
+
+    def bits(ids):
+        b = np.zeros(G, bool)
+        b[list(ids)] = True
+        return b
+
+    c = O.hot_assign(slot_of, group_of, bits([4, 1]), bits([]))
+    assert c == [(1, 0), (4, 1)] and group_of.tolist() == [1, 4, -1]
+    c = O.hot_assign(slot_of, group_of, bits([0, 5]), bits([1]))
+    assert c == [(0, 0), (5, 2)] and group_of.tolist() == [0, 4, 5]
+    assert slot_of.tolist() == [0, -1, -1, -1, 1, 2]
+    c = O.hot_assign(slot_of, group_of, bits([2]), bits([4]))
+    assert c == [(2, 1)] and group_of.tolist() == [0, 2, 5]
+    assert slot_of.tolist() == [0, -1, 1, -1, -1, 2]
+
+
+def test_hot_region_invariants_over_tam_sequence():
+    """Over 200 TAM steps on random activity: the region's occupied slots hold
+    exactly the hot set, slot_of and group_of are inverse maps, a group that stays
+    hot never moves, the copies are exactly the entering groups, and the region
+    of a matrix equals the brute-force gather src[group_of[s]] slot by slot."""
+    rng = np.random.default_rng(11)
+    G, K, lam, eps = 40, 9, 0.8, 0.01
+    src = rng.integers(0, 2 ** 16, size=(32 * G, 3))
+    region = np.zeros((32 * K, 3), src.dtype)
+    score = np.zeros(G)
+    hot = np.zeros(G, bool)
+    slot_of = np.full(G, -1)
+    group_of = np.full(K, -1)
+    act = rng.random(G) < 0.3
+    for _ in range(200):
+        act = np.where(rng.random(G) < 0.8, act, rng.random(G) < 0.3)
+        words = np.where(act, rng.integers(1, 2 ** 32, G), 0).astype(np.uint32)
+        before = slot_of.copy()
+        score, _, hot_new, ent, left = O.tam_update(score, hot, words, lam, eps, K)
+        copies = O.hot_assign(slot_of, group_of, ent, left)
+        O.hot_copy(region, src, copies)
+        assert sorted(g for g, _ in copies) == np.flatnonzero(ent).tolist()
+        assert set(group_of[group_of >= 0].tolist()) == set(np.flatnonzero(hot_new).tolist())
+        for s in range(K):
+            if group_of[s] >= 0:
+                assert slot_of[group_of[s]] == s
+                assert np.array_equal(region[32 * s:32 * s + 32], src[32 * group_of[s]:32 * group_of[s] + 32])
+        stay = hot & hot_new
+        assert np.array_equal(slot_of[stay], before[stay])
+        assert np.all(slot_of[~hot_new] == -1)
+        hot = hot_new
