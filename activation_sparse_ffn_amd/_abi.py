@@ -24,7 +24,8 @@ EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict",
            "sfx_compact", "sfx_sparse_up", "sfx_sparse_down_ws", "sfx_sparse_down", "sfx_tam_ws",
            "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
            "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read", "sfx_predict_q4",
-           "sfx_topk_now_update", "sfx_hot_update")
+           "sfx_topk_now_update", "sfx_hot_update", "sfx_count_active", "sfx_select_kth_ws",
+           "sfx_select_kth", "sfx_hot_first_order_ws", "sfx_hot_first_order", "sfx_gather_rows")
 HOT_MAX_MATS = 8
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
@@ -87,6 +88,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_topk_now_update.argtypes = [P, I, I, P, I, P, P, P, P, P]
     lib.sfx_hot_update.restype = I
     lib.sfx_hot_update.argtypes = [P, I, I, I, P, P, P, P, P, P, I, P, P, P]
+    lib.sfx_count_active.restype = I
+    lib.sfx_count_active.argtypes = [P, I, I, P, P]
+    lib.sfx_select_kth_ws.restype = Z
+    lib.sfx_select_kth_ws.argtypes = []
+    lib.sfx_select_kth.restype = I
+    lib.sfx_select_kth.argtypes = [P, Z, P, Z, P, P, Z]
+    lib.sfx_hot_first_order_ws.restype = Z
+    lib.sfx_hot_first_order_ws.argtypes = [I]
+    lib.sfx_hot_first_order.restype = I
+    lib.sfx_hot_first_order.argtypes = [P, I, P, P, P, P, Z]
+    lib.sfx_gather_rows.restype = I
+    lib.sfx_gather_rows.argtypes = [P, I, I, Z, P, P, P]
     lib.sfx_ffn_step_ws.restype = Z
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
@@ -300,6 +313,44 @@ def sfx_hot_update(G, K, entered_bits, left_bits, slot_of, group_of, copies, nco
                                gb if nmat > 0 else None, _ptr(src) if nmat > 0 else None,
                                _ptr(dst) if nmat > 0 else None)
     _check(st, "sfx_hot_update")
+
+
+# ------------------------------------------------------------------------- calibration
+
+def sfx_count_active(tok_bits, f, counts, stream=None):
+    """counts [f] int32 += active tokens per neuron; tok_bits [B][ceil(f/32)]."""
+    B = tok_bits.shape[0]
+    _check(load().sfx_count_active(_stream(stream), B, int(f), _ptr(tok_bits), _ptr(counts)), "sfx_count_active")
+
+
+def sfx_select_kth(values, k, out, ws=None, stream=None):
+    """out[0] = k-th smallest (0-based) of the fp32 values, exact."""
+    _need(values, torch.float32, "values")
+    if ws is None:
+        ws = workspace(load().sfx_select_kth_ws(), values.device)
+    st = load().sfx_select_kth(_stream(stream), values.numel(), _ptr(values), int(k), _ptr(out), _ptr(ws),
+                               ws.numel())
+    _check(st, "sfx_select_kth")
+
+
+def sfx_hot_first_order(counts, perm, group=None, ws=None, stream=None):
+    """perm [f] int32 = hot-first neuron table from counts [f] (and group ids)."""
+    f = counts.numel()
+    if group is not None and ws is None:
+        ws = workspace(load().sfx_hot_first_order_ws(f), counts.device)
+    st = load().sfx_hot_first_order(_stream(stream), f, _ptr(counts), _ptr(group), _ptr(perm), _ptr(ws),
+                                    ws.numel() if ws is not None else 0)
+    _check(st, "sfx_hot_first_order")
+
+
+def sfx_gather_rows(src, idx, dst, stream=None):
+    """dst row r = src row idx[r]; rows along the first dimension."""
+    if src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:] or dst.shape[0] != idx.numel():
+        raise ValueError("dst must be [len(idx)] + src row shape, same dtype")
+    row_bytes = src[0].numel() * src.element_size()
+    st = load().sfx_gather_rows(_stream(stream), dst.shape[0], src.shape[0], row_bytes, _ptr(src), _ptr(idx),
+                                _ptr(dst))
+    _check(st, "sfx_gather_rows")
 
 
 # ------------------------------------------------------------------------- fused step

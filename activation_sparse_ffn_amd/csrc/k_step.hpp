@@ -329,6 +329,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   if (threadIdx.x == 0) s_grp = 0u;
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
+  int k_prev = -1;                           // active neurons of the previous layer
   Raw<16> w1r[kU];
   prefetch_w1<kU>(p, (CLayer*)p.layers, w1r);
   prefetch_w2(p, (CLayer*)p.layers, s_w2);
@@ -580,9 +581,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     };
     // Up rows first, for this workgroup's own active neurons: the union bits of its
     // mask words w + P m (still in s_words), so no exchange is waited for; at most
-    // kOwnCap of them (two rounds of the waves).  A workgroup whose words are dense
-    // (co-activated groups of 32 are stored together) leaves the rest to the even
-    // split below, after the union exchange.
+    // `cap` of them: twice the previous layer's even share ceil(k / P), at least one
+    // round of the waves and at most kOwnCap (two rounds; kOwnCap for the first
+    // layer).  These rows overlap the union exchange.  A workgroup whose words are
+    // dense (hot-first storage puts the most active neurons in the first words)
+    // leaves the rest to the split below, after the union exchange.
+    const int cap = k_prev < 0 ? kOwnCap : min(kOwnCap, max(kWork, 2 * ((k_prev + P - 1) / P)));
     {
       const int nw2 = w < W ? (W - w + P - 1) / P : 0;
       auto own_word = [&](int m) {
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       };
       int own_k = 0;
       for (int m = 0; m < nw2; ++m) own_k += __popc(own_word(m));
-      const int own_n = min(own_k, kOwnCap);
+      const int own_n = min(own_k, cap);
       for (int e = wave; e < own_n; e += kWork) {
         // entry e of the own list: word m, its rem-th set bit
         int m = 0, rem = e;
@@ -627,13 +631,15 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     const uint32_t w1 = wpt == 2 && g0 + 1 < W ? s_uw[g0 + 1] : 0u;
     const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
     // the same scan also counts, per owner o = tid < P, its own entries past
-    // kOwnCap (the rows the even split below takes over): both counts fit in 16
-    // bits (k <= f <= 32 kMaxWords), so they are scanned packed in one word
+    // `cap` (the rows the split below takes over): both counts fit in 16 bits
+    // (k <= f <= 32 kMaxWords), so they are scanned packed in one word
     uint32_t ovc = 0;
+    uint32_t* s_own = reinterpret_cast<uint32_t*>(s_red) + 512;   // [P] own rows done first
     if (tid < P) {
       uint32_t c = 0;
       for (int g = tid; g < W; g += P) c += __popc(s_uw[g]);
-      ovc = c > (uint32_t)kOwnCap ? c - (uint32_t)kOwnCap : 0u;
+      ovc = c > (uint32_t)cap ? c - (uint32_t)cap : 0u;
+      s_own[tid] = c - ovc;
     }
     const uint32_t pk = cnt | (ovc << 16);
     uint32_t inc = pk;
@@ -660,6 +666,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
     if (tid == 0) s_pref[W] = total;
     k = (int)total;
+    k_prev = k;
     in_lds = k <= kNidCap;
     if (in_lds) {
       uint32_t pos = base;
@@ -670,19 +677,28 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
     if (w == 0 && tid == 0) *Ld->count = k;
     lds_barrier();
-    // Own entries past kOwnCap of every workgroup (owner o: the set bits of words
-    // o + P m in order, from entry kOwnCap on), split evenly over the workgroups
-    // by the owner prefix s_ovp from the scan above.
+    // Own entries past `cap` of every workgroup (owner o: the set bits of words
+    // o + P m in order, from entry cap on), ranked by owner through the prefix
+    // s_ovp from the scan above, fill the workgroups up to T = ceil(k / P) rows
+    // each: workgroup w takes the T - own_w overflow ranks after those of
+    // workgroups 0..w-1 (each wave sums the deficits before w itself).  Since
+    // P T >= k the deficits cover every overflow rank, and no workgroup does more
+    // than max(T, cap) up rows.
     {
       const int nov = (int)s_ovp[P];             // overflow rows of all workgroups
-      const int q0 = (int)(((long long)nov * w) / P), q1 = (int)(((long long)nov * (w + 1)) / P);
+      const int fair = (k + P - 1) / P;          // T
+      int dsum = 0;
+      for (int o = lane; o < w; o += kWave) dsum += max(fair - (int)s_own[o], 0);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, kWave);
+      const int q0 = min(dsum, nov), q1 = min(dsum + max(fair - (int)s_own[w], 0), nov);
       for (int r = q0 + wave; r < q1; r += kWork) {
         int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if ((int)s_ovp[mid] <= r) lo = mid; else hi = mid;
         }
-        int m = 0, rem = kOwnCap + (r - (int)s_ovp[lo]);
+        int m = 0, rem = cap + (r - (int)s_ovp[lo]);
         uint32_t um = s_uw[lo];
         while (rem >= __popc(um)) { rem -= __popc(um); um = s_uw[lo + P * (++m)]; }
         for (int i = 0; i < rem; ++i) um &= um - 1;

@@ -249,6 +249,44 @@ int sfx_hot_update(void* stream, int L, int G, int K, const uint32_t* entered_bi
   return launch_status(e);
 }
 
+// ------------------------------------------------------------------------------ calibration
+
+int sfx_count_active(void* stream, int B, int f, const uint32_t* tok_bits, int32_t* counts) {
+  if (B < 1 || B > SFX_MAX_B || f < 1) return SFX_E_SHAPE;
+  if (!tok_bits || !counts) return SFX_E_NULL;
+  if (!aligned4(tok_bits) || !aligned4(counts)) return SFX_E_ALIGN;
+  return launch_status(sfx::launch_count_active((hipStream_t)stream, B, f, tok_bits, counts));
+}
+
+size_t sfx_select_kth_ws(void) { return sfx::select_ws_bytes(); }
+
+int sfx_select_kth(void* stream, size_t n, const float* values, size_t k, float* out, void* ws, size_t ws_bytes) {
+  if (n < 1 || n > (size_t)0xFFFFFFFFu || k >= n) return SFX_E_SHAPE;
+  if (!values || !out) return SFX_E_NULL;
+  if (!aligned4(values) || !aligned4(out)) return SFX_E_ALIGN;
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < sfx::select_ws_bytes()) return SFX_E_WORKSPACE;
+  return launch_status(sfx::launch_select_kth((hipStream_t)stream, n, values, k, out, ws));
+}
+
+size_t sfx_hot_first_order_ws(int f) { return f < 1 ? 0 : sfx::order_ws_bytes(f); }
+
+int sfx_hot_first_order(void* stream, int f, const int32_t* counts, const int32_t* group, int32_t* perm, void* ws,
+                        size_t ws_bytes) {
+  if (f < 1 || f > (1 << 24)) return SFX_E_SHAPE;
+  if (!counts || !perm) return SFX_E_NULL;
+  if (!aligned4(counts) || !aligned4(perm) || (group && !aligned4(group))) return SFX_E_ALIGN;
+  if (group && (!ws || ((uintptr_t)ws & 255u) || ws_bytes < sfx::order_ws_bytes(f))) return SFX_E_WORKSPACE;
+  return launch_status(sfx::launch_hot_first_order((hipStream_t)stream, f, counts, group, perm, ws));
+}
+
+int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const void* src, const int32_t* idx,
+                    void* dst) {
+  if (n_dst < 1 || n_src < 1 || row_bytes == 0 || (row_bytes & 3u)) return SFX_E_SHAPE;
+  if (!src || !idx || !dst) return SFX_E_NULL;
+  if (!aligned4(src) || !aligned4(idx) || !aligned4(dst)) return SFX_E_ALIGN;
+  return launch_status(sfx::launch_gather_rows((hipStream_t)stream, n_dst, n_src, row_bytes, src, idx, dst));
+}
+
 // ------------------------------------------------------------------------------ fused step
 
 size_t sfx_ffn_step_ws(int wdt, int act, int B, int d, int h, int f) {

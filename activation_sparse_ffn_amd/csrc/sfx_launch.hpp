@@ -49,6 +49,15 @@ hipError_t launch_tam(hipStream_t s, int L, int G, const uint32_t* union_bits, f
 hipError_t launch_topk_now(hipStream_t s, int L, int G, const uint32_t* union_bits, int K, uint32_t* hot_bits,
                            uint32_t* entered, uint32_t* left, int32_t* topk, int32_t* topk_count);
 
+hipError_t launch_count_active(hipStream_t s, int B, int f, const uint32_t* tok_bits, int32_t* counts);
+size_t select_ws_bytes();
+hipError_t launch_select_kth(hipStream_t s, size_t n, const float* v, size_t k, float* out, void* ws);
+size_t order_ws_bytes(int f);
+hipError_t launch_hot_first_order(hipStream_t s, int f, const int32_t* counts, const int32_t* group, int32_t* perm,
+                                  void* ws);
+hipError_t launch_gather_rows(hipStream_t s, int n_dst, int n_src, size_t row_bytes, const void* src,
+                              const int32_t* idx, void* dst);
+
 constexpr int kHotMaxMats = 8;
 constexpr int kHotMaxLayers = 1024;
 constexpr int kHotChunk = 16384;         // bytes per work item of the copy kernel

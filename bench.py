@@ -58,6 +58,9 @@ def parse():
                    help="store the predictor (W1, W2) in int4 g32 with fp16 scales (separate calls)")
     p.add_argument("--stream-probe", type=int, default=0, metavar="MIB",
                    help="only run the streaming-read probe over MIB MiB (5 reads) and print its bandwidth")
+    p.add_argument("--no-calib", action="store_true",
+                   help="use the generator's hot-first layers and closed-form thresholds instead of "
+                        "raw-order layers calibrated on the device")
     p.add_argument("--churn", action="store_true",
                    help="only the hot-region churn study (Falcon-40B-shaped layers, TAM vs Top-K)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -132,6 +135,47 @@ def popcount32(t):
     return ((u.unsqueeze(-1) >> sh) & 1).sum(-1)
 
 
+N_CAL = 1024
+
+
+def calibrated_layer(cfg, layer, dev, n_cal=N_CAL):
+    """The offline calibration pass on a raw-order layer: thresholds at the
+    configured density, activation counts and the hot-first table, from n_cal
+    calibration tokens (a token stream disjoint from the measured one), then every
+    per-neuron row reordered.  Returns (calibrated layer, calibration summary)."""
+    import dataclasses
+    import synthetic as S
+    from activation_sparse_ffn_amd.calib import apply_order, calibrate_layer
+    toks = S.make_tokens(cfg, layer.index, n_cal, 1, device=dev, tag="calib")[:, 0]
+    r = calibrate_layer(layer.tensors(), toks, cfg.density, group=layer.group)
+    t = dict(layer.tensors())
+    if layer.group is not None:
+        t["group"] = layer.group
+    c = apply_order(t, r["perm"])
+    perm = r["perm"].cpu().numpy()
+    keys = ("W2", "W2_s", "Wa", "Wa_s", "Wl", "Wl_s", "Wd", "Wd_s", "ba", "perm", "group")
+    new = dataclasses.replace(layer, threshold=r["threshold"], p=layer.p[perm], **{k: c.get(k) for k in keys})
+    return new, {"threshold": r["threshold"], "active_share": r["active_share"]}
+
+
+def make_stack(cfg, L, dev, calibrate=True):
+    """L layers of the configuration: raw-order layers calibrated on the device, or
+    (calibrate=False) the generator's own hot-first layers with closed-form thresholds."""
+    import synthetic as S
+    if not calibrate:
+        return [S.make_layer(cfg, l, device=dev) for l in range(L)], None
+    layers, cal = [], []
+    for l in range(L):
+        ly, c = calibrated_layer(cfg, S.make_layer(cfg, l, device=dev, order="raw"), dev)
+        layers.append(ly)
+        cal.append(c)
+    th = np.array([c["threshold"] for c in cal])
+    sh = np.array([c["active_share"] for c in cal])
+    return layers, {"tokens_per_layer": N_CAL, "threshold_mean": round(float(th.mean()), 5),
+                    "threshold_min": round(float(th.min()), 5), "threshold_max": round(float(th.max()), 5),
+                    "calibration_active_share": round(float(sh.mean()), 5)}
+
+
 class Workload:
     """One stack of synthetic layers and the step that is timed on it."""
 
@@ -147,7 +191,7 @@ class Workload:
         self.tam_k = max(1, G // 4) if cfg.tam is None else cfg.tam["K"]
         self.tam_args = (args.tam_lambda, args.tam_eps)
         say(f"generating {L} layers of {cfg.workload} ({mode}, batch {B})")
-        self.layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
+        self.layers, self.calibration = make_stack(cfg, L, dev, calibrate=not args.no_calib)
         if mode == "pipeline":
             self.xs = S.make_layer_chain(cfg, L, W + K, B, device=dev)
         else:
@@ -295,6 +339,7 @@ def time_workload(wl, roofline_steps):
 
 def summary(wl, r):
     return {"workload": wl.cfg.workload, "batch": wl.B, "layers": wl.L, "path": wl.mode,
+            "calibrated": wl.calibration is not None,
             "us_per_layer_step": round(r["ms_step"] * 1e3 / wl.L, 3),
             "tokens_per_s_per_layer": round(wl.B * wl.L / (r["ms_step"] * 1e-3), 1),
             "effective_GBps": round(r["gbps"], 1), "hbm_frac": round(r["gbps"] / PEAK_HBM_GBPS, 4),
@@ -358,7 +403,7 @@ def hot_region_churn(dev, L=4, B=1, steps=512):
     cfg = S.CONFIGS["C5"]
     G, K, eps = cfg.groups, cfg.tam["K"], cfg.tam["eps"]
     say(f"hot-region churn: generating {L} layers of {cfg.workload}")
-    layers = [S.make_layer(cfg, l, device=dev) for l in range(L)]
+    layers, _ = make_stack(cfg, L, dev)
     xs = [S.make_tokens(cfg, l, steps, B, device=dev) for l in range(L)]
     ubits = torch.zeros(L, G, dtype=torch.int32, device=dev)
     bufs = [StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pred_storage, device=dev, union_bits=ubits[l])
@@ -564,9 +609,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.wdtype,
-        "data": "synthetic (seeded, generated on device)",
+        "data": "synthetic (seeded, generated on device)" +
+                ("; raw-order layers calibrated on the device" if wl.calibration else ""),
         "config": {"workload": cfg.workload, "batch": B, "layers": L, "d": cfg.d, "f": cfg.f, "h": cfg.h,
-                   "act": cfg.act, "density": cfg.density,
+                   "act": cfg.act, "density": cfg.density, "calibration": wl.calibration,
                    "tam": {"lambda": args.tam_lambda, "eps": args.tam_eps, "K": wl.tam_k, "G": wl.G}},
         "us_per_layer_step": round(ms_step * 1e3 / L, 3),
         "effective_GBps": round(r["gbps"], 1),

@@ -12,6 +12,8 @@
  *   sfx_sparse_down  y      = sum_j hact_j Wd[idx_j]            active rows only
  *   sfx_tam_update   per-group momentum score and hot set       once per step, all layers
  *   sfx_hot_update   hot region slots + copy of entering groups  once per step, all layers
+ *   sfx_select_kth, sfx_count_active, sfx_hot_first_order, sfx_gather_rows
+ *                    offline calibration: thresholds, frequencies, hot-first order
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a caller-owned DEVICE pointer unless the comment
@@ -316,6 +318,50 @@ int sfx_hot_update(void* stream, int L, int G, int K,
                    int32_t* slot_of, int32_t* group_of, int32_t* copies, int32_t* ncopies,
                    int nmat, const size_t* group_bytes,
                    const void* const* src, void* const* dst);
+
+/* ---------------------------------------------------------------------------------
+ * Offline calibration (not part of the decode step).  PowerInfer page, Method:
+ * offline profiling counts how often each neuron is active on calibration inputs,
+ * and a neuron table maps the stored order to the model's; KAIROX page, Core
+ * method, item 1: co-active neurons are stored as contiguous groups; Paper vs code,
+ * predictor threshold: one threshold per layer.  A calibration pass runs
+ * sfx_predict / sfx_compact on calibration tokens, then:
+ *
+ * sfx_count_active -- counts[i] += number of the B tokens whose mask holds neuron i.
+ *   tok_bits [B][ceil(f/32)] uint32 (sfx_compact's per-token masks); counts [f]
+ *   int32, in/out (start at zero).
+ *
+ * sfx_select_kth -- out[0] = the k-th smallest (0-based) of the n fp32 values, exact
+ *   (a radix select on the values' order-preserving 32-bit keys; -0 sorts below
+ *   +0, NaNs above +inf or below -inf by their sign).  With n = tokens x f scores
+ *   and k = floor((1 - rho) n) it is the threshold at which a share rho of the
+ *   calibration scores is active.  1 <= n < 2^32, k < n.  ws >= sfx_select_kth_ws()
+ *   bytes, 256-byte aligned (any contents).  out: one device float.
+ *
+ * sfx_hot_first_order -- perm [f] int32, written: the hot-first neuron table, slot r
+ *   of the new order holds old slot perm[r].  Neurons are ranked by
+ *   (group count desc, group id asc, neuron count desc, slot asc), where the group
+ *   count is the sum of counts over the group's members; group == NULL makes every
+ *   neuron its own group (plain frequency order).  group [f] int32: group id of
+ *   each slot in 0..f-1 (ids outside that range rank last, as group 0xFFFFFFFF with
+ *   count 0); groups of exactly 32 members come out as aligned blocks of 32.
+ *   ws >= sfx_hot_first_order_ws(f) bytes, 256-byte aligned, when group != NULL.
+ *   1 <= f <= 2^24.
+ *
+ * sfx_gather_rows -- dst row r = src row idx[r] for r < n_dst (applies perm to a
+ *   matrix, a bias or a scale table).  row_bytes a positive multiple of 4; src
+ *   holds n_src rows; an idx entry outside 0..n_src-1 leaves its dst row
+ *   untouched.  src and dst must not overlap.
+ * ------------------------------------------------------------------------------- */
+int sfx_count_active(void* stream, int B, int f, const uint32_t* tok_bits, int32_t* counts);
+size_t sfx_select_kth_ws(void);
+int sfx_select_kth(void* stream, size_t n, const float* values, size_t k, float* out,
+                   void* ws, size_t ws_bytes);
+size_t sfx_hot_first_order_ws(int f);
+int sfx_hot_first_order(void* stream, int f, const int32_t* counts, const int32_t* group,
+                        int32_t* perm, void* ws, size_t ws_bytes);
+int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const void* src,
+                    const int32_t* idx, void* dst);
 
 /* ---------------------------------------------------------------------------------
  * sfx_ffn_step -- the whole step for L layers in one launch: for each layer in order,

@@ -31,6 +31,11 @@ Functions and the passages they follow:
   hot_assign, hot_copy  KAIROX page, Core method, items 3 and 6: a contiguous hot
                 region of K group slots; leaving groups free their slots and only
                 entering groups are copied in.
+  calib_threshold, neuron_counts, hot_first_order, permute_rows
+                PowerInfer page, Method, offline profiling (activation counts on
+                calibration inputs) and the neuron table; KAIROX page, Core method,
+                item 1 (co-active neurons stored as contiguous groups); Paper vs
+                code, predictor threshold (one per layer).
   dense_ffn     the dense layer the sparse step reproduces when every neuron with
                 a nonzero activation is in the active set (used only by the pins).
   ffn_step      the four steps in order; with a separate predictor input xp it is
@@ -310,3 +315,50 @@ def hot_copy(region: np.ndarray, src: np.ndarray, copies):
     for g, s in copies:
         region[32 * s:32 * s + 32] = src[32 * g:32 * g + 32]
     return region
+
+
+# ----------------------------------------------------------------------------- offline calibration
+
+def calib_threshold(scores: np.ndarray, density: float) -> float:
+    """Per-layer threshold: the k-th smallest calibration score (0-based), with
+    k = floor((1 - density) * n) over all n = tokens x f scores, so that the scores
+    >= it are a share `density` of the whole (exactly, when the scores are distinct)."""
+    v = np.sort(np.asarray(scores, dtype=F64).ravel())
+    k = min(int((1.0 - density) * v.size), v.size - 1)
+    return float(v[k])
+
+
+def neuron_counts(masks: np.ndarray) -> np.ndarray:
+    """Calibration frequency of each neuron: the number of tokens whose mask holds it.
+    masks [N][f] bool."""
+    return np.asarray(masks, dtype=bool).sum(axis=0).astype(np.int64)
+
+
+def hot_first_order(counts: np.ndarray, group: np.ndarray = None) -> np.ndarray:
+    """Hot-first neuron table: new slot r holds old slot perm[r].  Groups (group ids
+    per slot; None = every neuron alone) are ranked by their members' total count
+    descending, then group id ascending; inside a group, members by count descending,
+    then slot ascending."""
+    counts = np.asarray(counts, dtype=np.int64)
+    f = counts.shape[0]
+    slot = np.arange(f)
+    if group is None:
+        gid, gsum = slot, counts
+    else:
+        gid = np.asarray(group, dtype=np.int64)
+        totals = {}
+        for i in range(f):
+            totals[gid[i]] = totals.get(gid[i], 0) + counts[i]
+        gsum = np.array([totals[g] for g in gid])
+    # lexsort: last key first -> group count desc, group id asc, count desc, slot asc
+    return np.lexsort((slot, -counts, gid, -gsum)).astype(np.int32)
+
+
+def permute_rows(layer: dict, perm: np.ndarray) -> dict:
+    """The layer with every per-neuron row (W2, Wa, Wl, Wd, their scale tables, ba)
+    taken in `perm` order; W1 and its scales are unchanged."""
+    out = dict(layer)
+    for k in ("W2", "W2_s", "Wa", "Wa_s", "Wl", "Wl_s", "Wd", "Wd_s", "ba"):
+        if layer.get(k) is not None:
+            out[k] = np.asarray(layer[k])[perm]
+    return out

@@ -8,4 +8,5 @@ Both the HIP path and the fp64 oracle consume what it produces.
 """
 from .configs import CONFIGS, FFNConfig, scaled  # noqa: F401
 from .gen import (LAYER_COS, Layer, make_layer, make_layer_chain, make_tokens, seed_for,  # noqa: F401
-                  storage_numpy, threshold_for, zipf_profile, quantize_q4)
+                  storage_numpy, threshold_for, threshold_for_share, layer_threshold, zipf_profile,
+                  quantize_q4)

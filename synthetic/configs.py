@@ -26,6 +26,8 @@ class FFNConfig:
     tam: Optional[dict] = None
     workload: str = ""
     pred_q4: bool = False  # predictor W1 / W2 stored as int4 g32 (x stays fp16)
+    pred_profile: str = "zipf"  # 'zipf': neuron i's predictor fires with probability p_i;
+                                # 'iid': plain N(0, 1/fan_in) predictor, same rate for all
 
     @property
     def pdtype(self) -> str:
@@ -46,7 +48,7 @@ class FFNConfig:
 CONFIGS = {
     "C1": FFNConfig("C1", d=256, f=1024, h=64, wdtype="f32", act="relu", layers=1,
                     steps=8, batches=(1,), density=0.10, x_process="iid", planted=False,
-                    workload="tiny ReLU FFN d=256 f=1024 fp32"),
+                    pred_profile="iid", workload="tiny ReLU FFN d=256 f=1024 fp32"),
     "C2": FFNConfig("C2", d=4096, f=16384, h=1024, wdtype="f16", act="relu", layers=32,
                     steps=256, batches=(1,), density=0.08, x_process="ar1", planted=False,
                     workload="OPT-6.7B-shaped ReLU FFN d=4096 f=16384 h=1024 fp16, 32 layers"),

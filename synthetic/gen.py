@@ -9,17 +9,27 @@ The recipe reproduces the structure the pages measure, on seeded random data:
 * temporal locality of successive tokens (KAIROX, Key observations, observation 3):
   AR(1) tokens x_t = 0.9 x_{t-1} + sqrt(0.19) xi_t with unit stationary variance;
 * co-activated groups of 32 (KAIROX, Core method, items 1 and 3): the predictor's
-  output rows of one group share a common direction, W2_i = sqrt(0.9) u_grp +
+  output rows of one group share a common direction, r_i = sqrt(0.9) u_grp +
   sqrt(0.1) v_i, so the group's scores move together;
-* hot-first storage (PowerInfer, Method, neuron table; KAIROX, Core method, item 3):
-  slot i holds the neuron of Zipf rank i+1, so groups of 32 consecutive slots are
-  contiguous and ordered by frequency.  `perm` is the neuron table (slot -> id).
+* a predictor that fires with the same power law (PowerInfer, Method, Insight 1:
+  the predictor predicts that activation).  With W1 ~ N(0, 1/d) and unit-variance
+  tokens every hidden unit is relu of a standard normal: mean mu = 1/sqrt(2 pi),
+  standard deviation sd = sqrt(1/2 - 1/(2 pi)).  Row i of W2 is its random part r_i
+  (N(0, 1/h) entries, row mean removed) plus m_i / (mu h) on every entry, so its
+  score is about N(m_i, sd^2); m_i = sd Phi^-1(p_i) and the threshold 0 give
+  P(score_i >= 0) = p_i.  Configuration C1 keeps a plain N(0, 1/h) W2 (its
+  recipe states one): scores N(0, 1/2), threshold Phi^-1(1 - density) / sqrt(2);
+* storage order.  `order="hot_first"` (the default) stores slot i = the neuron of
+  Zipf rank i+1, planted groups as aligned blocks of 32: the layer as offline
+  placement would leave it (PowerInfer, Method, neuron table; KAIROX, Core method,
+  item 3).  `order="raw"` stores the same neurons in a seeded random order, as a
+  model ships before calibration: `perm` of the hot-first layer maps its slots to
+  the raw layer's (hot_first row r = raw row perm[r]), and `group` gives each raw
+  slot's planted group, the output of the offline grouping step.
 
-The per-layer threshold is set for the configured density from the score
-distribution in closed form: with W1 ~ N(0, 1/d), W2 ~ N(0, 1/h) and unit-variance
-tokens, a score is N(0, 1/2), so t = Phi^-1(1 - density) / sqrt(2).
-
-Nothing here evaluates the predictor, the gate or the FFN.
+The thresholds here are closed forms; a calibration pass replaces them with the
+(1 - density)-quantile of measured scores.  Nothing here evaluates the predictor,
+the gate or the FFN.
 """
 import hashlib
 import math
@@ -28,7 +38,7 @@ from typing import Dict, Optional
 
 import numpy as np
 import torch
-from scipy.special import ndtri
+from scipy.special import ndtr, ndtri
 
 from .configs import FFNConfig
 
@@ -74,9 +84,36 @@ def zipf_profile(f: int, density: float, s: float = ZIPF_S, pmax: float = ZIPF_P
     return np.minimum(pmax, hi * base)
 
 
+RELU_MEAN = 1.0 / math.sqrt(2.0 * math.pi)                 # E relu(z), z ~ N(0, 1)
+RELU_SD = math.sqrt(0.5 - 1.0 / (2.0 * math.pi))           # sd of relu(z)
+
+
 def threshold_for(density: float) -> float:
-    """Per-layer threshold for the configured density (closed form, see module doc)."""
+    """Closed-form threshold of the plain N(0, 1/h) predictor (scores N(0, 1/2))."""
     return float(np.float32(ndtri(1.0 - density) / math.sqrt(2.0)))
+
+
+def layer_threshold(cfg: FFNConfig) -> float:
+    """Closed-form per-layer threshold of the configuration's predictor."""
+    return 0.0 if cfg.pred_profile == "zipf" else threshold_for(cfg.density)
+
+
+def threshold_for_share(cfg: FFNConfig, share: float) -> float:
+    """Closed-form threshold at which about `share` of the neurons are active per
+    token (tests that need long or short active lists): for the power-law predictor
+    the t with mean_i Phi(Phi^-1(p_i) - t / sd) = share (bisection); for the plain
+    predictor Phi^-1(1 - share) / sqrt(2)."""
+    if cfg.pred_profile != "zipf":
+        return threshold_for(share)
+    z = ndtri(zipf_profile(cfg.f, cfg.density))
+    lo, hi = -20.0, 20.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if ndtr(z - mid / RELU_SD).mean() > share:
+            lo = mid
+        else:
+            hi = mid
+    return float(np.float32(0.5 * (lo + hi)))
 
 
 def _randn(g: torch.Generator, rows: int, cols: int, device) -> torch.Tensor:
@@ -123,8 +160,9 @@ class Layer:
     ba: torch.Tensor               # [f]     fp32 bias of the activated branch
     Wd: torch.Tensor               # [f][d]  down projection, neuron-major; q4: uint8 [f][d/2]
     threshold: float
-    perm: torch.Tensor             # [f]     int32 neuron table: slot -> original neuron id
+    perm: torch.Tensor             # [f]     int32 neuron table: slot -> raw-order slot
     p: np.ndarray                  # [f]     Zipf activation probability per slot
+    group: Optional[torch.Tensor] = None   # [f] int32 planted group of each slot (planted configs)
     Wl: Optional[torch.Tensor] = None      # [f][d] ReGLU linear branch
     Wa_s: Optional[torch.Tensor] = None    # q4 scales [f][d/32] fp16
     Wl_s: Optional[torch.Tensor] = None
@@ -141,10 +179,13 @@ class Layer:
         return out
 
 
-def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
+def make_layer(cfg: FFNConfig, layer: int, device="cpu", order: str = "hot_first") -> Layer:
+    if order not in ("hot_first", "raw"):
+        raise ValueError("order is 'hot_first' or 'raw'")
     d, f, h = cfg.d, cfg.f, cfg.h
     pdt = TORCH_DTYPE[cfg.pdtype]
     name = cfg.name
+    p = zipf_profile(f, cfg.density)
 
     W1 = _randn(_rng(name, layer, "W1", device), h, d, device) / math.sqrt(d)
     if cfg.planted:
@@ -156,6 +197,9 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
         del u, v
     else:
         W2 = _randn(_rng(name, layer, "W2", device), f, h, device) / math.sqrt(h)
+    if cfg.pred_profile == "zipf":
+        m = torch.from_numpy(RELU_SD * ndtri(p)).to(device)
+        W2 = W2 - W2.mean(dim=1, keepdim=True) + (m / (RELU_MEAN * h)).unsqueeze(1)
     W1_s = W2_s = None
     if cfg.pred_q4:
         W1, W1_s = quantize_q4(W1)
@@ -163,7 +207,6 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
     else:
         W1, W2 = W1.to(pdt), W2.to(pdt)
 
-    p = zipf_profile(f, cfg.density)
     ba = torch.from_numpy(ndtri(p)).to(torch.float32).to(device)
 
     Wa64 = _unit_rows(_rng(name, layer, "Wa", device), f, d, device)
@@ -183,11 +226,25 @@ def make_layer(cfg: FFNConfig, layer: int, device="cpu") -> Layer:
         Wl = Wl64.to(wdt) if Wl64 is not None else None
     del Wa64, Wd64, Wl64
 
-    g = _rng(name, layer, "perm", "cpu")
-    perm = torch.randperm(f, generator=g).to(torch.int32).to(device)
-    return Layer(cfg=cfg, index=layer, W1=W1, W2=W2, Wa=Wa, ba=ba, Wd=Wd,
-                 threshold=threshold_for(cfg.density), perm=perm, p=p,
-                 Wl=Wl, Wa_s=Wa_s, Wl_s=Wl_s, Wd_s=Wd_s, W1_s=W1_s, W2_s=W2_s)
+    # raw order: raw slot j holds hot-first slot sigma[j]; so hot-first slot r is raw
+    # slot perm[r] with perm = sigma^-1
+    sigma = torch.randperm(f, generator=_rng(name, layer, "perm", "cpu"))
+    group = (torch.arange(f, dtype=torch.int32) // 32) if cfg.planted else None
+    if order == "hot_first":
+        perm = torch.argsort(sigma).to(torch.int32).to(device)
+        return Layer(cfg=cfg, index=layer, W1=W1, W2=W2, Wa=Wa, ba=ba, Wd=Wd,
+                     threshold=layer_threshold(cfg), perm=perm, p=p,
+                     group=group.to(device) if group is not None else None,
+                     Wl=Wl, Wa_s=Wa_s, Wl_s=Wl_s, Wd_s=Wd_s, W1_s=W1_s, W2_s=W2_s)
+    sd = sigma.to(device)
+
+    def shuf(t):
+        return None if t is None else t.index_select(0, sd).contiguous()
+
+    return Layer(cfg=cfg, index=layer, W1=W1, W2=shuf(W2), Wa=shuf(Wa), ba=shuf(ba), Wd=shuf(Wd),
+                 threshold=layer_threshold(cfg), perm=torch.arange(f, dtype=torch.int32, device=device),
+                 p=p[sigma.numpy()], group=shuf(group.to(device)) if group is not None else None,
+                 Wl=shuf(Wl), Wa_s=shuf(Wa_s), Wl_s=shuf(Wl_s), Wd_s=shuf(Wd_s), W1_s=W1_s, W2_s=shuf(W2_s))
 
 
 def make_tokens(cfg: FFNConfig, layer: int, steps: int, B: int, device="cpu", tag: str = "x") -> torch.Tensor:

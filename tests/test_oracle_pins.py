@@ -420,3 +420,69 @@ def test_hot_region_invariants_over_tam_sequence():
         assert np.array_equal(slot_of[stay], before[stay])
         assert np.all(slot_of[~hot_new] == -1)
         hot = hot_new
+
+
+# ----------------------------------------------------------------------------- offline calibration
+
+def test_calib_threshold_hand_case_and_share():
+    """calib_threshold: scores (3, 1, 4, 1, 5, 9, 2, 6), density 0.25 -> k = 6 of the
+    sorted (1, 1, 2, 3, 4, 5, 6, 9) -> t = 6, and exactly 2 of 8 scores are >= t.
+    An off-by-one in k (t = 5 or 9) or a descending sort (t = 1) fails.  On distinct
+    random scores the share >= t is exactly (n - k) / n for several densities."""
+    s = np.array([[3, 1, 4, 1], [5, 9, 2, 6]], float)
+    t = O.calib_threshold(s, 0.25)
+    assert t == 6.0 and int((s >= t).sum()) == 2
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((37, 53))
+    for rho in (0.01, 0.06, 0.12, 0.5):
+        t = O.calib_threshold(v, rho)
+        k = int((1 - rho) * v.size)
+        assert int((v >= t).sum()) == v.size - k
+
+
+def test_neuron_counts_and_hot_first_order_hand_case():
+    """Counts are column sums of the masks.  Without groups the order is count desc,
+    slot asc: counts (2, 5, 5, 0, 3) -> (1, 2, 4, 0, 3).  With groups {0: slots 0, 3},
+    {1: slots 1, 4}, {2: slot 2}: group totals 2, 8, 5 -> group 1 (slots 1, 4 by
+    count), group 2 (slot 2), group 0 (slot 0 then 3) -> (1, 4, 2, 0, 3).  Ranking
+    groups ascending, by id, or members by slot first all fail."""
+    masks = np.array([[1, 1, 1, 0, 1], [1, 1, 1, 0, 1], [0, 1, 1, 0, 1],
+                      [0, 1, 1, 0, 0], [0, 1, 1, 0, 0]], bool)
+    c = O.neuron_counts(masks)
+    assert c.tolist() == [2, 5, 5, 0, 3]
+    assert O.hot_first_order(c).tolist() == [1, 2, 4, 0, 3]
+    assert O.hot_first_order(c, np.array([0, 1, 2, 0, 1])).tolist() == [1, 4, 2, 0, 3]
+
+
+def test_hot_first_order_brute_force_and_blocks():
+    """On random counts with tied totals: the table is a permutation, adjacent slots
+    respect the four-key order, and groups of exactly 32 come out as aligned blocks."""
+    rng = np.random.default_rng(12)
+    G = 20
+    group = rng.permutation(np.repeat(np.arange(G), 32))
+    counts = rng.integers(0, 4, size=32 * G)
+    perm = O.hot_first_order(counts, group)
+    assert sorted(perm.tolist()) == list(range(32 * G))
+    tot = {g: counts[group == g].sum() for g in range(G)}
+    key = [(-tot[group[i]], group[i], -counts[i], i) for i in perm]
+    assert key == sorted(key)
+    blocks = group[perm].reshape(G, 32)
+    assert np.all(blocks == blocks[:, :1])
+
+
+def test_permute_rows_leaves_the_step_unchanged():
+    """permute_rows on a ReGLU layer with scale-free rows: the step on the permuted
+    layer has the permuted scores, the mapped index set and the same y."""
+    rng = np.random.default_rng(15)
+    d, h, f = 16, 8, 40
+    layer = {"W1": rng.standard_normal((h, d)), "W2": rng.standard_normal((f, h)),
+             "Wa": rng.standard_normal((f, d)), "Wl": rng.standard_normal((f, d)),
+             "ba": rng.standard_normal(f), "Wd": rng.standard_normal((f, d))}
+    x = rng.standard_normal((3, d))
+    p = rng.permutation(f)
+    a = O.ffn_step(x, layer, "f32", "f32", "reglu", 0.2)
+    b = O.ffn_step(x, O.permute_rows(layer, p), "f32", "f32", "reglu", 0.2)
+    assert np.array_equal(b["scores"], a["scores"][:, p])
+    inv = np.argsort(p)
+    assert b["idx"].tolist() == sorted(inv[a["idx"]].tolist())
+    assert np.allclose(a["y"], b["y"], rtol=1e-12, atol=1e-12)

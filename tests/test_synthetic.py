@@ -142,3 +142,35 @@ def test_layer_chain_cosine_and_variance():
     assert abs(float(lag) - 0.9) < 0.03
     again = S.make_layer_chain(cfg, 3, 6, 2)
     assert all(torch.equal(u, v) for u, v in zip(xs, again))
+
+
+@pytest.mark.parametrize("name,share", [("C2", 0.2), ("C5", 0.3), ("C1", 0.2)])
+def test_threshold_for_share(name, share):
+    """The closed-form threshold for a target per-token share gives about that share
+    with the oracle's predictor on generated data."""
+    cfg = _small(name, d=512, f=4096, h=256) if name != "C1" else S.CONFIGS["C1"]
+    t = S.threshold_for_share(cfg, share)
+    dens = []
+    for li in range(4):
+        L = S.make_layer(cfg, li)
+        x = S.make_tokens(cfg, li, 32, 1)[:, 0]
+        sc = O.predict(O.decode(S.storage_numpy(x), cfg.pdtype),
+                       O.decode(S.storage_numpy(L.W1), cfg.pdtype), O.decode(S.storage_numpy(L.W2), cfg.pdtype))
+        dens.append((sc >= t).mean())
+    assert np.mean(dens) == pytest.approx(share, rel=0.2)
+    assert S.threshold_for_share(cfg, cfg.density) == pytest.approx(S.layer_threshold(cfg), abs=1e-3)
+
+
+def test_raw_order_is_a_shuffle_of_hot_first():
+    """order='raw' stores the hot-first layer's rows in a seeded random order, and
+    the hot-first layer's perm maps its slots to the raw slots."""
+    cfg = _small("C3", d=256, f=320, h=64)
+    hf = S.make_layer(cfg, 0)
+    raw = S.make_layer(cfg, 0, order="raw")
+    perm = hf.perm.long()
+    assert sorted(perm.tolist()) == list(range(320)) and not torch.equal(perm, torch.arange(320))
+    for k in ("W2", "Wa", "Wl", "Wd", "ba"):
+        assert torch.equal(getattr(raw, k)[perm], getattr(hf, k)), k
+    assert torch.equal(raw.group[perm], hf.group) and torch.equal(hf.group, torch.arange(320) // 32)
+    assert np.array_equal(raw.p[perm.numpy()], hf.p)
+    assert torch.equal(hf.W1, raw.W1) and raw.threshold == hf.threshold
