@@ -286,6 +286,52 @@ __device__ __forceinline__ void prefetch_w2(const StepParams& p, CLayer* Ld, uin
   }
 }
 
+// The fused step's W2 rows: workgroup w owns rows w + P j (j < nr2), strided over
+// the workgroups, so hot-first storage spreads the most active neurons evenly
+// over them; own row q lands at s_w2 + q * (h/8) * 16, like prefetch_w2.
+__device__ __forceinline__ void prefetch_w2_rows(const StepParams& p, CLayer* Ld, uint8_t* s_w2) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int w = blockIdx.x;
+  const int P = gridDim.x;
+  if (wave >= kAW && wave < kCW && p.w2_lds != 0) {
+    const uint8_t* W2 = (const uint8_t*)Ld->W2;
+    const int nch2 = p.h / 8;
+    const size_t rb2 = (size_t)p.h * 2;
+    const int nr2 = w < p.f ? (p.f - w + P - 1) / P : 0;
+    const int items = nr2 * nch2;
+    constexpr int kStride = (kCW - kAW) * kWave;
+    const int i_first = (wave - kAW) * kWave + lane;
+    int q = i_first / nch2, c = i_first - q * nch2;
+    const int dq = kStride / nch2, dc = kStride - dq * nch2;
+#pragma unroll 1
+    for (int i0 = (wave - kAW) * kWave; i0 < items; i0 += kStride) {
+      if (i0 + lane < items) {
+        int row = w + P * q;
+        if (row >= p.f) row = p.f - 1;       // never: q < nr2
+        __builtin_amdgcn_global_load_lds((const void*)(W2 + (size_t)row * rb2 + (size_t)c * 16),
+                                         (__attribute__((address_space(3))) void*)(s_w2 + (size_t)i0 * 16), 16, 0, 0);
+      }
+      q += dq;
+      c += dc;
+      if (c >= nch2) { c -= nch2; ++q; }
+    }
+  }
+}
+
+// One stage of a 32 x 32 bit-matrix transpose held one row per lane (each half
+// wave its own matrix): rows L and L ^ s swap the s x s blocks off the diagonal of
+// their 2s x 2s block; `hi` marks the columns t with t & s set.
+__device__ __forceinline__ uint32_t transpose_step(uint32_t x, int lane, int s, uint32_t hi) {
+  const uint32_t y = __shfl_xor(x, s, kWave);
+  return (lane & s) ? ((x & hi) | ((y & hi) >> s)) : ((x & ~hi) | ((y & ~hi) << s));
+}
+
+// Own mask words per workgroup (at most) when workgroup w owns rows w + P j.
+__device__ __forceinline__ int own_words_max(int f, int P) { return (((f + P - 1) / P) + 31) >> 5; }
+
 // Thread and shape values, re-derived at the start of every phase behind opaque
 // copies: values computed once would be hoisted out of the layer loop and kept
 // live through every phase.
@@ -332,7 +378,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   int k_prev = -1;                           // active neurons of the previous layer
   Raw<16> w1r[kU];
   prefetch_w1<kU>(p, (CLayer*)p.layers, w1r);
-  prefetch_w2(p, (CLayer*)p.layers, s_w2);
+  prefetch_w2_rows(p, (CLayer*)p.layers, s_w2);
   for (int l = 0; l < p.L; ++l) {
     const uint32_t tag = e0 + (uint32_t)l + 1u;
     CLayer* Ld = (CLayer*)p.layers + l;
@@ -367,7 +413,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         group_sync(&s_grp, g0 + 2 * kAW, p.err);              // inputs landed
       } else if (l > 0 && wave < kCW) {
         lds_wait_at_least(&s_grp, g0 + kAW, p.err);
-        prefetch_w2(p, Ld, s_w2);
+        prefetch_w2_rows(p, Ld, s_w2);
       }
       float acc[NB];
 #pragma unroll
@@ -413,9 +459,11 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     // ---------------------------------------------------------------- phase B
     {
       SFX_PHASE_IDS;
-      // owned mask words w + P m, m < nw2
-      const int nw2 = w < W ? (W - w + P - 1) / P : 0;
-      const int rows2 = nw2 * 32;
+      // owned rows w + P j, j < nr2, and their mask words m < nwo (bit j % 32 of
+      // word j / 32)
+      const int nr2 = w < f ? (f - w + P - 1) / P : 0;
+      const int nwo = (nr2 + 31) >> 5;
+      const int rows2 = nr2;
       const bool w2_lds = p.w2_lds != 0;
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
@@ -470,7 +518,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
               if constexpr (kLds) {
                 wv[r] = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
               } else {
-                const int row = min(32 * (w + P * (q >> 5)) + (q & 31), f - 1);
+                const int row = min(w + P * q, f - 1);
                 wv[r] = load_raw<16>(W2 + (size_t)row * rb2 + (size_t)c * 16);
               }
             }
@@ -496,34 +544,34 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       if (w2_lds) scores_pass(std::true_type{});
       else scores_pass(std::false_type{});
       __syncthreads();
-      // mask words by wave ballots (lane = row of a 64-row pair of words), then the
-      // union goes out tagged, then the scores
-      for (int m0 = 2 * wave; m0 < nw2; m0 += 2 * kNW) {
+      // own mask words by wave ballots (lane = own row j of a 64-row pair of
+      // words), then the union words go out tagged (block words [0, nwm)), the
+      // per-token words too when the caller asked for per-token masks (block words
+      // nwm (1 + b) + m), then the scores
+      for (int m0 = 2 * wave; m0 < nwo; m0 += 2 * kNW) {
         const int m = m0 + (lane >> 5);
-        const int g = w + P * m;
-        const int row = 32 * g + (lane & 31);
-        const bool in = m < nw2 && row < f;
+        const int j = 32 * m + (lane & 31);
+        const bool in = m < nwo && j < nr2;
         const float thr = Ld->threshold;
         for (int b = 0; b < B; ++b) {
-          const uint64_t bal = __ballot(in && s_sc[(32 * m + (lane & 31)) * NB + b] >= thr);
-          if ((lane & 31) == 0 && m < nw2) {
-            const uint32_t word = (uint32_t)(lane == 0 ? bal : (bal >> 32));
-            if (Ld->tok_bits != nullptr) Ld->tok_bits[(size_t)b * W + g] = word;
-            s_words[m * NB + b] = word;
-          }
+          const uint64_t bal = __ballot(in && s_sc[j * NB + b] >= thr);
+          if ((lane & 31) == 0 && m < nwo) s_words[m * NB + b] = (uint32_t)(lane == 0 ? bal : (bal >> 32));
         }
       }
       lds_barrier();
-      if (tid < nw2) {
+      const int nwm = own_words_max(f, P);
+      if (tid < nwo) {
         uint32_t u = 0;
         for (int b = 0; b < B; ++b) u |= s_words[tid * NB + b];
-        const int g = w + P * tid;
         st_tagged(p.uni + (size_t)w * p.us + tid, tag, u);
-        Ld->union_bits[g] = u;
+      }
+      if (Ld->tok_bits != nullptr && tid < nwo * B) {
+        const int m = tid / B, b = tid - m * B;
+        st_tagged(p.uni + (size_t)w * p.us + nwm * (1 + b) + m, tag, s_words[m * NB + b]);
       }
       for (int i = tid; i < rows2 * B; i += kNT) {
         const int q = i / B, b = i - q * B;
-        const int row = 32 * (w + P * (q >> 5)) + (q & 31);
+        const int row = w + P * q;
         if (row < f) Ld->scores[(size_t)b * f + row] = s_sc[q * NB + b];
       }
     }
@@ -580,22 +628,23 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
     };
     // Up rows first, for this workgroup's own active neurons: the union bits of its
-    // mask words w + P m (still in s_words), so no exchange is waited for; at most
-    // `cap` of them: twice the previous layer's even share ceil(k / P), at least one
-    // round of the waves and at most kOwnCap (two rounds; kOwnCap for the first
-    // layer).  These rows overlap the union exchange.  A workgroup whose words are
-    // dense (hot-first storage puts the most active neurons in the first words)
-    // leaves the rest to the split below, after the union exchange.
+    // own rows w + P j (mask words still in s_words), so no exchange is waited for;
+    // at most `cap` of them: twice the previous layer's even share ceil(k / P), at
+    // least one round of the waves and at most kOwnCap (two rounds; kOwnCap for the
+    // first layer).  These rows overlap the union exchange; the rows past `cap`
+    // are left to the split below, after the union exchange.
     const int cap = k_prev < 0 ? kOwnCap : min(kOwnCap, max(kWork, 2 * ((k_prev + P - 1) / P)));
+    const int nwm = own_words_max(f, P);
     {
-      const int nw2 = w < W ? (W - w + P - 1) / P : 0;
+      const int nr2 = w < f ? (f - w + P - 1) / P : 0;
+      const int nwo = (nr2 + 31) >> 5;
       auto own_word = [&](int m) {
         uint32_t u = 0;
         for (int b = 0; b < B; ++b) u |= s_words[m * NB + b];
         return u;
       };
       int own_k = 0;
-      for (int m = 0; m < nw2; ++m) own_k += __popc(own_word(m));
+      for (int m = 0; m < nwo; ++m) own_k += __popc(own_word(m));
       const int own_n = min(own_k, cap);
       for (int e = wave; e < own_n; e += kWork) {
         // entry e of the own list: word m, its rem-th set bit
@@ -603,15 +652,18 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         uint32_t um = own_word(0);
         while (rem >= __popc(um)) { rem -= __popc(um); um = own_word(++m); }
         for (int i = 0; i < rem; ++i) um &= um - 1;
-        up_row(32 * (w + P * m) + __builtin_ctz(um));
+        up_row(w + P * (32 * m + __builtin_ctz(um)));
       }
     }
-    // thread o polls the union block of workgroup o (words o + P m) into s_uw
+    // thread o polls the union words of owner o into s_raw[o][m] (zero past the
+    // owner's words); s_w2 is free from the end of phase B to the next layer
+    uint32_t* s_raw = reinterpret_cast<uint32_t*>(s_w2);      // [P][nwm]
 #pragma unroll 1
     for (int o = tid; o < P; o += kNT) {
-      const int nw = o < W ? (W - o + P - 1) / P : 0;
+      const int nro = o < f ? (f - o + P - 1) / P : 0;
+      const int nw = (nro + 31) >> 5;
 #pragma unroll 1
-      for (int m0 = 0; m0 < nw; m0 += 8) {
+      for (int m0 = 0; m0 < nwm; m0 += 8) {
         unsigned long long uv[8];
         const int n = min(8, nw - m0);
         auto valid = [&](int i) { return i < n; };
@@ -619,10 +671,53 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         poll_tagged_if<8, decltype(valid), decltype(addr), kStepPS>(uv, valid, addr, tag, p.err);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (i < n) s_uw[o + P * (m0 + i)] = (uint32_t)uv[i];
+          if (m0 + i < nwm) s_raw[o * nwm + m0 + i] = i < n ? (uint32_t)uv[i] : 0u;
       }
     }
     lds_barrier();
+    // Union words in the standard layout (bit b of word g = neuron 32 g + b).  With
+    // P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and belong to
+    // owners 32 (g mod P/32) + b.  Lane L holds the mask word c of owner 64 q + L
+    // (bits j = 32 c + t); a 32 x 32 bit transpose within each half wave (five
+    // exchange stages) leaves in lane t the bits j = 32 c + t of owners 64 q .. + 31
+    // (lanes 0..31) or 64 q + 32 .. + 63 (lanes 32..63): words j P/32 + 2q (+1).
+    {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int nq = P >> 6;
+      const int nr2m = (f + P - 1) / P;
+      for (int it = wv; it < nq * nwm; it += kNW) {
+        const int q = it % nq, c = it / nq;
+        uint32_t x = s_raw[(64 * q + lane) * nwm + c];
+        x = transpose_step(x, lane, 16, 0xFFFF0000u);
+        x = transpose_step(x, lane, 8, 0xFF00FF00u);
+        x = transpose_step(x, lane, 4, 0xF0F0F0F0u);
+        x = transpose_step(x, lane, 2, 0xCCCCCCCCu);
+        x = transpose_step(x, lane, 1, 0xAAAAAAAAu);
+        const int j = 32 * c + (lane & 31);
+        const int g = j * (P >> 5) + 2 * q + (lane >> 5);
+        if (j < nr2m && g < W) s_uw[g] = x;
+      }
+    }
+    lds_barrier();
+    // outputs of this workgroup: union words g = w + P m and, when asked for, the
+    // per-token words (bit b from owner 32 (g mod P/32) + b, one tagged word per lane)
+    for (int g = w + P * tid; g < W; g += P * kNT) Ld->union_bits[g] = s_uw[g];
+    if (Ld->tok_bits != nullptr && wave == 0) {
+      for (int g = w; g < W; g += P) {
+        const int j = g / (P >> 5), c = g - j * (P >> 5);
+        for (int b = 0; b < B; ++b) {
+          unsigned long long tv[1];
+          auto valid = [&](int i) { (void)i; return lane < 32; };
+          auto addr = [&](int i) {
+            (void)i;
+            return p.uni + (size_t)(32 * c + (lane & 31)) * p.us + nwm * (1 + b) + (j >> 5);
+          };
+          poll_tagged_if<1, decltype(valid), decltype(addr), kStepPS>(tv, valid, addr, tag, p.err);
+          const uint64_t bal = __ballot(lane < 32 && (((uint32_t)tv[0] >> (j & 31)) & 1u) != 0u);
+          if (lane == 0) Ld->tok_bits[(size_t)b * W + g] = (uint32_t)bal;
+        }
+      }
+    }
     // thread t owns words [wpt t, wpt t + wpt): one word when W <= 512, so a full
     // (hot) word costs 32 steps of the extraction below, not 64
     const int wpt = W <= kNT ? 1 : 2;
@@ -637,7 +732,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     uint32_t* s_own = reinterpret_cast<uint32_t*>(s_red) + 512;   // [P] own rows done first
     if (tid < P) {
       uint32_t c = 0;
-      for (int g = tid; g < W; g += P) c += __popc(s_uw[g]);
+      for (int m = 0; m < nwm; ++m) c += __popc(s_raw[tid * nwm + m]);
       ovc = c > (uint32_t)cap ? c - (uint32_t)cap : 0u;
       s_own[tid] = c - ovc;
     }
@@ -677,8 +772,8 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     }
     if (w == 0 && tid == 0) *Ld->count = k;
     lds_barrier();
-    // Own entries past `cap` of every workgroup (owner o: the set bits of words
-    // o + P m in order, from entry cap on), ranked by owner through the prefix
+    // Own entries past `cap` of every workgroup (owner o: the set bits of its own
+    // mask words in order, from entry cap on), ranked by owner through the prefix
     // s_ovp from the scan above, fill the workgroups up to T = ceil(k / P) rows
     // each: workgroup w takes the T - own_w overflow ranks after those of
     // workgroups 0..w-1 (each wave sums the deficits before w itself).  Since
@@ -699,10 +794,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           if ((int)s_ovp[mid] <= r) lo = mid; else hi = mid;
         }
         int m = 0, rem = cap + (r - (int)s_ovp[lo]);
-        uint32_t um = s_uw[lo];
-        while (rem >= __popc(um)) { rem -= __popc(um); um = s_uw[lo + P * (++m)]; }
+        uint32_t um = s_raw[lo * nwm];
+        while (rem >= __popc(um)) { rem -= __popc(um); um = s_raw[lo * nwm + (++m)]; }
         for (int i = 0; i < rem; ++i) um &= um - 1;
-        up_row(32 * (lo + P * m) + __builtin_ctz(um));
+        up_row(lo + P * (32 * m + __builtin_ctz(um)));
       }
     }
 

@@ -30,7 +30,10 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   StepGeom g{};
   g.ok = false;
   g.P = P;
-  if (P < 8 || P > 256 || (wdt != DT_F16 && wdt != DT_BF16) || B < 1 || B > 4 || (act != 0 && act != 1)) return g;
+  // P = 64, 128 or 256: the fused step rebuilds union words from the owners' masks
+  // with one ballot per 64 owners, the 8 waves split evenly over the owner groups
+  if (P != 64 && P != 128 && P != 256) return g;
+  if ((wdt != DT_F16 && wdt != DT_BF16) || B < 1 || B > 4 || (act != 0 && act != 1)) return g;
   if (d < 8 || h < 8 || d % 8 != 0 || h % 8 != 0 || f < 1) return g;
   const int W = (f + 31) / 32;
   if (W > kMaxWords) return g;
@@ -76,11 +79,15 @@ namespace {
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
-// Tagged union words per workgroup block.
-int step_union_block(int f, int P) {
+// Tagged words per workgroup block of the union exchange: the fused step's own
+// mask words (rows w + P j) and, for the per-token masks, B more of them; the Live
+// Pipeline kernel's union words (words w + P m).
+int step_union_block(int f, int P, int B) {
   const int W = (f + 31) / 32;
   const int nw2max = (W + P - 1) / P;
-  return (nw2max + 7) & ~7;
+  const int nwm = ((f + P - 1) / P + 31) / 32;
+  const int n = nw2max > nwm * (1 + B) ? nw2max : nwm * (1 + B);
+  return (n + 7) & ~7;
 }
 
 // control line | barrier flags [P][kFlagStride] | hidden [P][16] | union [P][us] |
@@ -88,7 +95,7 @@ int step_union_block(int f, int P) {
 size_t step_ws_bytes(int B, int h, int f, int P) {
   (void)h;
   const size_t fl = up256((size_t)P * kFlagStride * 4);
-  return 256 + fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P) * 8) +
+  return 256 + fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P, B) * 8) +
          up256((size_t)f * B * 8);
 }
 
@@ -106,7 +113,7 @@ StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layer
   p.cw = g.cw;
   uint8_t* base = (uint8_t*)ws;
   p.err = (uint32_t*)base;
-  p.us = step_union_block(f, g.P);
+  p.us = step_union_block(f, g.P, B);
   const size_t fl = up256((size_t)g.P * kFlagStride * 4);
   p.fbar = (uint32_t*)(base + 256);
   size_t off = 256 + fl;
