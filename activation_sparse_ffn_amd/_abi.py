@@ -25,7 +25,8 @@ EXPORTS = ("sfx_status_str", "sfx_abi_version", "sfx_predict_ws", "sfx_predict",
            "sfx_tam_update", "sfx_ffn_step_ws", "sfx_ffn_step", "sfx_sparse_down_noalloc",
            "sfx_ffn_pipeline_ws", "sfx_ffn_pipeline", "sfx_stream_read", "sfx_predict_q4",
            "sfx_topk_now_update", "sfx_hot_update", "sfx_count_active", "sfx_select_kth_ws",
-           "sfx_select_kth", "sfx_hot_first_order_ws", "sfx_hot_first_order", "sfx_gather_rows")
+           "sfx_select_kth", "sfx_hot_first_order_ws", "sfx_hot_first_order", "sfx_gather_rows",
+           "sfx_dense_ffn_ws", "sfx_dense_ffn")
 HOT_MAX_MATS = 8
 SFX_DOWN_SCRATCH_BYTES = 17 << 20
 
@@ -100,6 +101,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfx_hot_first_order.argtypes = [P, I, P, P, P, P, Z]
     lib.sfx_gather_rows.restype = I
     lib.sfx_gather_rows.argtypes = [P, I, I, Z, P, P, P]
+    lib.sfx_dense_ffn_ws.restype = Z
+    lib.sfx_dense_ffn_ws.argtypes = [I, I, I, I]
+    lib.sfx_dense_ffn.restype = I
+    lib.sfx_dense_ffn.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, Z]
     lib.sfx_ffn_step_ws.restype = Z
     lib.sfx_ffn_step_ws.argtypes = [I, I, I, I, I, I]
     lib.sfx_ffn_step.restype = I
@@ -260,6 +265,28 @@ def sfx_sparse_down(Wd, idx, count, hact, y, ws, Wd_scales=None, stream=None):
     q = (_ptr(hact), _ptr(y), _ptr(ws))
     st = load().sfx_sparse_down(_stream(stream), wdt, B, d, f, *p, kmax, *q, ws.numel() if ws is not None else 0)
     _check(st, "sfx_sparse_down")
+
+
+def sfx_dense_ffn_ws(wdt: int, B: int, d: int, f: int) -> int:
+    return load().sfx_dense_ffn_ws(wdt, B, d, f)
+
+
+def sfx_dense_ffn(x, Wa, ba, Wd, hact, y, ws, act="relu", Wa_scales=None, Wl=None, Wl_scales=None,
+                  Wd_scales=None, stream=None):
+    """The FFN over every neuron: hact[f][B] and y[B][d] (both overwritten)."""
+    B, d = x.shape
+    f = Wa.shape[0]
+    wdt = _wdt_of(Wa)
+    if hact.numel() < f * B or tuple(y.shape) != (B, d):
+        raise ValueError("sfx_dense_ffn: hact [f][B] and y [B][d] expected")
+    _need(hact, torch.float32, "hact")
+    _need(y, torch.float32, "y")
+    if ba is not None:
+        _need(ba, torch.float32, "ba")
+    p = (_ptr(x), _ptr(Wa), _ptr(Wa_scales), _ptr(ba), _ptr(Wl), _ptr(Wl_scales), _ptr(Wd), _ptr(Wd_scales),
+         _ptr(hact), _ptr(y), _ptr(ws))
+    st = load().sfx_dense_ffn(_stream(stream), wdt, ACTS[act], B, d, f, *p, ws.numel() if ws is not None else 0)
+    _check(st, "sfx_dense_ffn")
 
 
 def sfx_sparse_down_noalloc(Wd, idx, count, hact, y, Wd_scales=None, stream=None):

@@ -190,6 +190,33 @@ int sfx_sparse_down_noalloc(void* stream, int wdt, int B, int d, int f, const vo
                                         hact, y, scratch));
 }
 
+// ------------------------------------------------------------------------------ dense step
+
+size_t sfx_dense_ffn_ws(int wdt, int B, int d, int f) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32 || B < 1 || B > SFX_MAX_B || d < 1 || f < 1) return 0;
+  return sfx::dense_ws_bytes(wdt, B, d, f);
+}
+
+int sfx_dense_ffn(void* stream, int wdt, int act, int B, int d, int f, const void* x, const void* Wa,
+                  const void* Wa_scales, const float* ba, const void* Wl, const void* Wl_scales, const void* Wd,
+                  const void* Wd_scales, float* hact, float* y, void* ws, size_t ws_bytes) {
+  if (wdt < SFX_F32 || wdt > SFX_Q4G32) return SFX_E_DTYPE;
+  if (act != SFX_RELU && act != SFX_REGLU && act != SFX_RELU2) return SFX_E_DTYPE;
+  if (B < 1 || B > SFX_MAX_B || d < 1 || f < 1) return SFX_E_SHAPE;
+  if (!x || !Wa || !Wd || !hact || !y) return SFX_E_NULL;
+  if (act == SFX_REGLU && !Wl) return SFX_E_NULL;
+  if (wdt == SFX_Q4G32 && (!Wa_scales || !Wd_scales || (act == SFX_REGLU && !Wl_scales))) return SFX_E_NULL;
+  if (!row_ok(wdt, d)) return wdt == SFX_Q4G32 ? SFX_E_SHAPE : SFX_E_ALIGN;
+  if (!aligned16(x) || !aligned16(Wa) || !aligned16(Wd) || !aligned16(hact) || !aligned16(y) ||
+      (Wl && !aligned16(Wl)))
+    return SFX_E_ALIGN;
+  if (!sfx::up_supported(wdt, act, B) || !sfx::down_supported(wdt, B)) return SFX_E_UNSUPPORTED;
+  const int w = check_ws(ws, ws_bytes, sfx::dense_ws_bytes(wdt, B, d, f));
+  if (w != SFX_OK) return w;
+  return launch_status(sfx::launch_dense((hipStream_t)stream, wdt, act, B, d, f, x, Wa, Wa_scales, ba,
+                                         act == SFX_REGLU ? Wl : nullptr, Wl_scales, Wd, Wd_scales, hact, y, ws));
+}
+
 // ------------------------------------------------------------------------------ TAM
 
 size_t sfx_tam_ws(int G, int K) { return sfx::tam_ws_bytes(G, K); }

@@ -34,6 +34,10 @@ hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* 
                        const void* Wd_s, const int32_t* idx, const int32_t* count, int kmax,
                        const float* hact, float* y, void* ws);
 bool down_supported(int wdt, int B);
+size_t dense_ws_bytes(int wdt, int B, int d, int f);
+hipError_t launch_dense(hipStream_t s, int wdt, int act, int B, int d, int f, const void* x, const void* Wa,
+                        const void* Wa_s, const float* ba, const void* Wl, const void* Wl_s, const void* Wd,
+                        const void* Wd_s, float* hact, float* y, void* ws);
 // Static scratch of the down kernel for callers that cannot allocate: its size, and
 // its device address on the current device (looked up on the first call per device).
 constexpr size_t kDownScratchBytes = SFX_DOWN_SCRATCH_BYTES;

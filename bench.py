@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-calib", action="store_true",
                    help="use the generator's hot-first layers and closed-form thresholds instead of "
                         "raw-order layers calibrated on the device")
+    p.add_argument("--dense-switch", action="store_true",
+                   help="only the sparse/dense study (Falcon-40B-shaped layers, batch 8..64)")
     p.add_argument("--churn", action="store_true",
                    help="only the hot-region churn study (Falcon-40B-shaped layers, TAM vs Top-K)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -138,7 +140,7 @@ def popcount32(t):
 N_CAL = 1024
 
 
-def calibrated_layer(cfg, layer, dev, n_cal=N_CAL):
+def calibrated_layer(cfg, layer, dev, n_cal=N_CAL, keep_counts=False):
     """The offline calibration pass on a raw-order layer: thresholds at the
     configured density, activation counts and the hot-first table, from n_cal
     calibration tokens (a token stream disjoint from the measured one), then every
@@ -155,7 +157,10 @@ def calibrated_layer(cfg, layer, dev, n_cal=N_CAL):
     perm = r["perm"].cpu().numpy()
     keys = ("W2", "W2_s", "Wa", "Wa_s", "Wl", "Wl_s", "Wd", "Wd_s", "ba", "perm", "group")
     new = dataclasses.replace(layer, threshold=r["threshold"], p=layer.p[perm], **{k: c.get(k) for k in keys})
-    return new, {"threshold": r["threshold"], "active_share": r["active_share"]}
+    out = {"threshold": r["threshold"], "active_share": r["active_share"]}
+    if keep_counts:
+        out["counts"] = r["counts"]
+    return new, out
 
 
 def make_stack(cfg, L, dev, calibrate=True):
@@ -468,6 +473,100 @@ def hot_region_churn(dev, L=4, B=1, steps=512):
     return out
 
 
+def dense_bytes(cfg, B):
+    """Algorithmic bytes of one dense layer-step: every row of W_up (and W_gate),
+    the biases and every row of W_down, the tokens, activations and y."""
+    d, f = cfg.d, cfg.f
+    na = 2 if cfg.act == "reglu" else 1
+    er = row_bytes(cfg)
+    return B * d * e_bytes(cfg.pdtype) + na * f * er + f * 4 + 2 * B * f * 4 + f * er + B * d * 4
+
+
+def dense_switch_study(dev, L=4, steps=8, batches=(8, 16, 32, 48, 64)):
+    """Sparse step against the dense FFN (sfx_dense_ffn) on calibrated
+    Falcon-40B-shaped layers at several batch sizes: time per layer-step of each,
+    graph-captured; the bandwidth each path reaches; and the switch's choice from
+    the calibration frequencies (expected union) with those bandwidths, against
+    the measured faster path."""
+    import torch
+    import synthetic as S
+    from activation_sparse_ffn_amd import StepBuffers, run_layer
+    from activation_sparse_ffn_amd import _abi as A
+    from activation_sparse_ffn_amd.switch import SparseDenseSwitch, expected_union
+    cfg = S.CONFIGS["C5"]
+    say(f"dense switch: generating {L} layers of {cfg.workload}")
+    layers, cal = [], []
+    for l in range(L):
+        ly, c = calibrated_layer(cfg, S.make_layer(cfg, l, device=dev, order="raw"), dev, keep_counts=True)
+        layers.append(ly)
+        cal.append((c["counts"].double() / N_CAL).cpu().numpy())
+    # each layer has its own neurons: the expected union is averaged over layers
+    tens = [ly.tensors() for ly in layers]
+    rows = []
+
+    def timed(fn, n_layers):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s_ in range(steps):
+                fn(s_)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (steps * n_layers)
+
+    for B in batches:
+        xs = [S.make_tokens(cfg, l, steps, B, device=dev) for l in range(L)]
+        buf = StepBuffers(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.pred_storage, device=dev)
+
+        def sparse(s_):
+            for l in range(L):
+                run_layer(buf, tens[l], xs[l][s_], layers[l].threshold, cfg.act, tok_bits=False)
+
+        hact = torch.empty(cfg.f, B, dtype=torch.float32, device=dev)
+        y = torch.empty(B, cfg.d, dtype=torch.float32, device=dev)
+        ws = A.workspace(A.sfx_dense_ffn_ws(A.SFX_F16, B, cfg.d, cfg.f), dev)
+
+        def dense(s_):
+            for l in range(L):
+                t = tens[l]
+                A.sfx_dense_ffn(xs[l][s_], t["Wa"], t["ba"], t["Wd"], hact, y, ws, act=cfg.act)
+
+        us_s = timed(sparse, L)
+        ks = []
+        for s_ in range(steps):
+            for l in range(L):
+                run_layer(buf, tens[l], xs[l][s_], layers[l].threshold, cfg.act, tok_bits=False)
+                ks.append(buf.count.clone())
+        k = float(torch.cat(ks).double().mean().item())
+        buf.check_status()
+        us_d = timed(dense, L)
+        kb = kernel_bytes(cfg, B, k)
+        eu = float(np.mean([expected_union(pl, B) for pl in cal]))
+        rows.append({"batch": B, "mean_union": round(k, 1), "expected_union": round(eu, 1),
+                     "sparse_us": round(us_s, 2), "dense_us": round(us_d, 2),
+                     "sparse_GBps": round(sum(kb.values()) / (us_s * 1e-6) / 1e9, 1),
+                     "dense_GBps": round(dense_bytes(cfg, B) / (us_d * 1e-6) / 1e9, 1),
+                     "faster": "dense" if us_d < us_s else "sparse"})
+        say(f"dense switch B={B}: sparse {us_s:.1f} us, dense {us_d:.1f} us, union {k:.0f}")
+        del buf, hact, y, ws, xs
+        torch.cuda.empty_cache()
+    # the switch at each batch: the byte model with the bandwidths measured at that
+    # batch (both paths slow down as the products grow), on the expected union
+    for r in rows:
+        sw = SparseDenseSwitch(pred_bytes=(cfg.h * cfg.d + cfg.f * cfg.h) * pred_weight_bytes(cfg),
+                               row_bytes=2 * row_bytes(cfg) + 4, f=cfg.f,
+                               sparse_gbps=r["sparse_GBps"], dense_gbps=r["dense_GBps"])
+        r["switch_choice"] = "dense" if sw.use_dense(r["expected_union"]) else "sparse"
+        r["crossover_density"] = round(sw.crossover_k() / cfg.f, 4)
+    return {"workload": cfg.workload + ", calibrated", "layers": L, "steps": steps, "by_batch": rows}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -575,6 +674,9 @@ def main():
     if args.churn:
         print(json.dumps(hot_region_churn(dev)), flush=True)
         return
+    if args.dense_switch:
+        print(json.dumps(dense_switch_study(dev)), flush=True)
+        return
 
     def mode_for(cfg, B, pipeline):
         if pipeline:
@@ -647,6 +749,8 @@ def main():
         extra["live_pipeline"] = pipes
         extra["stream_read_ceiling"] = stream_probe(dev)
         extra["tam_hot_region"] = hot_region_churn(dev)
+        torch.cuda.empty_cache()
+        extra["dense_switch"] = dense_switch_study(dev)
         torch.cuda.empty_cache()
         result["extra"] = extra
 

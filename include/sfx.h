@@ -234,6 +234,28 @@ int sfx_sparse_down_noalloc(void* stream, int wdt, int B, int d, int f,
                             float* y);
 
 /* ---------------------------------------------------------------------------------
+ * sfx_dense_ffn -- the FFN over every neuron, without the predictor (PowerInfer page,
+ * Implementation: long inputs switch to dense GPU computation in the prefill
+ * stage; KAIROX page, Future work: choose sparse or dense kernels online from the
+ * batch).  For every neuron i and token b:
+ *
+ *   hact[i][b] = act(Wa[i] x_b + b_i) (ReGLU: relu(.) (Wl[i] x_b); squared ReLU),
+ *   y_b = sum_i hact[i][b] Wd[i]                                  (i ascending)
+ *
+ * It is what sfx_sparse_up / sfx_sparse_down compute for the list 0..f-1, with the
+ * same kernels, so it equals the sparse step whose mask holds every neuron.  It
+ * reads all rows of Wa (Wl) and Wd and no predictor weights: cheaper than the
+ * sparse step once the union of the batch's masks holds most neurons.
+ *   Arguments as sfx_sparse_up / sfx_sparse_down; hact [f][B] fp32 (written);
+ *   ws >= sfx_dense_ffn_ws(wdt, B, d, f) bytes, 256-byte aligned, any contents.
+ * ------------------------------------------------------------------------------- */
+size_t sfx_dense_ffn_ws(int wdt, int B, int d, int f);
+int sfx_dense_ffn(void* stream, int wdt, int act, int B, int d, int f, const void* x,
+                  const void* Wa, const void* Wa_scales, const float* ba,
+                  const void* Wl, const void* Wl_scales, const void* Wd, const void* Wd_scales,
+                  float* hact, float* y, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
  * sfx_tam_update -- temporal activation momentum over groups of 32 neurons (KAIROX
  * page, Core method: item 3, decisions per group with at most 1024 groups per layer;
  * item 4, TAM with tau = (1 - lambda) + eps; item 6, set-difference update).
@@ -369,7 +391,9 @@ int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const 
  * (same outputs, same layouts), with each layer's y complete before the next
  * layer's input is read.  Same passages as those four calls.
  *
- * One persistent workgroup per compute unit; phases are separated by grid
+ * One persistent workgroup per compute unit (the device must have 64, 128 or 256
+ * of them, else SFX_E_UNSUPPORTED; workgroup w computes the scores of neurons
+ * w + P j); phases are separated by grid
  * barriers in the workspace, so the grid must be resident on the device: the call
  * returns SFX_E_UNSUPPORTED when the occupancy query says one workgroup does not
  * fit on a compute unit, and kernels of other streams running at the same time

@@ -212,3 +212,19 @@ def test_hot_update_validation(lib):
     assert call(slot=None) == E_NULL and call(src=None) == E_NULL and call(gb=None) == E_NULL
     assert call(slot=P(0x10002)) == E_ALIGN
     assert call(dst=P(0x10004)) == E_ALIGN                  # the pointer arrays need 8-byte alignment
+
+
+def test_dense_validation(lib):
+    n = lib.sfx_dense_ffn_ws(1, 32, 8192, 32768)
+    assert n >= 32768 * 4 and lib.sfx_dense_ffn_ws(1, 0, 8192, 32768) == 0
+
+    def call(**k):
+        return lib.sfx_dense_ffn(None, k.get("wdt", 1), k.get("act", 0), k.get("B", 32), k.get("d", 8192), 32768,
+                                 GOOD, k.get("Wa", GOOD), None, GOOD, k.get("Wl", None), None, k.get("Wd", GOOD),
+                                 None, GOOD, GOOD, k.get("ws", P(0x100000)), k.get("wsn", n))
+    assert call(wdt=7) == E_DTYPE and call(act=3) == E_DTYPE
+    assert call(B=65) == E_SHAPE and call(B=0) == E_SHAPE
+    assert call(Wa=None) == E_NULL and call(Wd=None) == E_NULL and call(act=1) == E_NULL
+    assert call(wdt=3) == E_NULL                            # int4 needs its scale tables
+    assert call(Wd=ODD) == E_ALIGN
+    assert call(wsn=n - 1) == E_WORKSPACE and call(ws=P(0x100010)) == E_WORKSPACE
