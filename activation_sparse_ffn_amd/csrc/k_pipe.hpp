@@ -263,14 +263,22 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     const bool in_lds = k <= nid_cap;
     for (int g = g0; g < min(W, g0 + wpt); ++g) {
       s_pref[g] = pos;
-      uint32_t wd = s_uw[g];
-      if (in_lds)
-        while (wd) { s_nid[pos++] = 32 * g + __builtin_ctz(wd); wd &= wd - 1; }
-      else
-        pos += __popc(wd);
+      pos += __popc(s_uw[g]);
     }
     if (gt == 0) s_pref[W] = total;
     if (w == 0 && gt == 0) *Lj->count = k;
+    gather_sync();
+    // the list, one byte of a word per step, bytes interleaved over the threads, so
+    // the dense words of hot-first storage spread over many threads
+    if (in_lds) {
+      for (int bt = gt; bt < 4 * W; bt += kGT) {
+        const int g = bt >> 2, sh = 8 * (bt & 3);
+        const uint32_t word = s_uw[g];
+        uint32_t wd = (word >> sh) & 0xFFu;
+        uint32_t at = s_pref[g] + __popc(word & ((1u << sh) - 1u));
+        while (wd) { s_nid[at++] = 32 * g + sh + __builtin_ctz(wd); wd &= wd - 1; }
+      }
+    }
     gather_sync();
     return k;
   };

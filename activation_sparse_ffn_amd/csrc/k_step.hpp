@@ -763,14 +763,19 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     k = (int)total;
     k_prev = k;
     in_lds = k <= kNidCap;
-    if (in_lds) {
-      uint32_t pos = base;
-      uint32_t wd = w0;
-      while (wd) { s_nid[pos++] = 32 * g0 + __builtin_ctz(wd); wd &= wd - 1; }
-      wd = w1;
-      while (wd) { s_nid[pos++] = 32 * (g0 + 1) + __builtin_ctz(wd); wd &= wd - 1; }
-    }
     if (w == 0 && tid == 0) *Ld->count = k;
+    lds_barrier();
+    // the list, one byte of a word per step, bytes interleaved over the threads, so
+    // the dense words of hot-first storage spread over many threads
+    if (in_lds) {
+      for (int bt = tid; bt < 4 * W; bt += kNT) {
+        const int g = bt >> 2, sh = 8 * (bt & 3);
+        const uint32_t word = s_uw[g];
+        uint32_t wd = (word >> sh) & 0xFFu;
+        uint32_t at = s_pref[g] + __popc(word & ((1u << sh) - 1u));
+        while (wd) { s_nid[at++] = 32 * g + sh + __builtin_ctz(wd); wd &= wd - 1; }
+      }
+    }
     lds_barrier();
     // Own entries past `cap` of every workgroup (owner o: the set bits of its own
     // mask words in order, from entry cap on), ranked by owner through the prefix
