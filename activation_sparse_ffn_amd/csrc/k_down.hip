@@ -332,6 +332,87 @@ __global__ __launch_bounds__(kBlock) void k_down_cols(const uint8_t* __restrict_
   }
 }
 
+// ------------------------------------------------------------------ B <= 2, int4 rows
+// The column-tile kernel for int4 g32 rows: workgroup t owns the 32 columns of group
+// t (16 bytes of codes and one fp16 scale per row), one lane per row, kCU rows per
+// lane in flight; the scale folds into the activation (q s h as q (s h): only the
+// rounding order differs from the decoded product).  No partial sums: indices and
+// activations, then codes and scales, two dependent round trips (the slice kernel
+// also wrote and re-read 2 MB of partial tiles per call at the OPT-30B shape).
+template <int NB>
+__global__ __launch_bounds__(kBlock) void k_down_cols_q4(const uint8_t* __restrict__ Wd,
+                                                         const uint16_t* __restrict__ Wd_s,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ count, int kmax,
+                                                         const float* __restrict__ hact, int B, int d, int f,
+                                                         float* __restrict__ y, int ntiles) {
+  constexpr int kCU = NB == 1 ? 16 : 8;   // rows per lane in flight
+  constexpr int V = 32 * NB;              // sums per lane: 32 columns x NB tokens
+  __shared__ float s_sum[kWavesPerBlock][V];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int w = blockIdx.x, P = gridDim.x;
+  const int tile = (P % 8 == 0 && P == ntiles) ? (w & 7) * (P >> 3) + (w >> 3) : w;
+  const size_t rb = (size_t)d >> 1;       // code bytes per row
+  const int ng = d >> 5;                  // scales per row
+  const int k = min(*count, kmax);
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  for (int r0 = threadIdx.x; r0 < k; r0 += kBlock * kCU) {
+    int nid[kCU];
+    float hv[kCU][NB];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int r = min(r0 + u * kBlock, k - 1);
+      nid[u] = idx[r];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) hv[u][b] = hact[(size_t)r * B + min(b, B - 1)];
+    }
+    Raw<16> wv[kCU];
+    uint16_t sc[kCU];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int i = (unsigned)nid[u] < (unsigned)f ? nid[u] : 0;
+      wv[u] = load_raw<16>(Wd + (size_t)i * rb + (size_t)tile * 16);
+      sc[u] = Wd_s[(size_t)i * ng + tile];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      if (r0 + u * kBlock < k && (unsigned)nid[u] < (unsigned)f) {
+        const float s = (float)__builtin_bit_cast(_Float16, sc[u]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            const float hs = hv[u][b] * s;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                acc[b * 32 + q * 8 + e] =
+                    fmaf((float)((int32_t)(wv[u].w[q] << (28 - 4 * e)) >> 28), hs, acc[b * 32 + q * 8 + e]);
+          }
+        }
+      }
+    }
+  }
+  // sum over the 64 lanes of each wave (halving exchanges), then the four waves in
+  // order: lane L ends with sum index L >> (6 - log2 V)
+  const float v = wave_reduce_multi<V>(acc);
+  if ((lane & (kWave / V - 1)) == 0) s_sum[wave][lane >> (6 - ilog2c(V))] = v;
+  __syncthreads();
+  if (threadIdx.x < V) {
+    const int b = threadIdx.x >> 5, c = tile * 32 + (threadIdx.x & 31);
+    if (b < B && c < d) {
+      float t = 0.f;
+#pragma unroll
+      for (int vv = 0; vv < kWavesPerBlock; ++vv) t += s_sum[vv][threadIdx.x];
+      y[(size_t)b * d + c] = t;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ B >= 3
 // From 3 tokens on the products run on the matrix cores: v_mfma_f32_16x16x4_f32
 // (fp32 operands, so the fp32 activations are used as they are and the 16-bit
@@ -636,6 +717,14 @@ hipError_t launch_down(hipStream_t s, int wdt, int B, int d, int f, const void* 
     case DT_F16: return dispatch<TF16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
     case DT_BF16: return dispatch<TBF16>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
     case DT_Q4:
+      if (cols_eligible(B)) {
+        const int ntiles = d / 32;
+        const uint8_t* W = (const uint8_t*)Wd;
+        const uint16_t* S = (const uint16_t*)Wd_s;
+        if (B == 1) k_down_cols_q4<1><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, S, idx, count, kmax, hact, B, d, f, y, ntiles);
+        else k_down_cols_q4<2><<<dim3(ntiles), dim3(kBlock), 0, s>>>(W, S, idx, count, kmax, hact, B, d, f, y, ntiles);
+        return hipGetLastError();
+      }
       switch (nb_class(B)) {
         case 1: return run<TQ4, 1>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
         case 2: return run<TQ4, 2>(s, p, B, d, f, Wd, Wd_s, idx, count, kmax, hact, y, ws);
