@@ -675,143 +675,83 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
     }
     lds_barrier();
-    // Union words in the standard layout (bit b of word g = neuron 32 g + b).  With
-    // P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and belong to
-    // owners 32 (g mod P/32) + b.  Lane L holds the mask word c of owner 64 q + L
-    // (bits j = 32 c + t); a 32 x 32 bit transpose within each half wave (five
-    // exchange stages) leaves in lane t the bits j = 32 c + t of owners 64 q .. + 31
-    // (lanes 0..31) or 64 q + 32 .. + 63 (lanes 32..63): words j P/32 + 2q (+1).
-    {
-      const int wv = __builtin_amdgcn_readfirstlane(wave);
-      const int nq = P >> 6;
-      const int nr2m = (f + P - 1) / P;
-      for (int it = wv; it < nq * nwm; it += kNW) {
-        const int q = it % nq, c = it / nq;
-        uint32_t x = s_raw[(64 * q + lane) * nwm + c];
-        x = transpose_step(x, lane, 16, 0xFFFF0000u);
-        x = transpose_step(x, lane, 8, 0xFF00FF00u);
-        x = transpose_step(x, lane, 4, 0xF0F0F0F0u);
-        x = transpose_step(x, lane, 2, 0xCCCCCCCCu);
-        x = transpose_step(x, lane, 1, 0xAAAAAAAAu);
-        const int j = 32 * c + (lane & 31);
-        const int g = j * (P >> 5) + 2 * q + (lane >> 5);
-        if (j < nr2m && g < W) s_uw[g] = x;
-      }
-    }
-    lds_barrier();
-    // outputs of this workgroup: union words g = w + P m and, when asked for, the
-    // per-token words (bit b from owner 32 (g mod P/32) + b, one tagged word per lane)
-    for (int g = w + P * tid; g < W; g += P * kNT) Ld->union_bits[g] = s_uw[g];
-    if (Ld->tok_bits != nullptr && wave == 0) {
-      for (int g = w; g < W; g += P) {
-        const int j = g / (P >> 5), c = g - j * (P >> 5);
-        for (int b = 0; b < B; ++b) {
-          unsigned long long tv[1];
-          auto valid = [&](int i) { (void)i; return lane < 32; };
-          auto addr = [&](int i) {
-            (void)i;
-            return p.uni + (size_t)(32 * c + (lane & 31)) * p.us + nwm * (1 + b) + (j >> 5);
-          };
-          poll_tagged_if<1, decltype(valid), decltype(addr), kStepPS>(tv, valid, addr, tag, p.err);
-          const uint64_t bal = __ballot(lane < 32 && (((uint32_t)tv[0] >> (j & 31)) & 1u) != 0u);
-          if (lane == 0) Ld->tok_bits[(size_t)b * W + g] = (uint32_t)bal;
-        }
-      }
-    }
-    // thread t owns words [wpt t, wpt t + wpt): one word when W <= 512, so a full
-    // (hot) word costs 32 steps of the extraction below, not 64
-    const int wpt = W <= kNT ? 1 : 2;
-    const int g0 = wpt * tid;
-    const uint32_t w0 = g0 < W ? s_uw[g0] : 0u;
-    const uint32_t w1 = wpt == 2 && g0 + 1 < W ? s_uw[g0 + 1] : 0u;
-    const uint32_t cnt0 = __popc(w0), cnt = cnt0 + __popc(w1);
-    // the same scan also counts, per owner o = tid < P, its own entries past
-    // `cap` (the rows the split below takes over): both counts fit in 16 bits
-    // (k <= f <= 32 kMaxWords), so they are scanned packed in one word
-    uint32_t ovc = 0;
+    // Owner counts, scanned once: c_o (active rows of owner o) and, packed in the
+    // same word, the owner's rows past `cap` (taken over by the split below); both
+    // fit in 16 bits (k <= f <= 32 kMaxWords).  The exclusive prefix of c_o places
+    // owner o's rows at positions [s_opre[o], s_opre[o + 1]) of an owner-major list
+    // (owner ascending, then row ascending), which the down phase walks: it needs
+    // no transposition or global scan first.
     uint32_t* s_own = reinterpret_cast<uint32_t*>(s_red) + 512;   // [P] own rows done first
-    if (tid < P) {
-      uint32_t c = 0;
-      for (int m = 0; m < nwm; ++m) c += __popc(s_raw[tid * nwm + m]);
-      ovc = c > (uint32_t)cap ? c - (uint32_t)cap : 0u;
-      s_own[tid] = c - ovc;
-    }
-    const uint32_t pk = cnt | (ovc << 16);
-    uint32_t inc = pk;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t n = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += n;
-    }
-    if (lane == kWave - 1) s_wt[wave] = inc;
-    lds_barrier();
-    uint32_t before_pk = 0, total_pk = 0;
-#pragma unroll
-    for (int v = 0; v < kNW; ++v) {
-      const uint32_t t = s_wt[v];
-      if (v < wave) before_pk += t;
-      total_pk += t;
-    }
-    const uint32_t base_pk = before_pk + inc - pk;
-    uint32_t* s_ovp = reinterpret_cast<uint32_t*>(s_red);     // [P + 1] owner prefix, free in phase C
-    if (tid < P) s_ovp[tid] = base_pk >> 16;
-    if (tid == 0) s_ovp[P] = total_pk >> 16;
-    const uint32_t base = base_pk & 0xffffu, total = total_pk & 0xffffu;
-    if (g0 < W) s_pref[g0] = base;
-    if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
-    if (tid == 0) s_pref[W] = total;
-    k = (int)total;
-    k_prev = k;
-    in_lds = k <= kNidCap;
-    if (w == 0 && tid == 0) *Ld->count = k;
-    lds_barrier();
-    // the list, one byte of a word per step, bytes interleaved over the threads, so
-    // the dense words of hot-first storage spread over many threads
-    if (in_lds) {
-      for (int bt = tid; bt < 4 * W; bt += kNT) {
-        const int g = bt >> 2, sh = 8 * (bt & 3);
-        const uint32_t word = s_uw[g];
-        uint32_t wd = (word >> sh) & 0xFFu;
-        uint32_t at = s_pref[g] + __popc(word & ((1u << sh) - 1u));
-        while (wd) { s_nid[at++] = 32 * g + sh + __builtin_ctz(wd); wd &= wd - 1; }
-      }
-    }
-    lds_barrier();
-    // Own entries past `cap` of every workgroup (owner o: the set bits of its own
-    // mask words in order, from entry cap on), ranked by owner through the prefix
-    // s_ovp from the scan above, fill the workgroups up to T = ceil(k / P) rows
-    // each: workgroup w takes the T - own_w overflow ranks after those of
-    // workgroups 0..w-1 (each wave sums the deficits before w itself).  Since
-    // P T >= k the deficits cover every overflow rank, and no workgroup does more
-    // than max(T, cap) up rows.
+    uint32_t* s_ovp = reinterpret_cast<uint32_t*>(s_red);         // [P + 1] overflow prefix
+    uint32_t* s_opre = reinterpret_cast<uint32_t*>(s_nid) + kNidCap - (kMaxP + 1);   // [P + 1]
+    int32_t* s_onid = s_nid;                                      // owner-major list
+    const int onid_cap = kNidCap - (kMaxP + 1);
     {
-      const int nov = (int)s_ovp[P];             // overflow rows of all workgroups
-      const int fair = (k + P - 1) / P;          // T
-      int dsum = 0;
-      for (int o = lane; o < w; o += kWave) dsum += max(fair - (int)s_own[o], 0);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, kWave);
-      const int q0 = min(dsum, nov), q1 = min(dsum + max(fair - (int)s_own[w], 0), nov);
-      for (int r = q0 + wave; r < q1; r += kWork) {
-        int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if ((int)s_ovp[mid] <= r) lo = mid; else hi = mid;
-        }
-        int m = 0, rem = cap + (r - (int)s_ovp[lo]);
-        uint32_t um = s_raw[lo * nwm];
-        while (rem >= __popc(um)) { rem -= __popc(um); um = s_raw[lo * nwm + (++m)]; }
-        for (int i = 0; i < rem; ++i) um &= um - 1;
-        up_row(lo + P * (32 * m + __builtin_ctz(um)));
+      uint32_t c = 0, ovc = 0;
+      if (tid < P) {
+        for (int m = 0; m < nwm; ++m) c += __popc(s_raw[tid * nwm + m]);
+        ovc = c > (uint32_t)cap ? c - (uint32_t)cap : 0u;
+        s_own[tid] = c - ovc;
       }
+      const uint32_t pk = c | (ovc << 16);
+      uint32_t inc = pk;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t n = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += n;
+      }
+      if (lane == kWave - 1) s_wt[wave] = inc;
+      lds_barrier();
+      uint32_t before_pk = 0, total_pk = 0;
+#pragma unroll
+      for (int v = 0; v < kNW; ++v) {
+        const uint32_t t = s_wt[v];
+        if (v < wave) before_pk += t;
+        total_pk += t;
+      }
+      const uint32_t base_pk = before_pk + inc - pk;
+      k = (int)(total_pk & 0xffffu);
+      k_prev = k;
+      in_lds = k <= onid_cap;
+      if (tid < P) {
+        s_ovp[tid] = base_pk >> 16;
+        s_opre[tid] = base_pk & 0xffffu;
+        if (in_lds) {                            // owner tid's rows, ascending
+          uint32_t at = base_pk & 0xffffu;
+          for (int m = 0; m < nwm; ++m) {
+            uint32_t wd = s_raw[tid * nwm + m];
+            while (wd) { s_onid[at++] = tid + P * (32 * m + __builtin_ctz(wd)); wd &= wd - 1; }
+          }
+        }
+      }
+      if (tid == 0) {
+        s_ovp[P] = total_pk >> 16;
+        s_opre[P] = total_pk & 0xffffu;
+      }
+      if (w == 0 && tid == 0) *Ld->count = k;
+      lds_barrier();
     }
-
+    // neuron at owner-major position q: from the LDS list, or (long lists) by a
+    // search of the owner prefix and a walk over that owner's set bits
+    auto pos_to_neuron = [&](int q) -> int {
+      if (in_lds) return s_onid[q];
+      int lo = 0, hi = P;                        // s_opre[lo] <= q < s_opre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)s_opre[mid] <= q) lo = mid; else hi = mid;
+      }
+      int m = 0, rem = q - (int)s_opre[lo];
+      uint32_t um = s_raw[lo * nwm];
+      while (rem >= __popc(um)) { rem -= __popc(um); um = s_raw[lo * nwm + (++m)]; }
+      for (int i = 0; i < rem; ++i) um &= um - 1;
+      return lo + P * (32 * m + __builtin_ctz(um));
+    };
 
     // ---------------------------------------------------------------- phase D
     {
       // Down-phase geometry: workers are waves [0, kWork); lane group j = lane mod
       // nct (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct
-      // walks the active rows.
+      // walks the active rows in owner-major order.
       const int nct = p.cw / 8;
       const int d_tile = tile_of(w, P);
       const int d_tiles = (d + p.cw - 1) / p.cw;   // tiles that hold columns
@@ -824,30 +764,124 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const uint8_t* Wd = (const uint8_t*)Ld->Wd;
       Raw<16> wdv[kRD];
       int nid[kRD];
-      auto load_wd = [&](int rb) {                 // kRD rows at a time, rb < k
-        // ranks past k are clamped to k - 1 (loaded, never used), so the loads
+      auto load_wd = [&](int qb) {                 // kRD positions at a time, qb < k
+        // positions past k are clamped to k - 1 (loaded, never used), so the loads
         // are issued back to back without branches
-        if (in_lds) {
 #pragma unroll
-          for (int u = 0; u < kRD; ++u) nid[u] = s_nid[min(rb + u * d_rs, k - 1)];
-        } else {
-#pragma unroll
-          for (int u = 0; u < kRD; ++u) nid[u] = rank_to_neuron(min(rb + u * d_rs, k - 1), s_pref, s_uw, W);
-        }
+        for (int u = 0; u < kRD; ++u) nid[u] = pos_to_neuron(min(qb + u * d_rs, k - 1));
 #pragma unroll
         for (int u = 0; u < kRD; ++u) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
       };
-      // the workers' first batch goes out before the activations are polled
+      // the workers' first batch goes out before anything else is waited for; the
+      // outputs in the standard layout are built while it is in flight
       if (d_ok && d_rr < k) load_wd(d_rr);
+
+      // Union words in the standard layout (bit b of word g = neuron 32 g + b).
+      // With P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and
+      // belong to owners 32 (g mod P/32) + b.  Lane L holds the mask word c of owner
+      // 64 q + L (bits j = 32 c + t); a 32 x 32 bit transpose within each half wave
+      // (five exchange stages) leaves in lane t the bits j = 32 c + t of owners
+      // 64 q .. + 31 (lanes 0..31) or 64 q + 32 .. + 63 (lanes 32..63): words
+      // j P/32 + 2q (+1).
+      {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int nq = P >> 6;
+        const int nr2m = (f + P - 1) / P;
+        for (int it = wv; it < nq * nwm; it += kNW) {
+          const int q = it % nq, c = it / nq;
+          uint32_t x = s_raw[(64 * q + lane) * nwm + c];
+          x = transpose_step(x, lane, 16, 0xFFFF0000u);
+          x = transpose_step(x, lane, 8, 0xFF00FF00u);
+          x = transpose_step(x, lane, 4, 0xF0F0F0F0u);
+          x = transpose_step(x, lane, 2, 0xCCCCCCCCu);
+          x = transpose_step(x, lane, 1, 0xAAAAAAAAu);
+          const int j = 32 * c + (lane & 31);
+          const int g = j * (P >> 5) + 2 * q + (lane >> 5);
+          if (j < nr2m && g < W) s_uw[g] = x;
+        }
+      }
+      lds_barrier();
+      // outputs of this workgroup: union words g = w + P m and, when asked for, the
+      // per-token words (bit b from owner 32 (g mod P/32) + b, one tagged word per lane)
+      for (int g = w + P * tid; g < W; g += P * kNT) Ld->union_bits[g] = s_uw[g];
+      if (Ld->tok_bits != nullptr && wave == 0) {
+        for (int g = w; g < W; g += P) {
+          const int j = g / (P >> 5), c = g - j * (P >> 5);
+          for (int b = 0; b < B; ++b) {
+            unsigned long long tv[1];
+            auto valid = [&](int i) { (void)i; return lane < 32; };
+            auto addr = [&](int i) {
+              (void)i;
+              return p.uni + (size_t)(32 * c + (lane & 31)) * p.us + nwm * (1 + b) + (j >> 5);
+            };
+            poll_tagged_if<1, decltype(valid), decltype(addr), kStepPS>(tv, valid, addr, tag, p.err);
+            const uint64_t bal = __ballot(lane < 32 && (((uint32_t)tv[0] >> (j & 31)) & 1u) != 0u);
+            if (lane == 0) Ld->tok_bits[(size_t)b * W + g] = (uint32_t)bal;
+          }
+        }
+      }
+      // prefix of the standard words (the rank of a neuron in the ascending list =
+      // s_pref[g] + its set bits below it in word g); thread t owns words [wpt t, +wpt)
+      {
+        const int wpt = W <= kNT ? 1 : 2;
+        const int g0 = wpt * tid;
+        const uint32_t cnt0 = g0 < W ? __popc(s_uw[g0]) : 0u;
+        const uint32_t cnt = cnt0 + (wpt == 2 && g0 + 1 < W ? __popc(s_uw[g0 + 1]) : 0u);
+        uint32_t inc = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t n = __shfl_up(inc, o, kWave);
+          if (lane >= o) inc += n;
+        }
+        if (lane == kWave - 1) s_wt[wave] = inc;
+        lds_barrier();
+        uint32_t before = 0;
+#pragma unroll
+        for (int v = 0; v < kNW; ++v)
+          if (v < wave) before += s_wt[v];
+        const uint32_t base = before + inc - cnt;
+        if (g0 < W) s_pref[g0] = base;
+        if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
+        if (tid == 0) s_pref[W] = (uint32_t)k;
+        lds_barrier();
+      }
+      // Own entries past `cap` of every workgroup (owner o: the set bits of its own
+      // mask words in order, from entry cap on), ranked by owner through the prefix
+      // s_ovp, fill the workgroups up to T = ceil(k / P) rows each: workgroup w takes
+      // the T - own_w overflow ranks after those of workgroups 0..w-1 (each wave sums
+      // the deficits before w itself).  Since P T >= k the deficits cover every
+      // overflow rank, and no workgroup does more than max(T, cap) up rows.
+      {
+        const int nov = (int)s_ovp[P];             // overflow rows of all workgroups
+        const int fair = (k + P - 1) / P;          // T
+        int dsum = 0;
+        for (int o = lane; o < w; o += kWave) dsum += max(fair - (int)s_own[o], 0);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, kWave);
+        const int q0 = min(dsum, nov), q1 = min(dsum + max(fair - (int)s_own[w], 0), nov);
+        for (int r = q0 + wave; r < q1; r += kWork) {
+          int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)s_ovp[mid] <= r) lo = mid; else hi = mid;
+          }
+          int m = 0, rem = cap + (r - (int)s_ovp[lo]);
+          uint32_t um = s_raw[lo * nwm];
+          while (rem >= __popc(um)) { rem -= __popc(um); um = s_raw[lo * nwm + (++m)]; }
+          for (int i = 0; i < rem; ++i) um &= um - 1;
+          up_row(lo + P * (32 * m + __builtin_ctz(um)));
+        }
+      }
+
       float yacc[NB * 8];
 #pragma unroll
       for (int i = 0; i < NB * 8; ++i) yacc[i] = 0.f;
       if (d_ok) {
-        for (int rb = d_rr; rb < k; rb += d_rs * kRD) {
-          if (rb != d_rr) load_wd(rb);
+        for (int qb = d_rr; qb < k; qb += d_rs * kRD) {
+          if (qb != d_rr) load_wd(qb);
           unsigned long long hv[kRD * NB];
-          const int nrow = min(kRD, (k - rb + d_rs - 1) / d_rs);
-          // entry u NB + b: activation of rank rb + u d_rs, token b
+          const int nrow = min(kRD, (k - qb + d_rs - 1) / d_rs);
+          // entry u NB + b: activation of position qb + u d_rs, token b
           auto valid = [&](int i) { return i / NB < nrow && i % NB < B; };
           auto addr = [&](int i) { return p.hact + (size_t)nid[i / NB] * B + min(i % NB, B - 1); };
           poll_tagged_if<kRD * NB, decltype(valid), decltype(addr), kStepPS>(hv, valid, addr, tag, p.err);
@@ -856,12 +890,15 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           if (d_j == 0) {
 #pragma unroll
             for (int u = 0; u < kRD; ++u) {
-              const int r = rb + u * d_rs;
-              if (u < nrow && r % d_tiles == d_tile) {
-                Ld->idx[r] = nid[u];
+              if (u < nrow) {
+                const int n = nid[u], g = n >> 5;
+                const int r = (int)s_pref[g] + __popc(s_uw[g] & ((1u << (n & 31)) - 1u));
+                if (r % d_tiles == d_tile) {
+                  Ld->idx[r] = n;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                  if (b < B) Ld->hact[(size_t)r * B + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+                  for (int b = 0; b < NB; ++b)
+                    if (b < B) Ld->hact[(size_t)r * B + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+                }
               }
             }
           }
