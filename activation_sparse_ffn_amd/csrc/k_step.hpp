@@ -288,37 +288,52 @@ __device__ __forceinline__ void prefetch_w2(const StepParams& p, CLayer* Ld, uin
 
 // The fused step's W2 rows: workgroup w owns rows w + P j (j < nr2), strided over
 // the workgroups, so hot-first storage spreads the most active neurons evenly
-// over them; own row q lands at s_w2 + q * (h/8) * 16, like prefetch_w2.
-__device__ __forceinline__ void prefetch_w2_rows(const StepParams& p, CLayer* Ld, uint8_t* s_w2) {
+// over them; own row q lands at s_w2 + q * (h/8) * 16, like prefetch_w2.  Waves
+// [wlo, whi) load own rows [q_lo, min(q_hi, nr2)), 16 bytes per lane.
+__device__ __forceinline__ void prefetch_w2_rows(const StepParams& p, CLayer* Ld, uint8_t* s_w2, int wlo, int whi,
+                                                 int q_lo, int q_hi) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int w = blockIdx.x;
   const int P = gridDim.x;
-  if (wave >= kAW && wave < kCW && p.w2_lds != 0) {
+  if (wave >= wlo && wave < whi && p.w2_lds != 0) {
     const uint8_t* W2 = (const uint8_t*)Ld->W2;
     const int nch2 = p.h / 8;
     const size_t rb2 = (size_t)p.h * 2;
     const int nr2 = w < p.f ? (p.f - w + P - 1) / P : 0;
-    const int items = nr2 * nch2;
-    constexpr int kStride = (kCW - kAW) * kWave;
-    const int i_first = (wave - kAW) * kWave + lane;
+    const int q_end = min(nr2, q_hi);
+    const int items = max(q_end - q_lo, 0) * nch2;
+    uint8_t* const dst = s_w2 + (size_t)q_lo * nch2 * 16;
+    const int stride = (whi - wlo) * kWave;
+    const int i_first = (wave - wlo) * kWave + lane;
     int q = i_first / nch2, c = i_first - q * nch2;
-    const int dq = kStride / nch2, dc = kStride - dq * nch2;
+    q += q_lo;
+    const int dq = stride / nch2, dc = stride - dq * nch2;
 #pragma unroll 1
-    for (int i0 = (wave - kAW) * kWave; i0 < items; i0 += kStride) {
+    for (int i0 = (wave - wlo) * kWave; i0 < items; i0 += stride) {
       if (i0 + lane < items) {
         int row = w + P * q;
         if (row >= p.f) row = p.f - 1;       // never: q < nr2
         __builtin_amdgcn_global_load_lds((const void*)(W2 + (size_t)row * rb2 + (size_t)c * 16),
-                                         (__attribute__((address_space(3))) void*)(s_w2 + (size_t)i0 * 16), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(dst + (size_t)i0 * 16), 16, 0, 0);
       }
       q += dq;
       c += dc;
       if (c >= nch2) { c -= nch2; ++q; }
     }
   }
+}
+#ifndef SFX_W2_LATE
+#define SFX_W2_LATE 2
+#endif
+// Own W2 rows [w2_split, nr2) that waves 0..kAW-1 load once their W1 rows are done
+// (the last SFX_W2_LATE eighths); waves kAW.. load [0, w2_split) from the start of
+// the layer.
+__device__ __forceinline__ int w2_split(int f, int P) {
+  const int nr2 = (f + P - 1) / P;
+  return nr2 - (nr2 * SFX_W2_LATE + 7) / 8;
 }
 
 // One stage of a 32 x 32 bit-matrix transpose held one row per lane (each half
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   int k_prev = -1;                           // active neurons of the previous layer
   Raw<16> w1r[kU];
   prefetch_w1<kU>(p, (CLayer*)p.layers, w1r);
-  prefetch_w2_rows(p, (CLayer*)p.layers, s_w2);
+  prefetch_w2_rows(p, (CLayer*)p.layers, s_w2, kAW, kNW, 0, 1 << 30);
   for (int l = 0; l < p.L; ++l) {
     const uint32_t tag = e0 + (uint32_t)l + 1u;
     CLayer* Ld = (CLayer*)p.layers + l;
@@ -411,9 +426,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         group_sync(&s_grp, g0 + kAW, p.err);                  // inputs requested
         if (x_lds) wait_memory();
         group_sync(&s_grp, g0 + 2 * kAW, p.err);              // inputs landed
-      } else if (l > 0 && wave < kCW) {
+      } else if (l > 0) {
         lds_wait_at_least(&s_grp, g0 + kAW, p.err);
-        prefetch_w2_rows(p, Ld, s_w2);
+        prefetch_w2_rows(p, Ld, s_w2, kAW, kNW, 0, w2_split(f, P));
       }
       float acc[NB];
 #pragma unroll
@@ -455,6 +470,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           st_tagged(p.hid + (size_t)w * kHidBlock + wave * NB + b, tag, __float_as_uint(fmaxf(v, 0.f)));
       }
       if (wave < kAW) group_sync(&s_grp, g0 + 3 * kAW, p.err);  // inputs read: s_x is reused in phase B
+      // the rest of this layer's W2 rows (their waits fall in the scores phase,
+      // which needs them anyway)
+      if (l > 0) prefetch_w2_rows(p, Ld, s_w2, 0, kAW, w2_split(f, P), 1 << 30);
     }
     // ---------------------------------------------------------------- phase B
     {
@@ -468,7 +486,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
-      if (w2_lds && wave >= kAW && wave < kCW) {
+      if (w2_lds && wave >= kAW) {
         wait_memory();                         // this wave's LDS rows have landed
       }
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows

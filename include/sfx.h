@@ -388,8 +388,11 @@ int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const 
 /* ---------------------------------------------------------------------------------
  * sfx_ffn_step -- the whole step for L layers in one launch: for each layer in order,
  * exactly what sfx_predict, sfx_compact, sfx_sparse_up and sfx_sparse_down compute
- * (same outputs, same layouts), with each layer's y complete before the next
- * layer's input is read.  Same passages as those four calls.
+ * (same outputs, same layouts), one layer after the other behind grid barriers.
+ * Same passages as those four calls.  The data behind every layer's x must be in
+ * place when the launch starts: a layer's x may not be an earlier layer's y of the
+ * same launch (outputs are plain stores, visible to other compute units only once
+ * the kernel has ended).
  *
  * One persistent workgroup per compute unit (the device must have 64, 128 or 256
  * of them, else SFX_E_UNSUPPORTED; workgroup w computes the scores of neurons
