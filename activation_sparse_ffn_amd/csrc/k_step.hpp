@@ -365,6 +365,56 @@ __device__ __forceinline__ int own_words_max(int f, int P) { return (((f + P - 1
   (void)lane; (void)wave; (void)P; (void)B; (void)d; (void)h; (void)f; (void)W; \
   (void)nch1; (void)nch2; (void)rb1; (void)rb2
 
+// Tile shares of the down phase: layer l's share of workgroup w (tile w / dsplit,
+// 64 columns x NB tokens) sits in buffer l mod 2; a workgroup can only be one
+// layer ahead of another, so layer l + 2 cannot overwrite it before the share is
+// summed in layer l + 1.  The tile's first workgroup adds its dsplit shares in
+// share order: wave kAW + b takes token b, lane = column, entry s of yv = share s.
+__device__ __forceinline__ bool tile_y_mine(const StepParams& p) {
+  const int b = (int)(threadIdx.x >> 6) - kAW;
+  return b >= 0 && b < p.B && blockIdx.x % p.dsplit == 0 && (int)blockIdx.x / p.dsplit < p.dtiles;
+}
+template <int NB>
+__device__ __forceinline__ const unsigned long long* tile_y_addr(const StepParams& p, int lp, int s) {
+  const int lane = threadIdx.x & (kWave - 1), b = (int)(threadIdx.x >> 6) - kAW;
+  return p.ypart + ((size_t)(lp & 1) * gridDim.x + blockIdx.x + min(s, p.dsplit - 1)) * (64 * NB) + b * 64 + lane;
+}
+template <int NB>
+__device__ __forceinline__ void tile_y_issue(const StepParams& p, int lp, unsigned long long (&yv)[8]) {
+  if (!tile_y_mine(p)) return;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) yv[s] = ld_agent64(tile_y_addr<NB>(p, lp, s));
+}
+// Checks the tags (stale words are polled again, bounded), adds the shares and
+// writes y of layer lp (token kAW - wave, the lane's column).
+template <int NB>
+__device__ __forceinline__ void tile_y_sum(const StepParams& p, int lp, uint32_t tagp, unsigned long long (&yv)[8]) {
+  if (!tile_y_mine(p)) return;
+  for (int spins = 0;; ++spins) {
+    bool stale = false;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) stale |= s < p.dsplit && !tag_ok(yv[s], tagp);
+    if (!stale) break;
+    if (spins > kSpin || ((spins & 255) == 255 && ld_agent(p.err) != 0u)) {
+      store_through(p.err, 3u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < p.dsplit && !tag_ok(yv[s], tagp)) yv[s] = ld_agent64(tile_y_addr<NB>(p, lp, s));
+  }
+  const int col = ((int)blockIdx.x / p.dsplit) * 64 + (int)(threadIdx.x & (kWave - 1));
+  const int b = (int)(threadIdx.x >> 6) - kAW;
+  if (col < p.d) {
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < p.dsplit) sum += __uint_as_float((uint32_t)yv[s]);
+    ((CLayer*)p.layers + lp)->y[(size_t)b * p.d + col] = sum;
+  }
+}
+
 // T: TF16 or TBF16.  NB: token class (1, 2, 4).  DL: 1 for d <= 4096.
 template <class T, int NB, bool REGLU, int DL>
 __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
@@ -486,9 +536,13 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
+      // the previous layer's tile shares (long written) land while the W2 rows do
+      unsigned long long yv[8];
+      if (l > 0) tile_y_issue<NB>(p, l - 1, yv);
       if (w2_lds && wave >= kAW) {
         wait_memory();                         // this wave's LDS rows have landed
       }
+      if (l > 0) tile_y_sum<NB>(p, l - 1, tag - 1u, yv);
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
       // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row]
       constexpr int kPT = kAW * kWave;
@@ -664,14 +718,14 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       int own_k = 0;
       for (int m = 0; m < nwo; ++m) own_k += __popc(own_word(m));
       const int own_n = min(own_k, cap);
-      for (int e = wave; e < own_n; e += kWork) {
-        // entry e of the own list: word m, its rem-th set bit
+      auto own_entry = [&](int e) {              // entry e of the own list: word m, its rem-th set bit
         int m = 0, rem = e;
         uint32_t um = own_word(0);
         while (rem >= __popc(um)) { rem -= __popc(um); um = own_word(++m); }
         for (int i = 0; i < rem; ++i) um &= um - 1;
-        up_row(w + P * (32 * m + __builtin_ctz(um)));
-      }
+        return w + P * (32 * m + __builtin_ctz(um));
+      };
+      for (int e = wave; e < own_n; e += kWork) up_row(own_entry(e));
     }
     // thread o polls the union words of owner o into s_raw[o][m] (zero past the
     // owner's words); s_w2 is free from the end of phase B to the next layer
@@ -767,32 +821,37 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 
     // ---------------------------------------------------------------- phase D
     {
-      // Down-phase geometry: workers are waves [0, kWork); lane group j = lane mod
-      // nct (nct <= 2) reads columns c0 + 8 j, lane slot wave * 64/nct + lane / nct
-      // walks the active rows in owner-major order.
-      const int nct = p.cw / 8;
-      const int d_tile = tile_of(w, P);
-      const int d_tiles = (d + p.cw - 1) / p.cw;   // tiles that hold columns
-      const int c0 = d_tile * p.cw;
-      const int d_j = lane & (nct - 1);
-      const int d_rr = wave * (kWave / nct) + lane / nct;
-      const int d_rs = kWork * (kWave / nct);
+      // Down-phase geometry: workgroup w takes the column tile d_tile = w / dsplit
+      // (64 columns: 128 bytes, one line, of every active row) and the positions
+      // d_sub + dsplit i of the owner-major list (d_sub = w mod dsplit).  The same
+      // bytes read as 32-byte slices of every row took about three times as long:
+      // a compute unit keeps only so many line requests in flight.  Lane group
+      // j = lane mod 8 reads columns c0 + 8 j; row slot wave * 8 + lane / 8 walks
+      // the local positions i.
+      const int dsplit = p.dsplit;
+      const int d_tile = w / dsplit, d_sub = w - d_tile * dsplit;
+      const int d_tiles = p.dtiles;
+      const int c0 = d_tile * 64;
+      const int d_j = lane & 7;
+      const int d_rr = wave * 8 + (lane >> 3);
+      const int d_rs = kWork * 8;
       const int d_col = c0 + d_j * 8;
-      const bool d_ok = wave < kWork && d_col < d;
+      const bool d_ok = wave < kWork && d_tile < d_tiles && d_col < d;
+      const int kl = k > d_sub ? (k - d_sub + dsplit - 1) / dsplit : 0;   // local positions
       const uint8_t* Wd = (const uint8_t*)Ld->Wd;
       Raw<16> wdv[kRD];
       int nid[kRD];
-      auto load_wd = [&](int qb) {                 // kRD positions at a time, qb < k
-        // positions past k are clamped to k - 1 (loaded, never used), so the loads
-        // are issued back to back without branches
+      auto load_wd = [&](int qb) {                 // kRD local positions at a time, qb < kl
+        // positions past kl are clamped to kl - 1 (loaded, never used), so the
+        // loads are issued back to back without branches
 #pragma unroll
-        for (int u = 0; u < kRD; ++u) nid[u] = pos_to_neuron(min(qb + u * d_rs, k - 1));
+        for (int u = 0; u < kRD; ++u) nid[u] = pos_to_neuron(d_sub + dsplit * min(qb + u * d_rs, kl - 1));
 #pragma unroll
         for (int u = 0; u < kRD; ++u) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
       };
       // the workers' first batch goes out before anything else is waited for; the
       // outputs in the standard layout are built while it is in flight
-      if (d_ok && d_rr < k) load_wd(d_rr);
+      if (d_ok && d_rr < kl) load_wd(d_rr);
 
       // Union words in the standard layout (bit b of word g = neuron 32 g + b).
       // With P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and
@@ -877,7 +936,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, kWave);
         const int q0 = min(dsum, nov), q1 = min(dsum + max(fair - (int)s_own[w], 0), nov);
-        for (int r = q0 + wave; r < q1; r += kWork) {
+        auto ov_entry = [&](int r) {               // neuron of overflow rank r
           int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]
           while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -887,18 +946,19 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           uint32_t um = s_raw[lo * nwm];
           while (rem >= __popc(um)) { rem -= __popc(um); um = s_raw[lo * nwm + (++m)]; }
           for (int i = 0; i < rem; ++i) um &= um - 1;
-          up_row(lo + P * (32 * m + __builtin_ctz(um)));
-        }
+          return lo + P * (32 * m + __builtin_ctz(um));
+        };
+        for (int r = q0 + wave; r < q1; r += kWork) up_row(ov_entry(r));
       }
 
       float yacc[NB * 8];
 #pragma unroll
       for (int i = 0; i < NB * 8; ++i) yacc[i] = 0.f;
       if (d_ok) {
-        for (int qb = d_rr; qb < k; qb += d_rs * kRD) {
+        for (int qb = d_rr; qb < kl; qb += d_rs * kRD) {
           if (qb != d_rr) load_wd(qb);
           unsigned long long hv[kRD * NB];
-          const int nrow = min(kRD, (k - qb + d_rs - 1) / d_rs);
+          const int nrow = min(kRD, (kl - qb + d_rs - 1) / d_rs);
           // entry u NB + b: activation of position qb + u d_rs, token b
           auto valid = [&](int i) { return i / NB < nrow && i % NB < B; };
           auto addr = [&](int i) { return p.hact + (size_t)nid[i / NB] * B + min(i % NB, B - 1); };
@@ -936,23 +996,34 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           }
         }
       }
-      // sum over the lanes of each lane group, then over the worker waves (lane
-      // groups 0 and 1 are the same columns when nct = 1), in a fixed order
-      constexpr int V = NB * 8;
-      const float v = wave_reduce_multi_groups<V, 2>(yacc);
-      lds_barrier();                                     // s_red was read in phase B
-      if ((lane & (kWave / V - 1)) < 2) s_red[wave * 64 + (lane >> (6 - ilog2c(V))) * 2 + (lane & 1)] = v;
+      // Sum over the 8 row slots of each wave (lane L ends with column
+      // 8 (L mod 8) + L / 8 of the tile, per token), then over the worker waves in a
+      // fixed order: this workgroup's share of the tile, handed over tagged.  The
+      // tile's first workgroup adds the dsplit shares (tile_y_sum) one layer later,
+      // during the grid barrier, or at the end of the launch.
+      float vb[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float t8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t8[e] = yacc[b * 8 + e];
+        vb[b] = wave_reduce_multi_groups<8, 8>(t8);
+      }
+      lds_barrier();                                     // every wave is past its rows: s_x is free
+      float* s_part = reinterpret_cast<float*>(s_x);     // [kNW][NB][64]
+      {
+        const int colL = 8 * (lane & 7) + (lane >> 3);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s_part[(wave * NB + b) * 64 + colL] = vb[b];
+      }
       lds_barrier();
-      for (int i = tid; i < nct * B * 8; i += kNT) {
-        const int j = i / (B * 8);
-        const int be = i - j * B * 8;                    // b * 8 + e
-        const int col = c0 + j * 8 + (be & 7);
-        if (col < d) {
-          float s = 0.f;
-          for (int wv2 = 0; wv2 < kWork; ++wv2)
-            for (int jj = j; jj < 2; jj += nct) s += s_red[wv2 * 64 + be * 2 + jj];
-          Ld->y[(size_t)(be >> 3) * d + col] = s;
-        }
+      // written by waves kAW + b (their next full memory wait is in the scores
+      // phase; wave 0's comes as soon as the next layer's inputs are requested)
+      if (d_tile < d_tiles && wave >= kAW && wave - kAW < B) {
+        const int col = lane, b = wave - kAW;
+        float sum = 0.f;
+        for (int wv2 = 0; wv2 < kWork; ++wv2) sum += s_part[(wv2 * NB + b) * 64 + col];
+        st_tagged(p.ypart + ((size_t)(l & 1) * P + w) * (64 * NB) + b * 64 + col, tag, __float_as_uint(sum));
       }
     }
     }                                          // phases C and D
@@ -984,6 +1055,12 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
       lds_barrier();
     }
+  }
+  // y of the last layer (the earlier layers' were summed in the next layer)
+  {
+    unsigned long long yv[8];
+    tile_y_issue<NB>(p, p.L - 1, yv);
+    tile_y_sum<NB>(p, p.L - 1, e0 + (uint32_t)p.L, yv);
   }
   // Every workgroup ends with all its flags at e0 + L, so all flags agree at the next call.
   if (threadIdx.x == 0) store_through(p.fbar + (size_t)blockIdx.x * kFS, e0 + (uint32_t)p.L);

@@ -55,6 +55,9 @@ StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P) {
   while (n < nct) n <<= 1;
   if (n > 2) return g;                       // down: at most 2 lane groups of 8 columns
   g.cw = 8 * n;
+  // fused step's down phase: 64-column tiles, each split over dsplit workgroups
+  g.dtiles = (d + 63) / 64;
+  g.dsplit = P / g.dtiles < 8 ? P / g.dtiles : 8;
   g.ok = true;
   (void)kNT;
   return g;
@@ -91,12 +94,12 @@ int step_union_block(int f, int P, int B) {
 }
 
 // control line | barrier flags [P][kFlagStride] | hidden [P][16] | union [P][us] |
-// hact [f][B]  (tagged words: 8 bytes)
+// hact [f][B] | tile shares of y [2][P][64 NB]  (tagged words: 8 bytes)
 size_t step_ws_bytes(int B, int h, int f, int P) {
   (void)h;
   const size_t fl = up256((size_t)P * kFlagStride * 4);
   return 256 + fl + up256((size_t)P * 16 * 8) + up256((size_t)P * step_union_block(f, P, B) * 8) +
-         up256((size_t)f * B * 8);
+         up256((size_t)f * B * 8) + up256((size_t)2 * P * 64 * nb_class(B) * 8);
 }
 
 StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layers, void* ws, const StepGeom& g) {
@@ -122,6 +125,10 @@ StepParams step_params(int B, int d, int h, int f, int L, const LayerDesc* layer
   p.uni = (unsigned long long*)(base + off);
   off += up256((size_t)g.P * p.us * 8);
   p.hact = (unsigned long long*)(base + off);
+  off += up256((size_t)f * B * 8);
+  p.ypart = (unsigned long long*)(base + off);
+  p.dsplit = g.dsplit;
+  p.dtiles = g.dtiles;
   return p;
 }
 

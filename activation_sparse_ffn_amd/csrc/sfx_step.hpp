@@ -17,16 +17,19 @@ struct StepParams {
   int w2_lds;     // 1: the workgroup's W2 rows are staged in LDS
   int cw;         // columns of y per workgroup in the down phase (8, 16, 32 or 64)
   int us;         // tagged union words per workgroup block (multiple of 8)
+  int dsplit;     // fused step, down phase: workgroups per 64-column tile (<= 8)
+  int dtiles;     // fused step, down phase: 64-column tiles, ceil(d / 64)
   uint32_t* err;               // nonzero after a wait timed out
   uint32_t* fbar;              // [P] x kFlagStride: layer done (grid barrier); holds layer tags
   unsigned long long* hid;     // [P][16]  {tag, hidden}: rows w + P s, s < nr1, all tokens
   unsigned long long* uni;     // [P][us]  {tag, union word}: words w + P m
   unsigned long long* hact;    // [f][B]   {tag, activation} by active rank
+  unsigned long long* ypart;   // [2][P][64 NB] {tag, share of y}: fused step's tile shares
 };
 
 struct StepGeom {
   bool ok;
-  int P, nr1, w2_lds, cw, dl;
+  int P, nr1, w2_lds, cw, dl, dsplit, dtiles;
 };
 
 StepGeom step_geometry(int wdt, int act, int B, int d, int h, int f, int P);
