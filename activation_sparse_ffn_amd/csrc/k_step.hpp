@@ -336,6 +336,19 @@ __device__ __forceinline__ int w2_split(int f, int P) {
   return nr2 - (nr2 * SFX_W2_LATE + 7) / 8;
 }
 
+// A layer's input rows [B][d] into s_x by waves 0..kAW-1, 16 bytes per lane
+// (B d 2 <= kXBytes).
+__device__ __forceinline__ void load_x_lds(const StepParams& p, CLayer* Ld, uint8_t* s_x) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const uint8_t* x = (const uint8_t*)Ld->x;
+  const int items = p.B * (p.d / 8);
+#pragma unroll 1
+  for (int i0 = wave * kWave; i0 < items; i0 += kAW * kWave)
+    if (i0 + lane < items)
+      __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)(i0 + lane) * 16),
+                                       (__attribute__((address_space(3))) void*)(s_x + (size_t)i0 * 16), 16, 0, 0);
+}
+
 // One stage of a 32 x 32 bit-matrix transpose held one row per lane (each half
 // wave its own matrix): rows L and L ^ s swap the s x s blocks off the diagonal of
 // their 2s x 2s block; `hi` marks the columns t with t & s set.
@@ -455,24 +468,17 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const int a_row = w + P * wave;
       const bool a_active = wave < p.nr1 && a_row < h;
       const uint8_t* x = (const uint8_t*)Ld->x;
-      // The input rows go to LDS first (waves 0..3, 16 bytes per lane) and only
-      // then does this layer's W2 stream start, so they are not
-      // queued behind it.  Inputs larger than the staging area are read directly.
-      // Waves 0..3 synchronise among themselves (group_sync) so the streaming
-      // waves, blocked while their loads issue, hold nobody up.
+      // The input rows go to LDS first (waves 0..3, 16 bytes per lane; for layers
+      // after the first they were requested during the grid barrier) and only
+      // then does this layer's W2 stream start, so they are not queued behind
+      // it.  Inputs larger than the staging area are read directly.  Waves 0..3
+      // synchronise among themselves (group_sync) so the streaming waves,
+      // blocked while their loads issue, hold nobody up.
       const bool x_lds = (size_t)B * rb1 <= (size_t)kXBytes;
       uint8_t* s_xin = s_x;
       const uint32_t g0 = 3u * kAW * (uint32_t)l;      // s_grp arrivals before this layer
       if (wave < kAW) {
-        if (x_lds) {
-          const int items = B * nch1;
-#pragma unroll 1
-          for (int i0 = wave * kWave; i0 < items; i0 += kAW * kWave)
-            if (i0 + lane < items)
-              __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)(i0 + lane) * 16),
-                                               (__attribute__((address_space(3))) void*)(s_xin + (size_t)i0 * 16),
-                                               16, 0, 0);
-        }
+        if (x_lds && l == 0) load_x_lds(p, Ld, s_x);
         group_sync(&s_grp, g0 + kAW, p.err);                  // inputs requested
         if (x_lds) wait_memory();
         group_sync(&s_grp, g0 + 2 * kAW, p.err);              // inputs landed
@@ -1034,6 +1040,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       lds_barrier();
       if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
       prefetch_w1<kU>(p, (CLayer*)p.layers + l + 1, w1r);
+      // the next layer's input (in place since the launch) goes to LDS now: s_x is
+      // free once every wave has passed the barrier above
+      if (wave < kAW && (size_t)B * rb1 <= (size_t)kXBytes) load_x_lds(p, (CLayer*)p.layers + l + 1, s_x);
       if (kTlbWarm && wave == kCW - 1 && lane == 0) {
         // one load per 2 MiB page of the next layer's weights, spread over the
         // workgroups, so their address translations are warm when the layer starts
