@@ -445,12 +445,16 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
   __shared__ uint32_t s_words[64];
   __shared__ uint32_t s_wt[kNW];
+  __shared__ uint32_t s_nosplit;             // = layer tag: a hidden value is outside the fp16 range
   uint32_t* s_pref = reinterpret_cast<uint32_t*>(s_x);
   uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
 
   __shared__ uint32_t s_grp;                 // group_sync arrivals of waves 0..3
-  if (threadIdx.x == 0) s_grp = 0u;
+  if (threadIdx.x == 0) {
+    s_grp = 0u;
+    s_nosplit = 0u;                          // layer tags start at 1
+  }
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
   int k_prev = -1;                           // active neurons of the previous layer
@@ -550,23 +554,50 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
       if (l > 0) tile_y_sum<NB>(p, l - 1, tag - 1u, yv);
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
-      // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row]
+      // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row].  With
+      // fp16 W2 rows staged in LDS the hidden goes in as two fp16 pieces instead,
+      // hi = fp16(h) and lo = fp16((h - hi) 2^11) (h to about 2^-22 relative, the
+      // scaled lo clear of the subnormals), so the scores run on the fp16
+      // dot-product instruction with fp32 sums; a hidden value outside the fp16
+      // range sends the layer to the fp32 spread and sums instead.
       constexpr int kPT = kAW * kWave;
-      if (wave < kAW) {
+      constexpr bool kSplitH = std::is_same<T, TF16>::value;
+      uint16_t* s_hh = reinterpret_cast<uint16_t*>(s_hid);     // [TB][h] hi
+      uint16_t* s_hl = s_hh + (size_t)TB * h;                   // [TB][h] lo * 2^11
+      auto spread = [&](bool split_in) {
+        if (wave < kAW) {
 #pragma unroll 1
-        for (int o = tid; o < P; o += kPT) {
-          const int ns = o < h ? (h - o + P - 1) / P : 0;
-          // block entry s NB + b holds row o + P s, token b
-          unsigned long long hw[4 * NB];
-          auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
-          auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
-          poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kStepPS>(hw, valid, addr, tag, p.err);
+          for (int o = tid; o < P; o += kPT) {
+            const int ns = o < h ? (h - o + P - 1) / P : 0;
+            // block entry s NB + b holds row o + P s, token b
+            unsigned long long hw[4 * NB];
+            auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
+            auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
+            poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kStepPS>(hw, valid, addr, tag, p.err);
 #pragma unroll
-          for (int i = 0; i < 4 * NB; ++i)
-            if (valid(i)) s_hid[(i % NB) * h + o + P * (i / NB)] = __uint_as_float((uint32_t)hw[i]);
+            for (int i = 0; i < 4 * NB; ++i) {
+              if (valid(i)) {
+                const float v = __uint_as_float((uint32_t)hw[i]);
+                const int at = (i % NB) * h + o + P * (i / NB);
+                if (split_in) {
+                  if (!(fabsf(v) < 65504.f)) s_nosplit = tag;
+                  const _Float16 hi = (_Float16)v;
+                  const _Float16 lo = (_Float16)((v - (float)hi) * 2048.f);
+                  s_hh[at] = __builtin_bit_cast(uint16_t, hi);
+                  s_hl[at] = __builtin_bit_cast(uint16_t, lo);
+                } else {
+                  s_hid[at] = v;
+                }
+              }
+            }
+          }
         }
-      }
-      __syncthreads();
+        __syncthreads();
+      };
+      const bool split_try = kSplitH && w2_lds;
+      spread(split_try);
+      const bool split = split_try && s_nosplit != tag;
+      if (split_try && !split) spread(false);   // the words are still in place: no wait
       // The W2 source is chosen once, outside the loop: with the choice inside it,
       // every row read became its own branch with a full memory wait, one LDS
       // round trip per row.
@@ -619,7 +650,56 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           }
         }
       };
-      if (w2_lds) scores_pass(std::true_type{});
+      // the split hidden against the fp16 rows in LDS: two dot-product sums per
+      // row, hi and lo (scaled back by 2^-11 at the end)
+      auto scores_pass_split = [&]() {
+        const int tb = B;
+        for (int q0 = wave; q0 < rows2; q0 += kNW * kRB) {
+          float a2[kRB * TB], a3[kRB * TB];
+#pragma unroll
+          for (int i = 0; i < kRB * TB; ++i) { a2[i] = 0.f; a3[i] = 0.f; }
+          for (int c = lane; c < nch2; c += kWave) {
+            half2_t hh[TB][4], hl[TB][4];
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+              const uint4 u = *reinterpret_cast<const uint4*>(s_hh + (size_t)(b < tb ? b : 0) * h + c * 8);
+              const uint4 v = *reinterpret_cast<const uint4*>(s_hl + (size_t)(b < tb ? b : 0) * h + c * 8);
+              hh[b][0] = __builtin_bit_cast(half2_t, u.x); hh[b][1] = __builtin_bit_cast(half2_t, u.y);
+              hh[b][2] = __builtin_bit_cast(half2_t, u.z); hh[b][3] = __builtin_bit_cast(half2_t, u.w);
+              hl[b][0] = __builtin_bit_cast(half2_t, v.x); hl[b][1] = __builtin_bit_cast(half2_t, v.y);
+              hl[b][2] = __builtin_bit_cast(half2_t, v.z); hl[b][3] = __builtin_bit_cast(half2_t, v.w);
+            }
+            Raw<16> wv[kRB];
+#pragma unroll
+            for (int r = 0; r < kRB; ++r) {
+              const int q = min(q0 + r * kNW, rows2 - 1);
+              wv[r] = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < kRB; ++r) {
+                const half2_t wj = __builtin_bit_cast(half2_t, wv[r].w[j]);
+#pragma unroll
+                for (int b = 0; b < TB; ++b) {
+                  a2[r * TB + b] = __builtin_amdgcn_fdot2(wj, hh[b][j], a2[r * TB + b], false);
+                  a3[r * TB + b] = __builtin_amdgcn_fdot2(wj, hl[b][j], a3[r * TB + b], false);
+                }
+              }
+          }
+#pragma unroll
+          for (int i = 0; i < kRB * TB; ++i) a2[i] = fmaf(a3[i], 1.f / 2048.f, a2[i]);
+          const float v = wave_reduce_multi<kRB * TB>(a2);
+          if (reduce_owner<kRB * TB>(lane)) {
+            const int idx = reduce_index<kRB * TB>(lane);
+            const int r = idx / TB, b = idx - r * TB;
+            const int q = q0 + r * kNW;
+            if (q < rows2 && b < tb) s_sc[q * NB + b] = v;
+          }
+        }
+      };
+      if (split) scores_pass_split();
+      else if (w2_lds) scores_pass(std::true_type{});
       else scores_pass(std::false_type{});
       __syncthreads();
       // own mask words by wave ballots (lane = own row j of a 64-row pair of

@@ -68,26 +68,72 @@ __device__ __forceinline__ int opaque_lane() {
   return t & (kWave - 1);
 }
 
+// Value of lane L ^ O (O = 8, 4, 2, 1) by DPP within rows of 16 lanes: VALU
+// operations, no LDS crossbar round trip.  Xor 4 takes row_shr:4 on lanes with bit
+// 2 set and row_shl:4 on the others.
+template <int O>
+__device__ __forceinline__ float lane_xor_dpp(float x, int lane) {
+  const int xi = __float_as_int(x);
+  if constexpr (O == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xf, 0xf, false));   // row_ror:8
+  } else if constexpr (O == 4) {
+    const int from_below = __builtin_amdgcn_update_dpp(0, xi, 0x114, 0xf, 0xf, false);  // row_shr:4
+    const int from_above = __builtin_amdgcn_update_dpp(0, xi, 0x104, 0xf, 0xf, false);  // row_shl:4
+    return __int_as_float((lane & 4) ? from_below : from_above);
+  } else if constexpr (O == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4e, 0xf, 0xf, false));    // quad_perm 2,3,0,1
+  } else {
+    static_assert(O == 1, "lane_xor_dpp: O in 1, 2, 4, 8");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xb1, 0xf, 0xf, false));    // quad_perm 1,0,3,2
+  }
+}
+// a (lanes kept by the lower half of each 2 O block) + b (kept by the upper
+// half) exchanged across lane bit O = 32 or 16 with the gfx950 lane-swap
+// instructions: returns, in lane L, the sum of L's and (L ^ O)'s values of the
+// element L keeps (a below, b above).
+template <int O>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                         : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Halving reduction: at lane bit O the lanes with the bit clear keep the first
+// half of the values, the others the second half, each adding its partner's.
+// The pairing (L with L ^ O) and the order of every addition are those of a
+// plain exchange by lane xor.
 template <int V, int O, int M = 1>
 struct WaveReduceStep {
   __device__ __forceinline__ static void run(float* v, int lane) {
     constexpr int half = V / 2;
-    const bool up = (lane & O) != 0;
+    if constexpr (O >= 16) {
 #pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = up ? v[i] : v[i + half];
-      const float keep = up ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, O, kWave);
+      for (int i = 0; i < half; ++i) v[i] = swap_add<O>(v[i], v[i + half]);
+    } else {
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = up ? v[i] : v[i + half];
+        const float keep = up ? v[i + half] : v[i];
+        v[i] = keep + lane_xor_dpp<O>(send, lane);
+      }
     }
     WaveReduceStep<half, O / 2, M>::run(v, lane);
   }
 };
 template <int O, int M>
 struct WaveReduceStep<1, O, M> {
-  __device__ __forceinline__ static void run(float* v, int) {
-#pragma unroll
-    for (int o = O; o >= M; o >>= 1) v[0] += __shfl_xor(v[0], o, kWave);
+  __device__ __forceinline__ static void run(float* v, int lane) {
+    if constexpr (O >= M) {
+      if constexpr (O >= 16) v[0] = swap_add<O>(v[0], v[0]);
+      else v[0] += lane_xor_dpp<O>(v[0], lane);
+      WaveReduceStep<1, O / 2, M>::run(v, lane);
+    }
   }
+};
+template <int M>
+struct WaveReduceStep<1, 0, M> {
+  __device__ __forceinline__ static void run(float*, int) {}
 };
 template <int V>
 __device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {

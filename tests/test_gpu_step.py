@@ -195,3 +195,41 @@ def test_fused_benchmark_launch():
         say(f"   layer {l}", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in r.items()})
     del layers, st
     torch.cuda.empty_cache()
+
+
+def test_fused_hidden_outside_fp16_range():
+    """fp16 predictor rows: the fused step splits the hidden into two fp16 pieces
+    for its scores; a hidden value past 65504 sends that layer to fp32 sums.  Layer
+    0 gets one hidden row of about 8e5 (W1 row 5 = 1000 sign(x)), layer 1 is
+    normal: scores within 1e-5 of fp64 relative to max(1, |s|), the gate bit-exact
+    on the GPU's scores, activations and y against the oracle on the GPU's list."""
+    from oracle import sfx_oracle as O
+    from gpu_helpers import Y_RTOL, rel_err
+    cfg = SMALL["C2s"]
+    layers = [S.make_layer(cfg, l, device=DEV) for l in range(2)]
+    x = [S.make_tokens(cfg, l, 1, 1, device=DEV)[0].clone() for l in range(2)]
+    layers[0].W1[5] = (1000.0 * torch.sign(x[0][0].float())).to(layers[0].W1.dtype)
+    st = StackStep(layers, cfg.d, cfg.f, cfg.h, 1, cfg.wdtype, cfg.act)
+    say("fused step, hidden past the fp16 range in layer 0")
+    st.run(st.descriptors(x))
+    torch.cuda.synchronize()
+    assert st.error_word() == 0
+    for l in range(2):
+        out = _outputs(st, l)
+        lnp = layer_np(layers[l])
+        x64 = O.decode(S.storage_numpy(x[l]), cfg.pdtype)
+        s64 = O.predict(x64, *O.predictor_weights(lnp, cfg.pdtype))
+        if l == 0:
+            assert np.max(x64 @ O.decode(lnp["W1"], cfg.pdtype).T) > 65504.0
+        err = np.max(np.abs(out["scores"].astype(np.float64) - s64) / np.maximum(1.0, np.abs(s64)))
+        say(f"   layer {l}: score rel err {err:.2e}, count {out['count']}")
+        assert err <= 1e-5, err
+        _, uni, idx, cnt = O.gate(out["scores"].astype(np.float64), layers[l].threshold)
+        assert np.array_equal(O.pack_bits(uni), out["union_bits"]) and cnt == out["count"]
+        assert np.array_equal(idx, out["idx"])
+        gidx = out["idx"]
+        hact_ref = O.sparse_up(x64, O.rows(lnp["Wa"], cfg.wdtype, gidx), np.asarray(lnp["ba"], np.float64)[gidx],
+                               cfg.act)
+        y_ref = O.sparse_down(O.rows(lnp["Wd"], cfg.wdtype, gidx), hact_ref)
+        assert rel_err(out["hact"], hact_ref) <= Y_RTOL[cfg.wdtype]
+        assert rel_err(out["y"], y_ref) <= Y_RTOL[cfg.wdtype]
