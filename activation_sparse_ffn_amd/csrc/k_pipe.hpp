@@ -243,12 +243,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     const int g0 = wpt * gt;
     uint32_t cnt = 0;
     for (int g = g0; g < min(W, g0 + wpt); ++g) cnt += __popc(s_uw[g]);
-    uint32_t inc = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t n = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += n;
-    }
+    const uint32_t inc = wave_inclusive_scan_u32(cnt);
     if (lane == kWave - 1) s_wt[gs] = inc;
     gather_sync();
     uint32_t before = 0, total = 0;

@@ -352,9 +352,10 @@ __device__ __forceinline__ void load_x_lds(const StepParams& p, CLayer* Ld, uint
 // One stage of a 32 x 32 bit-matrix transpose held one row per lane (each half
 // wave its own matrix): rows L and L ^ s swap the s x s blocks off the diagonal of
 // their 2s x 2s block; `hi` marks the columns t with t & s set.
-__device__ __forceinline__ uint32_t transpose_step(uint32_t x, int lane, int s, uint32_t hi) {
-  const uint32_t y = __shfl_xor(x, s, kWave);
-  return (lane & s) ? ((x & hi) | ((y & hi) >> s)) : ((x & ~hi) | ((y & ~hi) << s));
+template <int S>
+__device__ __forceinline__ uint32_t transpose_step(uint32_t x, int lane, uint32_t hi) {
+  const uint32_t y = lane_xor_u32<S>(x, lane);
+  return (lane & S) ? ((x & hi) | ((y & hi) >> S)) : ((x & ~hi) | ((y & ~hi) << S));
 }
 
 // Own mask words per workgroup (at most) when workgroup w owns rows w + P j.
@@ -852,12 +853,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         s_own[tid] = c - ovc;
       }
       const uint32_t pk = c | (ovc << 16);
-      uint32_t inc = pk;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t n = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += n;
-      }
+      const uint32_t inc = wave_inclusive_scan_u32(pk);
       if (lane == kWave - 1) s_wt[wave] = inc;
       lds_barrier();
       uint32_t before_pk = 0, total_pk = 0;
@@ -953,11 +949,11 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         for (int it = wv; it < nq * nwm; it += kNW) {
           const int q = it % nq, c = it / nq;
           uint32_t x = s_raw[(64 * q + lane) * nwm + c];
-          x = transpose_step(x, lane, 16, 0xFFFF0000u);
-          x = transpose_step(x, lane, 8, 0xFF00FF00u);
-          x = transpose_step(x, lane, 4, 0xF0F0F0F0u);
-          x = transpose_step(x, lane, 2, 0xCCCCCCCCu);
-          x = transpose_step(x, lane, 1, 0xAAAAAAAAu);
+          x = transpose_step<16>(x, lane, 0xFFFF0000u);
+          x = transpose_step<8>(x, lane, 0xFF00FF00u);
+          x = transpose_step<4>(x, lane, 0xF0F0F0F0u);
+          x = transpose_step<2>(x, lane, 0xCCCCCCCCu);
+          x = transpose_step<1>(x, lane, 0xAAAAAAAAu);
           const int j = 32 * c + (lane & 31);
           const int g = j * (P >> 5) + 2 * q + (lane >> 5);
           if (j < nr2m && g < W) s_uw[g] = x;
@@ -990,12 +986,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const int g0 = wpt * tid;
         const uint32_t cnt0 = g0 < W ? __popc(s_uw[g0]) : 0u;
         const uint32_t cnt = cnt0 + (wpt == 2 && g0 + 1 < W ? __popc(s_uw[g0 + 1]) : 0u);
-        uint32_t inc = cnt;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t n = __shfl_up(inc, o, kWave);
-          if (lane >= o) inc += n;
-        }
+        const uint32_t inc = wave_inclusive_scan_u32(cnt);
         if (lane == kWave - 1) s_wt[wave] = inc;
         lds_barrier();
         uint32_t before = 0;
@@ -1019,8 +1010,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const int fair = (k + P - 1) / P;          // T
         int dsum = 0;
         for (int o = lane; o < w; o += kWave) dsum += max(fair - (int)s_own[o], 0);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, kWave);
+        dsum = wave_sum_i32(dsum, lane);
         const int q0 = min(dsum, nov), q1 = min(dsum + max(fair - (int)s_own[w], 0), nov);
         auto ov_entry = [&](int r) {               // neuron of overflow rank r
           int lo = 0, hi = P;                      // s_ovp[lo] <= r < s_ovp[hi]

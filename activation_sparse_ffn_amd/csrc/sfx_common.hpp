@@ -48,13 +48,6 @@ struct alignas(N) Raw { uint32_t w[N / 4]; };
 template <int N>
 __device__ __forceinline__ Raw<N> load_raw(const void* p) { return *reinterpret_cast<const Raw<N>*>(p); }
 
-// Butterfly sum over the 64 lanes of a wave; every lane gets the total.  The
-// order of additions is fixed, so the result is reproducible.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 
 // Sum each of V values (V a power of two, V <= 64) over the 64 lanes of a wave,
 // halving the values held per lane at every exchange (about V + 6 shuffles instead
@@ -87,6 +80,57 @@ __device__ __forceinline__ float lane_xor_dpp(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xb1, 0xf, 0xf, false));    // quad_perm 1,0,3,2
   }
 }
+// 32-bit value of lane L ^ O, any O in 32, 16, 8, 4, 2, 1 (lane swaps for 32 and
+// 16, DPP below): VALU operations only.
+template <int O>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x, int lane) {
+  if constexpr (O == 32 || O == 16) {
+    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & O) ? r[0] : r[1];
+  } else {
+    return __float_as_uint(lane_xor_dpp<O>(__uint_as_float(x), lane));
+  }
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within rows of 16,
+// then lane 15 added to rows 1 and 3 and lane 31 to rows 2 and 3 (DPP row
+// broadcasts).
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return (uint32_t)v;
+}
+// Butterfly sum over the 64 lanes of a wave (lane L with L ^ 32, then 16, ..., 1);
+// every lane gets the total.  The order of additions is fixed, so the result is
+// reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+  int lane = threadIdx.x;
+  asm volatile("" : "+v"(lane));
+  lane &= kWave - 1;
+  v += __uint_as_float(lane_xor_u32<32>(__float_as_uint(v), lane));
+  v += __uint_as_float(lane_xor_u32<16>(__float_as_uint(v), lane));
+  v += __uint_as_float(lane_xor_u32<8>(__float_as_uint(v), lane));
+  v += __uint_as_float(lane_xor_u32<4>(__float_as_uint(v), lane));
+  v += __uint_as_float(lane_xor_u32<2>(__float_as_uint(v), lane));
+  v += __uint_as_float(lane_xor_u32<1>(__float_as_uint(v), lane));
+  return v;
+}
+// Sum over the 64 lanes, every lane ends with it.
+__device__ __forceinline__ int wave_sum_i32(int v, int lane) {
+  v += (int)lane_xor_u32<32>((uint32_t)v, lane);
+  v += (int)lane_xor_u32<16>((uint32_t)v, lane);
+  v += (int)lane_xor_u32<8>((uint32_t)v, lane);
+  v += (int)lane_xor_u32<4>((uint32_t)v, lane);
+  v += (int)lane_xor_u32<2>((uint32_t)v, lane);
+  v += (int)lane_xor_u32<1>((uint32_t)v, lane);
+  return v;
+}
+
 // a (lanes kept by the lower half of each 2 O block) + b (kept by the upper
 // half) exchanged across lane bit O = 32 or 16 with the gfx950 lane-swap
 // instructions: returns, in lane L, the sum of L's and (L ^ O)'s values of the
