@@ -89,8 +89,7 @@ __global__ __launch_bounds__(kT) void k_compact(const float* __restrict__ scores
     }
     if (mine && c != 0u) part += c - 1u;
   }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+  part = (uint32_t)wave_sum_i32((int)part, lane);
   if (lane == 0) s_red[wave] = part;
   __syncthreads();
   uint32_t prefix = 0;

@@ -309,8 +309,12 @@ __global__ __launch_bounds__(kBlock) void k_down_cols(const uint8_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = acc[b][e];
-#pragma unroll
-      for (int o = kLPR; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+      if constexpr (kLPR <= 1) v += __uint_as_float(lane_xor_u32<1>(__float_as_uint(v), lane));
+      if constexpr (kLPR <= 2) v += __uint_as_float(lane_xor_u32<2>(__float_as_uint(v), lane));
+      if constexpr (kLPR <= 4) v += __uint_as_float(lane_xor_u32<4>(__float_as_uint(v), lane));
+      if constexpr (kLPR <= 8) v += __uint_as_float(lane_xor_u32<8>(__float_as_uint(v), lane));
+      v += __uint_as_float(lane_xor_u32<16>(__float_as_uint(v), lane));
+      v += __uint_as_float(lane_xor_u32<32>(__float_as_uint(v), lane));
       acc[b][e] = v;
     }
   if (lane < kLPR) {
