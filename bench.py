@@ -48,8 +48,8 @@ def parse():
     p.add_argument("--tam-eps", type=float, default=0.01)
     p.add_argument("--separate", action="store_true", help="time the five separate calls per layer")
     p.add_argument("--fused", action="store_true",
-                   help="time sfx_ffn_step where it supports the shape, also from 3 tokens on (by default the "
-                        "separate calls are timed there: on the matrix cores they measured faster)")
+                   help="time sfx_ffn_step where it supports the shape (the default already does; kept for "
+                        "scripts that name the path)")
     p.add_argument("--pipeline", action="store_true",
                    help="time the Live Pipeline step (sfx_ffn_pipeline) as the headline: each layer's predictor "
                         "scores the previous layer's input (layer 0: the previous token's), inputs of adjacent "
@@ -684,9 +684,10 @@ def main():
                 print("bench.py: the Live Pipeline kernel does not take this shape", file=sys.stderr)
                 sys.exit(2)
             return "pipeline"
-        # the fused step where it is the faster path (1-2 tokens); from 3 tokens on the
-        # separate calls run on the matrix cores and measured faster (--fused forces it)
-        fused = (not args.separate) and (args.fused or B <= 2) and not cfg.pred_q4 and \
+        # the fused step wherever it takes the shape (up to 4 tokens): measured faster
+        # than the separate calls at 1-4 tokens on both 7B shapes (at 3 tokens 44.3
+        # against 52.8 us per layer-step, OPT-6.7B); --separate forces the calls
+        fused = (not args.separate) and not cfg.pred_q4 and \
             StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
         return "fused" if fused else "separate"
 

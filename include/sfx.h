@@ -416,10 +416,10 @@ int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const 
  *   ws       >= sfx_ffn_step_ws(wdt, act, B, d, h, f) bytes, zero-filled before
  *            its first use, used on one device only.
  * Returns SFX_E_UNSUPPORTED for shapes the fused kernel is not built for; the
- * separate calls cover those.  From 3 tokens on, the separate calls (which then
- * run on the matrix cores) measured faster than this kernel on MI355X (LLaMA2-7B
- * shape at 4 tokens: 58.4 against 70.5 us per layer-step); at 1 and 2 tokens this
- * kernel is the faster path.
+ * separate calls cover those.  Measured on MI355X against the separate calls (which
+ * run on the matrix cores from 3 tokens): faster at 1 to 4 tokens on the OPT-6.7B and
+ * LLaMA2-7B shapes (3 tokens, OPT-6.7B: 44.3 against 52.8 us per layer-step; 4
+ * tokens, LLaMA2-7B: 55.3 against 56.1).
  * ------------------------------------------------------------------------------- */
 typedef struct sfx_layer {
   const void* x;            /* [B][d] */
