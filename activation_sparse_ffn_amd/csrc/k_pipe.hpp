@@ -37,6 +37,10 @@ namespace step {
 constexpr int kNG = kAW + 1;             // gather waves: 0..kAW-1 and kCW
 constexpr int kNS = kCW - kAW;           // stream waves: kAW..kCW-1
 constexpr int kSpRed = kRedFloats / 2;   // s_red: [0, kSpRed) scores of own rows, then the down sums
+#ifndef SFX_PIPE_PRED_PRIO
+#define SFX_PIPE_PRED_PRIO 3
+#endif
+constexpr int kPredPrio = SFX_PIPE_PRED_PRIO;   // wave issue priority (s_setprio) of the predictor work
 
 // gather slot of a wave: kCW -> 0 (free at the start of a layer), waves 0..kAW-1 -> 1..kAW
 __device__ __forceinline__ int gather_slot(int wave) { return wave == kCW ? 0 : wave + 1; }
@@ -53,7 +57,8 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   constexpr int kRD = NB == 1 ? 12 : NB == 2 ? 6 : 3;   // down rows per lane loaded together
   // poll back-off (x 64 clocks): re-polls of uncached words compete with the weight
   // streams; measured on the OPT-6.7B shape, 2 -> 30 took the layer period from
-  // 28.1 to 25.6 us (8: 27.0, 100: 27.3)
+  // 28.1 to 25.6 us (8: 27.0, 100: 27.3); for the hidden poll alone 2 and 8 were
+  // also slower (24.7, 24.2 against 23.7 us)
   constexpr int kPS = 30;
   constexpr int kRB = TB <= 2 ? 8 : 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
@@ -62,13 +67,14 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   __shared__ uint32_t s_words[64];
   __shared__ uint32_t s_wt[kNW];
   __shared__ uint32_t s_gsync, s_ssync;      // arrivals of the gather / stream waves
+  __shared__ uint32_t s_nosplit;             // = layer tag: a hidden value is outside the fp16 range
   uint32_t* s_pref = reinterpret_cast<uint32_t*>(s_x);
   uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
   float* s_hid = reinterpret_cast<float*>(s_x + kXBytes - pipe_hid_bytes(TB, p.h));
   const int nid_cap = (kXBytes - kPrefBytes - kUwBytes - pipe_hid_bytes(TB, p.h)) / 4;
 
-  if (threadIdx.x == 0) { s_gsync = 0u; s_ssync = 0u; }
+  if (threadIdx.x == 0) { s_gsync = 0u; s_ssync = 0u; s_nosplit = 0u; }
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
   uint32_t gsn = 0, ssn = 0;                 // group-sync arrivals so far (wave-uniform)
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   // Hidden rows w + P s (waves 0..kAW-1, W1 row in registers) from the predictor
   // input, tagged out.
   Raw<16> w1r[kU];
-  auto hidden = [&](CLayer* Lj, uint32_t tg) {
+  auto hidden = [&](CLayer* Lj, uint32_t tg) __attribute__((always_inline)) {
     SFX_PHASE_IDS;
     const int a_row = w + P * wave;
     if (!(wave < kAW && wave < p.nr1 && a_row < h)) return;
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   // Scores of the owned rows (stream waves): wait for this wave's W2 rows, read the
   // hidden of every workgroup, score from LDS (or memory), ballots, union words
   // tagged out, outputs.
-  auto scores = [&](CLayer* Lj, uint32_t tg) {
+  auto scores = [&](CLayer* Lj, uint32_t tg) __attribute__((always_inline)) {
     SFX_PHASE_IDS;
     const int st = tid - kAW * kWave;        // 0 .. kNS*64-1
     constexpr int kST = kNS * kWave;
@@ -124,18 +130,67 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     const uint8_t* W2 = (const uint8_t*)Lj->W2;
     float* s_sc = s_red;                     // [rows2][NB]
     if (w2_lds) wait_memory();               // this wave's LDS rows have landed
+    // At one token thread st polls the blocks of workgroups st and st + kST (P <=
+    // 2 kST) in one round.  With fp16 W2 rows in LDS the hidden goes in as two fp16 pieces, hi =
+    // fp16(h) and lo = fp16((h - hi) 2^11), for the dot-product scores; a value
+    // outside the fp16 range sends the layer to the fp32 spread and sums.
+    constexpr bool kSplitH = std::is_same<T, TF16>::value;
+    uint16_t* s_hh = reinterpret_cast<uint16_t*>(s_hid);   // [TB][h] hi
+    uint16_t* s_hl = s_hh + (size_t)TB * h;                 // [TB][h] lo * 2^11
+    auto put = [&](bool split_in, int at, float v) {
+      if (split_in) {
+        if (!(fabsf(v) < 65504.f)) s_nosplit = tg;
+        const _Float16 hi = (_Float16)v;
+        const _Float16 lo = (_Float16)((v - (float)hi) * 2048.f);
+        s_hh[at] = __builtin_bit_cast(uint16_t, hi);
+        s_hl[at] = __builtin_bit_cast(uint16_t, lo);
+      } else {
+        s_hid[at] = v;
+      }
+    };
+    auto spread = [&](bool split_in) {
+      if constexpr (NB > 1) {                // one block per poll round (register budget)
 #pragma unroll 1
-    for (int o = st; o < P; o += kST) {
-      const int ns = o < h ? (h - o + P - 1) / P : 0;
-      unsigned long long hw[4 * NB];
-      auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
-      auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
-      poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kPS>(hw, valid, addr, tg, p.err);
+        for (int o = st; o < P; o += kST) {
+          const int ns = o < h ? (h - o + P - 1) / P : 0;
+          unsigned long long hw[4 * NB];
+          auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
+          auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
+          poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kPS>(hw, valid, addr, tg, p.err);
 #pragma unroll
-      for (int i = 0; i < 4 * NB; ++i)
-        if (valid(i)) s_hid[(i % NB) * h + o + P * (i / NB)] = __uint_as_float((uint32_t)hw[i]);
-    }
-    stream_sync();
+          for (int i = 0; i < 4 * NB; ++i)
+            if (valid(i)) put(split_in, (i % NB) * h + o + P * (i / NB), __uint_as_float((uint32_t)hw[i]));
+        }
+      } else if (st < P) {
+        const int o1 = st, o2 = st + kST;
+        const int ns1 = o1 < h ? (h - o1 + P - 1) / P : 0;
+        const int ns2 = o2 < P && o2 < h ? (h - o2 + P - 1) / P : 0;
+        unsigned long long hw[8 * NB];
+        // entries [0, 4 NB): block o1, [4 NB, 8 NB): block o2; entry s NB + b = row o + P s, token b
+        auto valid = [&](int i) {
+          const int e = i % (4 * NB);
+          return e / NB < (i < 4 * NB ? ns1 : ns2) && e % NB < B;
+        };
+        auto addr = [&](int i) {
+          const int o = i < 4 * NB ? o1 : min(o2, P - 1);
+          return p.hid + (size_t)o * kHidBlock + i % (4 * NB);
+        };
+        poll_tagged_if<8 * NB, decltype(valid), decltype(addr), kPS>(hw, valid, addr, tg, p.err);
+#pragma unroll
+        for (int i = 0; i < 8 * NB; ++i) {
+          if (valid(i)) {
+            const int e = i % (4 * NB);
+            const int o = i < 4 * NB ? o1 : o2;
+            put(split_in, (e % NB) * h + o + P * (e / NB), __uint_as_float((uint32_t)hw[i]));
+          }
+        }
+      }
+      stream_sync();
+    };
+    const bool split_try = kSplitH && w2_lds;
+    spread(split_try);
+    const bool split = split_try && s_nosplit != tg;
+    if (split_try && !split) spread(false);   // the words are still in place: no wait
     auto pass = [&](auto from_lds) {
       constexpr bool kLds = decltype(from_lds)::value;
       for (int q0 = wave - kAW; q0 < rows2; q0 += kNS * kRB) {
@@ -181,7 +236,55 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
         }
       }
     };
-    if (w2_lds) pass(std::true_type{});
+    // the split hidden against the fp16 rows in LDS: hi and lo dot-product sums per
+    // row (lo scaled back by 2^-11 at the end)
+    auto pass_split = [&]() {
+      for (int q0 = wave - kAW; q0 < rows2; q0 += kNS * kRB) {
+        float a2[kRB * TB], a3[kRB * TB];
+#pragma unroll
+        for (int i = 0; i < kRB * TB; ++i) { a2[i] = 0.f; a3[i] = 0.f; }
+        for (int c = lane; c < nch2; c += kWave) {
+          half2_t hh[TB][4], hl[TB][4];
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            const uint4 u = *reinterpret_cast<const uint4*>(s_hh + (size_t)(b < B ? b : 0) * h + c * 8);
+            const uint4 v = *reinterpret_cast<const uint4*>(s_hl + (size_t)(b < B ? b : 0) * h + c * 8);
+            hh[b][0] = __builtin_bit_cast(half2_t, u.x); hh[b][1] = __builtin_bit_cast(half2_t, u.y);
+            hh[b][2] = __builtin_bit_cast(half2_t, u.z); hh[b][3] = __builtin_bit_cast(half2_t, u.w);
+            hl[b][0] = __builtin_bit_cast(half2_t, v.x); hl[b][1] = __builtin_bit_cast(half2_t, v.y);
+            hl[b][2] = __builtin_bit_cast(half2_t, v.z); hl[b][3] = __builtin_bit_cast(half2_t, v.w);
+          }
+          Raw<16> wv[kRB];
+#pragma unroll
+          for (int r = 0; r < kRB; ++r) {
+            const int q = min(q0 + r * kNS, rows2 - 1);
+            wv[r] = *reinterpret_cast<const Raw<16>*>(s_w2 + ((size_t)q * nch2 + c) * 16);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < kRB; ++r) {
+              const half2_t wj = __builtin_bit_cast(half2_t, wv[r].w[j]);
+#pragma unroll
+              for (int b = 0; b < TB; ++b) {
+                a2[r * TB + b] = __builtin_amdgcn_fdot2(wj, hh[b][j], a2[r * TB + b], false);
+                a3[r * TB + b] = __builtin_amdgcn_fdot2(wj, hl[b][j], a3[r * TB + b], false);
+              }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRB * TB; ++i) a2[i] = fmaf(a3[i], 1.f / 2048.f, a2[i]);
+        const float v = wave_reduce_multi<kRB * TB>(a2);
+        if (reduce_owner<kRB * TB>(lane)) {
+          const int ix = reduce_index<kRB * TB>(lane);
+          const int r = ix / TB, b = ix - r * TB;
+          const int q = q0 + r * kNS;
+          if (q < rows2 && b < B) s_sc[q * NB + b] = v;
+        }
+      }
+    };
+    if (split) pass_split();
+    else if (w2_lds) pass(std::true_type{});
     else pass(std::false_type{});
     stream_sync();
     const float thr = Lj->threshold;
@@ -217,7 +320,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
 
   // Union exchange and scan (gather waves): the ascending list of layer j lands in
   // LDS (s_nid when it fits, else found from s_pref / s_uw); returns its length.
-  auto union_scan = [&](CLayer* Lj, uint32_t tg) -> int {
+  auto union_scan = [&](CLayer* Lj, uint32_t tg) __attribute__((always_inline)) -> int {
     SFX_PHASE_IDS;
     const int gs = gather_slot(wave);
     const int gt = gs * kWave + lane;        // 0 .. kNG*64-1
@@ -281,7 +384,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   // ------------------------------------------------ FFN of layer l (gather waves)
   // One up row: Wa (and Wl) row of neuron nid against x, bias, activation; out
   // tagged by neuron for the down phase, and at rank r in the outputs.
-  auto up_row = [&](CLayer* Ld, int nid, int r, uint32_t tg) {
+  auto up_row = [&](CLayer* Ld, int nid, int r, uint32_t tg) __attribute__((always_inline)) {
     SFX_PHASE_IDS;
     const uint8_t* x = (const uint8_t*)Ld->x;
     const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
@@ -354,7 +457,11 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     if (wave >= kAW && wave < kCW) {
       // ---------------------------------------------------- stream waves
       if (has_next) {
+        // the next layer's predictor is the critical path: its waves take issue
+        // priority over the gathers on the shared SIMDs while they score
+        __builtin_amdgcn_s_setprio(kPredPrio);
         scores(Ld + 1, tag + 1u);
+        __builtin_amdgcn_s_setprio(0);
         if (l + 2 < p.L) prefetch_w2(p, Ld + 2, s_w2);
       }
     } else {
@@ -364,7 +471,11 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       const int gs = gather_slot(wave);
       // hidden of the next layer first (its W1 row is in registers; the input is
       // in memory since the layer started)
-      if (has_next && wave < kAW) hidden(Ld + 1, tag + 1u);
+      if (has_next && wave < kAW) {
+        __builtin_amdgcn_s_setprio(kPredPrio);
+        hidden(Ld + 1, tag + 1u);
+        __builtin_amdgcn_s_setprio(0);
+      }
       // down geometry: lane group j = lane mod nct reads columns c0 + 8 j; slot
       // gs * 64/nct + lane / nct walks the list
       const int nct = p.cw / 8;

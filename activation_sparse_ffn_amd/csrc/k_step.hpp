@@ -116,6 +116,13 @@ __device__ __forceinline__ void lds_wait_at_least(const uint32_t* ctr, uint32_t 
     __builtin_amdgcn_s_sleep(1);
   }
 }
+// Arrival on an LDS counter once this wave's LDS accesses are done (no wait).
+__device__ __forceinline__ void group_arrive(uint32_t* ctr) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0)
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(ctr, 1u);
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t target, uint32_t* err) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS accesses are done
