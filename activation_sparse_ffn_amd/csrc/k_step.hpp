@@ -39,6 +39,8 @@ constexpr int kNT = 512;                 // threads per workgroup
 constexpr int kNW = kNT / kWave;         // 8 waves
 constexpr int kLds = 163840;             // gfx950 LDS per compute unit
 constexpr int kW2Bytes = 131072;         // LDS region for the W2 rows
+constexpr int kUpSlot0 = 16384;          // up rows' LDS slots in s_w2 (past the union words)
+constexpr int kUpSlot = 8192;            // one slot per wave: a row of d <= 4096 at 2 bytes
 constexpr int kRedFloats = 1024;         // reduction scratch
 constexpr int kXBytes = kLds - kW2Bytes - kRedFloats * 4 - 768;
 constexpr int kMaxWords = 1024;          // f <= 32768
@@ -447,7 +449,10 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   constexpr int kRB = TB <= 2 ? 8 : 4;    // score rows per lane per pass
   // own up rows a workgroup takes before the union exchange: two rounds of the
   // waves when a row is one load batch, one round otherwise
-  constexpr int kOwnCap = (kUP == kU ? 2 : 1) * kWork;
+  // ReGLU at one token: the Wl row goes through an LDS slot, so a row pair is one
+  // load batch as well
+  constexpr bool kGluSlot = REGLU && NB == 1;
+  constexpr int kOwnCap = (kUP == kU || kGluSlot ? 2 : 1) * kWork;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
   __shared__ __attribute__((aligned(16))) float s_red[kRedFloats];
@@ -751,6 +756,42 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
     // out tagged and indexed by neuron.
     const uint8_t* x = (const uint8_t*)Ld->x;
     auto up_row = [&](int nid) {
+      if constexpr (kGluSlot) {
+        // one load batch: the Wl row into this wave's 8 KB slot of s_w2 (free from
+        // the end of the scores to the next layer's W2 rows, past the union words
+        // s_raw), the Wa row and the input into registers
+        const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
+        const uint8_t* rl = (const uint8_t*)Ld->Wl + (size_t)nid * rb1;
+        uint8_t* slot = s_w2 + kUpSlot0 + wave * kUpSlot;
+        const float bias = Ld->ba != nullptr ? Ld->ba[nid] : 0.f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = min(lane + u * kWave, nch1 - 1);
+          __builtin_amdgcn_global_load_lds((const void*)(rl + (size_t)c * 16),
+                                           (__attribute__((address_space(3))) void*)(slot + u * kWave * 16), 16, 0, 0);
+        }
+        Raw<16> wa[kU], xq[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = min(lane + u * kWave, nch1 - 1);
+          wa[u] = load_raw<16>(ra + (size_t)c * 16);
+          xq[u] = load_raw<16>(x + (size_t)c * 16);
+        }
+        wait_memory();                           // registers and the slot
+        float za[1] = {0.f}, zl[1] = {0.f};
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (lane + u * kWave < nch1) {
+            dot_chunk<T>(wa[u].w, xq[u].w, za[0]);
+            const Raw<16> wl = *reinterpret_cast<const Raw<16>*>(slot + (u * kWave + lane) * 16);
+            dot_chunk<T>(wl.w, xq[u].w, zl[0]);
+          }
+        }
+        const float ta = wave_reduce_multi<1>(za);
+        const float v = fmaxf(ta + bias, 0.f) * wave_reduce_multi<1>(zl);
+        if (lane == 0) st_tagged(p.hact + (size_t)nid, tag, __float_as_uint(v));
+        return;
+      }
       const uint8_t* ra = (const uint8_t*)Ld->Wa + (size_t)nid * rb1;
       const uint8_t* rl = REGLU ? (const uint8_t*)Ld->Wl + (size_t)nid * rb1 : nullptr;
       // the bias goes out ahead of the row (loaded after the dot products it
