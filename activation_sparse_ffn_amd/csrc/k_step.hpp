@@ -389,10 +389,10 @@ __device__ __forceinline__ int own_words_max(int f, int P) { return (((f + P - 1
   (void)nch1; (void)nch2; (void)rb1; (void)rb2
 
 // Tile shares of the down phase: layer l's share of workgroup w (tile w / dsplit,
-// 64 columns x NB tokens) sits in buffer l mod 2; a workgroup can only be one
-// layer ahead of another, so layer l + 2 cannot overwrite it before the share is
-// summed in layer l + 1.  The tile's first workgroup adds its dsplit shares in
-// share order: wave kAW + b takes token b, lane = column, entry s of yv = share s.
+// 64 columns x NB tokens) sits in buffer l mod 2 (summed before the grid barrier of
+// layer l, so the next layer's shares never meet unsummed ones).  The tile's first
+// workgroup adds its dsplit shares in share order: wave kAW + b takes token b,
+// lane = column, entry s of yv = share s.
 __device__ __forceinline__ bool tile_y_mine(const StepParams& p) {
   const int b = (int)(threadIdx.x >> 6) - kAW;
   return b >= 0 && b < p.B && blockIdx.x % p.dsplit == 0 && (int)blockIdx.x / p.dsplit < p.dtiles;
@@ -559,13 +559,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
-      // the previous layer's tile shares (long written) land while the W2 rows do
-      unsigned long long yv[8];
-      if (l > 0) tile_y_issue<NB>(p, l - 1, yv);
       if (w2_lds && wave >= kAW) {
         wait_memory();                         // this wave's LDS rows have landed
       }
-      if (l > 0) tile_y_sum<NB>(p, l - 1, tag - 1u, yv);
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
       // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row].  With
       // fp16 W2 rows staged in LDS the hidden goes in as two fp16 pieces instead,
@@ -1122,9 +1118,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       }
       // Sum over the 8 row slots of each wave (lane L ends with column
       // 8 (L mod 8) + L / 8 of the tile, per token), then over the worker waves in a
-      // fixed order: this workgroup's share of the tile, handed over tagged.  The
-      // tile's first workgroup adds the dsplit shares (tile_y_sum) one layer later,
-      // during the grid barrier, or at the end of the launch.
+      // fixed order: this workgroup's share of the tile, handed over tagged; the
+      // tile's first workgroup adds the dsplit shares (tile_y_sum) before the grid
+      // barrier.
       float vb[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -1148,6 +1144,15 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         float sum = 0.f;
         for (int wv2 = 0; wv2 < kWork; ++wv2) sum += s_part[(wv2 * NB + b) * 64 + col];
         st_tagged(p.ypart + ((size_t)(l & 1) * P + w) * (64 * NB) + b * 64 + col, tag, __float_as_uint(sum));
+      }
+      // The tile's first workgroup adds the dsplit shares and writes y before it
+      // raises its flag, so y of this layer is complete when the grid barrier
+      // passes (the order a real model imposes: the next layer's input follows
+      // from y).
+      {
+        unsigned long long yv[8];
+        tile_y_issue<NB>(p, l, yv);
+        tile_y_sum<NB>(p, l, tag, yv);
       }
     }
     }                                          // phases C and D
@@ -1182,12 +1187,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       if (wave == kCW) wait_flags(p.fbar, P, tag, p.err, 1u);
       lds_barrier();
     }
-  }
-  // y of the last layer (the earlier layers' were summed in the next layer)
-  {
-    unsigned long long yv[8];
-    tile_y_issue<NB>(p, p.L - 1, yv);
-    tile_y_sum<NB>(p, p.L - 1, e0 + (uint32_t)p.L, yv);
   }
   // Every workgroup ends with all its flags at e0 + L, so all flags agree at the next call.
   if (threadIdx.x == 0) store_through(p.fbar + (size_t)blockIdx.x * kFS, e0 + (uint32_t)p.L);
