@@ -979,34 +979,71 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       // outputs in the standard layout are built while it is in flight
       if (d_ok && d_rr < kl) load_wd(d_rr);
 
+      // The outputs in the standard layout (union words and the list with its
+      // activations in rank order) are for the caller only: when this workgroup's
+      // positions fit the save area (s_w2 past the raw mask words and the up-row
+      // slots, which other waves may still fill with overflow rows while this wave
+      // saves; the area is free until the next layer's W2 rows), the down loop keeps
+      // (neuron, activation) of every position in LDS and the outputs are built after
+      // the grid-barrier flag, while the other workgroups finish; otherwise before
+      // the down loop, as the list is read.
+      constexpr int kSave0 = kUpSlot0 + (kGluSlot ? kWork * kUpSlot : 0);
+      const int save_cap = (kW2Bytes - kSave0) / (4 + 4 * NB);
+      const bool late_out = kl <= save_cap;
+      int32_t* s_snid = reinterpret_cast<int32_t*>(s_w2 + kSave0);          // [save_cap]
+      float* s_shv = reinterpret_cast<float*>(s_w2 + kSave0) + save_cap;    // [save_cap][NB]
+      auto std_outputs = [&]() {
       // Union words in the standard layout (bit b of word g = neuron 32 g + b).
-      // With P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and
-      // belong to owners 32 (g mod P/32) + b.  Lane L holds the mask word c of owner
-      // 64 q + L (bits j = 32 c + t); a 32 x 32 bit transpose within each half wave
-      // (five exchange stages) leaves in lane t the bits j = 32 c + t of owners
-      // 64 q .. + 31 (lanes 0..31) or 64 q + 32 .. + 63 (lanes 32..63): words
-      // j P/32 + 2q (+1).
-      {
-        const int wv = __builtin_amdgcn_readfirstlane(wave);
-        const int nq = P >> 6;
-        const int nr2m = (f + P - 1) / P;
-        for (int it = wv; it < nq * nwm; it += kNW) {
-          const int q = it % nq, c = it / nq;
-          uint32_t x = s_raw[(64 * q + lane) * nwm + c];
-          x = transpose_step<16>(x, lane, 0xFFFF0000u);
-          x = transpose_step<8>(x, lane, 0xFF00FF00u);
-          x = transpose_step<4>(x, lane, 0xF0F0F0F0u);
-          x = transpose_step<2>(x, lane, 0xCCCCCCCCu);
-          x = transpose_step<1>(x, lane, 0xAAAAAAAAu);
-          const int j = 32 * c + (lane & 31);
-          const int g = j * (P >> 5) + 2 * q + (lane >> 5);
-          if (j < nr2m && g < W) s_uw[g] = x;
+        // With P = 64, 128 or 256, the neurons of word g share j = g / (P/32) and
+        // belong to owners 32 (g mod P/32) + b.  Lane L holds the mask word c of owner
+        // 64 q + L (bits j = 32 c + t); a 32 x 32 bit transpose within each half wave
+        // (five exchange stages) leaves in lane t the bits j = 32 c + t of owners
+        // 64 q .. + 31 (lanes 0..31) or 64 q + 32 .. + 63 (lanes 32..63): words
+        // j P/32 + 2q (+1).
+        {
+          const int wv = __builtin_amdgcn_readfirstlane(wave);
+          const int nq = P >> 6;
+          const int nr2m = (f + P - 1) / P;
+          for (int it = wv; it < nq * nwm; it += kNW) {
+            const int q = it % nq, c = it / nq;
+            uint32_t x = s_raw[(64 * q + lane) * nwm + c];
+            x = transpose_step<16>(x, lane, 0xFFFF0000u);
+            x = transpose_step<8>(x, lane, 0xFF00FF00u);
+            x = transpose_step<4>(x, lane, 0xF0F0F0F0u);
+            x = transpose_step<2>(x, lane, 0xCCCCCCCCu);
+            x = transpose_step<1>(x, lane, 0xAAAAAAAAu);
+            const int j = 32 * c + (lane & 31);
+            const int g = j * (P >> 5) + 2 * q + (lane >> 5);
+            if (j < nr2m && g < W) s_uw[g] = x;
+          }
         }
-      }
-      lds_barrier();
-      // outputs of this workgroup: union words g = w + P m and, when asked for, the
-      // per-token words (bit b from owner 32 (g mod P/32) + b, one tagged word per lane)
-      for (int g = w + P * tid; g < W; g += P * kNT) Ld->union_bits[g] = s_uw[g];
+        lds_barrier();
+        // outputs of this workgroup: union words g = w + P m and, when asked for, the
+        // per-token words (bit b from owner 32 (g mod P/32) + b, one tagged word per lane)
+        for (int g = w + P * tid; g < W; g += P * kNT) Ld->union_bits[g] = s_uw[g];
+        // prefix of the standard words (the rank of a neuron in the ascending list =
+        // s_pref[g] + its set bits below it in word g); thread t owns words [wpt t, +wpt)
+        {
+          const int wpt = W <= kNT ? 1 : 2;
+          const int g0 = wpt * tid;
+          const uint32_t cnt0 = g0 < W ? __popc(s_uw[g0]) : 0u;
+          const uint32_t cnt = cnt0 + (wpt == 2 && g0 + 1 < W ? __popc(s_uw[g0 + 1]) : 0u);
+          const uint32_t inc = wave_inclusive_scan_u32(cnt);
+          if (lane == kWave - 1) s_wt[wave] = inc;
+          lds_barrier();
+          uint32_t before = 0;
+#pragma unroll
+          for (int v = 0; v < kNW; ++v)
+            if (v < wave) before += s_wt[v];
+          const uint32_t base = before + inc - cnt;
+          if (g0 < W) s_pref[g0] = base;
+          if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
+          if (tid == 0) s_pref[W] = (uint32_t)k;
+          lds_barrier();
+        }
+      };
+      if (!late_out) std_outputs();
+      // per-token words (read from the owners' tagged words: before the flag)
       if (Ld->tok_bits != nullptr && wave == 0) {
         for (int g = w; g < W; g += P) {
           const int j = g / (P >> 5), c = g - j * (P >> 5);
@@ -1022,26 +1059,6 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             if (lane == 0) Ld->tok_bits[(size_t)b * W + g] = (uint32_t)bal;
           }
         }
-      }
-      // prefix of the standard words (the rank of a neuron in the ascending list =
-      // s_pref[g] + its set bits below it in word g); thread t owns words [wpt t, +wpt)
-      {
-        const int wpt = W <= kNT ? 1 : 2;
-        const int g0 = wpt * tid;
-        const uint32_t cnt0 = g0 < W ? __popc(s_uw[g0]) : 0u;
-        const uint32_t cnt = cnt0 + (wpt == 2 && g0 + 1 < W ? __popc(s_uw[g0 + 1]) : 0u);
-        const uint32_t inc = wave_inclusive_scan_u32(cnt);
-        if (lane == kWave - 1) s_wt[wave] = inc;
-        lds_barrier();
-        uint32_t before = 0;
-#pragma unroll
-        for (int v = 0; v < kNW; ++v)
-          if (v < wave) before += s_wt[v];
-        const uint32_t base = before + inc - cnt;
-        if (g0 < W) s_pref[g0] = base;
-        if (wpt == 2 && g0 + 1 < W) s_pref[g0 + 1] = base + cnt0;
-        if (tid == 0) s_pref[W] = (uint32_t)k;
-        lds_barrier();
       }
       // Own entries past `cap` of every workgroup (owner o: the set bits of its own
       // mask words in order, from entry cap on), ranked by owner through the prefix
@@ -1089,13 +1106,21 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
 #pragma unroll
             for (int u = 0; u < kRD; ++u) {
               if (u < nrow) {
-                const int n = nid[u], g = n >> 5;
-                const int r = (int)s_pref[g] + __popc(s_uw[g] & ((1u << (n & 31)) - 1u));
-                if (r % d_tiles == d_tile) {
-                  Ld->idx[r] = n;
+                const int n = nid[u];
+                if (late_out) {
+                  const int i = qb + u * d_rs;
+                  s_snid[i] = n;
 #pragma unroll
-                  for (int b = 0; b < NB; ++b)
-                    if (b < B) Ld->hact[(size_t)r * B + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+                  for (int b = 0; b < NB; ++b) s_shv[i * NB + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+                } else {
+                  const int g = n >> 5;
+                  const int r = (int)s_pref[g] + __popc(s_uw[g] & ((1u << (n & 31)) - 1u));
+                  if (r % d_tiles == d_tile) {
+                    Ld->idx[r] = n;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                      if (b < B) Ld->hact[(size_t)r * B + b] = __uint_as_float((uint32_t)hv[u * NB + b]);
+                  }
                 }
               }
             }
@@ -1154,17 +1179,33 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         tile_y_issue<NB>(p, l, yv);
         tile_y_sum<NB>(p, l, tag, yv);
       }
+      // Grid barrier, first half: the flag goes up once every wave is done with the
+      // layer's exchanges (and y of this workgroup's tile is written).
+      lds_barrier();
+      if (l + 1 < p.L && tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
+      if (late_out) {
+        std_outputs();
+        if (d_tile < d_tiles) {
+          for (int i = tid; i < kl; i += kNT) {
+            const int n = s_snid[i], g = n >> 5;
+            const int r = (int)s_pref[g] + __popc(s_uw[g] & ((1u << (n & 31)) - 1u));
+            if (r % d_tiles == d_tile) {
+              Ld->idx[r] = n;
+              for (int b = 0; b < B; ++b) Ld->hact[(size_t)r * B + b] = s_shv[i * NB + b];
+            }
+          }
+        }
+        lds_barrier();                           // s_x is the next layer's input area
+      }
     }
     }                                          // phases C and D
     if (l + 1 < p.L) {
-      // grid barrier: every workgroup raises its flag once its layer is done and
-      // waits for all flags
+      // grid barrier, second half: every workgroup has raised its flag (end of
+      // phase D) and waits for all flags
       SFX_PHASE_IDS;
-      lds_barrier();
-      if (tid == 0) store_through(p.fbar + (size_t)w * kFS, tag);
       prefetch_w1<kU>(p, (CLayer*)p.layers + l + 1, w1r);
       // the next layer's input (in place since the launch) goes to LDS now: s_x is
-      // free once every wave has passed the barrier above
+      // free once every wave has passed the last LDS barrier of phase D
       if (wave < kAW && (size_t)B * rb1 <= (size_t)kXBytes) load_x_lds(p, (CLayer*)p.layers + l + 1, s_x);
       if (kTlbWarm && wave == kCW - 1 && lane == 0) {
         // one load per 2 MiB page of the next layer's weights, spread over the

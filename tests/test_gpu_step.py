@@ -147,6 +147,15 @@ def test_fused_long_list_w2_from_memory(B):
     torch.cuda.empty_cache()
 
 
+def test_fused_outputs_inside_down_loop():
+    """Every neuron active at 4 tokens with f = 32768: 8192 list positions per
+    workgroup, more than the LDS area that keeps (neuron, activation) pairs for
+    outputs written after the grid-barrier flag (5734 pairs at 4 tokens), so the
+    rank-order list and activations are written from the down loop itself."""
+    _run_and_check(WIDE, 2, 4, 1, threshold=float("-inf"), min_k=NID_CAP)
+    torch.cuda.empty_cache()
+
+
 def test_fused_long_list_w2_in_lds():
     """OPT-6.7B shape (W2 rows in LDS) with every neuron active: 16384 > 4920."""
     cfg = S.CONFIGS["C2"]
