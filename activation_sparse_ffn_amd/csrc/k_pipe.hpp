@@ -60,6 +60,17 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   // 28.1 to 25.6 us (8: 27.0, 100: 27.3); for the hidden poll alone 2 and 8 were
   // also slower (24.7, 24.2 against 23.7 us)
   constexpr int kPS = 30;
+  // The hidden exchange: each workgroup's tagged hidden words packed at 4 NB words
+  // (32 bytes at one token), so a round of polls over all workgroups touches a
+  // quarter of the cache lines it did at 16 words.  The stream waves start polling
+  // only once this workgroup's own hidden rows are out, plus a pause of kHidPause x
+  // 64 clocks (the others land over about a microsecond after it): polls issued
+  // before the hidden exists only added traffic.  Measured (one token, us per
+  // layer-step, OPT-6.7B / LLaMA2-7B shapes): polling from the stream waves' start
+  // 23.8 / 28.4; after the own hidden 21.3 / 25.9, with the pause 21.5 / 24.8;
+  // packed words, after the own hidden 20.8 / 25.0, with the pause 20.9 / 24.4.
+  constexpr int kHS = 4 * NB;
+  constexpr int kHidPause = 40;
   constexpr int kRB = TB <= 2 ? 8 : 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
@@ -67,6 +78,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   __shared__ uint32_t s_words[64];
   __shared__ uint32_t s_wt[kNW];
   __shared__ uint32_t s_gsync, s_ssync;      // arrivals of the gather / stream waves
+  __shared__ uint32_t s_hdone;               // waves 0..kAW-1 done with a round of hidden rows
   __shared__ uint32_t s_nosplit;             // = layer tag: a hidden value is outside the fp16 range
   uint32_t* s_pref = reinterpret_cast<uint32_t*>(s_x);
   uint32_t* s_uw = reinterpret_cast<uint32_t*>(s_x + kPrefBytes);
@@ -74,7 +86,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   float* s_hid = reinterpret_cast<float*>(s_x + kXBytes - pipe_hid_bytes(TB, p.h));
   const int nid_cap = (kXBytes - kPrefBytes - kUwBytes - pipe_hid_bytes(TB, p.h)) / 4;
 
-  if (threadIdx.x == 0) { s_gsync = 0u; s_ssync = 0u; s_nosplit = 0u; }
+  if (threadIdx.x == 0) { s_gsync = 0u; s_ssync = 0u; s_nosplit = 0u; s_hdone = 0u; }
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
   uint32_t gsn = 0, ssn = 0;                 // group-sync arrivals so far (wave-uniform)
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     const float v = wave_reduce_multi<NB>(acc);
     const int b = reduce_index<NB>(lane);
     if (reduce_owner<NB>(lane) && b < B)
-      st_tagged(p.hid + (size_t)w * kHidBlock + wave * NB + b, tg, __float_as_uint(fmaxf(v, 0.f)));
+      st_tagged(p.hid + (size_t)w * kHS + wave * NB + b, tg, __float_as_uint(fmaxf(v, 0.f)));
   };
 
   // Scores of the owned rows (stream waves): wait for this wave's W2 rows, read the
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
           const int ns = o < h ? (h - o + P - 1) / P : 0;
           unsigned long long hw[4 * NB];
           auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
-          auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
+          auto addr = [&](int i) { return p.hid + (size_t)o * kHS + i; };
           poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kPS>(hw, valid, addr, tg, p.err);
 #pragma unroll
           for (int i = 0; i < 4 * NB; ++i)
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
         };
         auto addr = [&](int i) {
           const int o = i < 4 * NB ? o1 : min(o2, P - 1);
-          return p.hid + (size_t)o * kHidBlock + i % (4 * NB);
+          return p.hid + (size_t)o * kHS + i % (4 * NB);
         };
         poll_tagged_if<8 * NB, decltype(valid), decltype(addr), kPS>(hw, valid, addr, tg, p.err);
 #pragma unroll
@@ -188,6 +200,9 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       stream_sync();
     };
     const bool split_try = kSplitH && w2_lds;
+    // round tg - e0 of the hidden rows: this workgroup's are out, the others' follow
+    lds_wait_at_least(&s_hdone, kAW * (tg - e0), p.err);
+    __builtin_amdgcn_s_sleep(kHidPause);
     spread(split_try);
     const bool split = split_try && s_nosplit != tg;
     if (split_try && !split) spread(false);   // the words are still in place: no wait
@@ -438,7 +453,10 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
     int wave = threadIdx.x >> 6;
     asm volatile("" : "+v"(wave));
     const uint32_t tg0 = e0 + 1u;
-    if (wave < kAW) hidden(L0, tg0);
+    if (wave < kAW) {
+      hidden(L0, tg0);
+      group_arrive(&s_hdone);
+    }
     if (wave >= kAW && wave < kCW) {
       scores(L0, tg0);
       if (p.L > 1) prefetch_w2(p, L0 + 1, s_w2);
@@ -474,6 +492,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       if (has_next && wave < kAW) {
         __builtin_amdgcn_s_setprio(kPredPrio);
         hidden(Ld + 1, tag + 1u);
+        group_arrive(&s_hdone);
         __builtin_amdgcn_s_setprio(0);
       }
       // down geometry: lane group j = lane mod nct reads columns c0 + 8 j; slot
