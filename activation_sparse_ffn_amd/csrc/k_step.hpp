@@ -156,7 +156,6 @@ constexpr bool kTlbWarm = SFX_TLB_WARM != 0;
 // Flags sit kFS words apart: flags sharing a cache line with many writers become
 // visible to other compute units much later.
 constexpr int kFS = kFlagStride;
-constexpr int kHidBlock = 16;            // tagged hidden words per workgroup: [nr1 <= 4][NB <= 4]
 
 // Layer descriptors are read-only for the whole launch: read them through the
 // constant address space so they come in on scalar loads.
@@ -452,6 +451,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   // ReGLU at one token: the Wl row goes through an LDS slot, so a row pair is one
   // load batch as well
   constexpr bool kGluSlot = REGLU && NB == 1;
+  constexpr int kHS = 4 * NB;             // tagged hidden words per workgroup, packed
   constexpr int kOwnCap = (kUP == kU || kGluSlot ? 2 : 1) * kWork;
   __shared__ __attribute__((aligned(16))) uint8_t s_w2[kW2Bytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kXBytes];
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         const float v = wave_reduce_multi<NB>(acc);
         const int b = reduce_index<NB>(lane);
         if (reduce_owner<NB>(lane) && b < B)
-          st_tagged(p.hid + (size_t)w * kHidBlock + wave * NB + b, tag, __float_as_uint(fmaxf(v, 0.f)));
+          st_tagged(p.hid + (size_t)w * kHS + wave * NB + b, tag, __float_as_uint(fmaxf(v, 0.f)));
       }
       if (wave < kAW) group_sync(&s_grp, g0 + 3 * kAW, p.err);  // inputs read: s_x is reused in phase B
       // the rest of this layer's W2 rows (their waits fall in the scores phase,
@@ -559,9 +559,13 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
       float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
-      if (w2_lds && wave >= kAW) {
-        wait_memory();                         // this wave's LDS rows have landed
-      }
+      // Every wave first waits for its own W2 rows (waves 0..3 for their late share,
+      // issued last), so the hidden is polled once the rows have landed, when the
+      // other workgroups' hidden words are long out.  Polled from the end of phase A
+      // instead, its rounds of loads slowed the W2 stream (one token: 22.9 -> 22.6 us
+      // per layer-step at the OPT-6.7B shape, 23.9 -> 23.4 at LLaMA2-7B, with the
+      // hidden words packed at 4 NB per workgroup).
+      if (w2_lds) wait_memory();
       // waves 0..3 read the hidden: thread o polls the block of workgroup o (rows
       // o + P s, s < nr1, all tokens) and spreads it into s_hid[b][row].  With
       // fp16 W2 rows staged in LDS the hidden goes in as two fp16 pieces instead,
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
             // block entry s NB + b holds row o + P s, token b
             unsigned long long hw[4 * NB];
             auto valid = [&](int i) { return i / NB < ns && i % NB < B; };
-            auto addr = [&](int i) { return p.hid + (size_t)o * kHidBlock + i; };
+            auto addr = [&](int i) { return p.hid + (size_t)o * kHS + i; };
             poll_tagged_if<4 * NB, decltype(valid), decltype(addr), kStepPS>(hw, valid, addr, tag, p.err);
 #pragma unroll
             for (int i = 0; i < 4 * NB; ++i) {
