@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
   lds_barrier();
   const uint32_t e0 = ld_agent(p.fbar + (size_t)blockIdx.x * kFS);
   int k_prev = -1;                           // active neurons of the previous layer
+  bool x_from_lds = false;                   // up rows read the input from s_x
   Raw<16> w1r[kU];
   prefetch_w1<kU>(p, (CLayer*)p.layers, w1r);
   prefetch_w2_rows(p, (CLayer*)p.layers, s_w2, kAW, kNW, 0, 1 << 30);
@@ -557,7 +558,14 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       const int rows2 = nr2;
       const bool w2_lds = p.w2_lds != 0;
       const uint8_t* W2 = (const uint8_t*)Ld->W2;
-      float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x) : reinterpret_cast<float*>(s_w2);
+      // The hidden goes after the layer's input when both fit in s_x, so the up rows
+      // read the input from LDS instead of memory: half the load requests of an up
+      // row (one token, OPT-6.7B shape: 22.6 -> 21.4 us per layer-step).
+      const size_t x_bytes = (size_t)B * rb1;
+      const bool x_keep = w2_lds && x_bytes + (size_t)TB * h * 4 <= (size_t)kXBytes;
+      const size_t hid_off = x_keep ? ((x_bytes + 255) & ~(size_t)255) : 0;
+      x_from_lds = x_keep;
+      float* s_hid = w2_lds ? reinterpret_cast<float*>(s_x + hid_off) : reinterpret_cast<float*>(s_w2);
       float* s_sc = s_red;                     // [rows2][NB]
       // Every wave first waits for its own W2 rows (waves 0..3 for their late share,
       // issued last), so the hidden is polled once the rows have landed, when the
@@ -775,7 +783,14 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
         for (int u = 0; u < kU; ++u) {
           const int c = min(lane + u * kWave, nch1 - 1);
           wa[u] = load_raw<16>(ra + (size_t)c * 16);
-          xq[u] = load_raw<16>(x + (size_t)c * 16);
+        }
+        if (x_from_lds) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            xq[u] = *reinterpret_cast<const Raw<16>*>(s_x + (size_t)min(lane + u * kWave, nch1 - 1) * 16);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) xq[u] = load_raw<16>(x + (size_t)min(lane + u * kWave, nch1 - 1) * 16);
         }
         wait_memory();                           // registers and the slot
         float za[1] = {0.f}, zl[1] = {0.f};
@@ -811,8 +826,20 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
           wa[u] = load_raw<16>(ra + (size_t)c * 16);
           if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+        }
+        if (x_from_lds) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
+          for (int u = 0; u < kUP; ++u)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              xq[u][b] = *reinterpret_cast<const Raw<16>*>(s_x + (size_t)min(b, B - 1) * rb1 +
+                                                           (size_t)min(lane + (u0 + u) * kWave, nch1 - 1) * 16);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kUP; ++u)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)min(lane + (u0 + u) * kWave, nch1 - 1) * 16);
         }
 #pragma unroll
         for (int u = 0; u < kUP; ++u) {
@@ -1089,6 +1116,9 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
           for (int i = 0; i < rem; ++i) um &= um - 1;
           return lo + P * (32 * m + __builtin_ctz(um));
         };
+        // the input is still in s_x unless the standard-layout outputs were built over
+        // it (before the down loop) or the owner-major list reaches into it
+        x_from_lds = x_from_lds && late_out && (size_t)B * rb1 <= (size_t)(kPrefBytes + kUwBytes);
         for (int r = q0 + wave; r < q1; r += kWork) up_row(ov_entry(r));
       }
 
