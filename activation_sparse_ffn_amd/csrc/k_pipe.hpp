@@ -322,7 +322,9 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       uint32_t u = 0;
       for (int b = 0; b < B; ++b) u |= s_words[st * NB + b];
       const int g = w + P * st;
-      st_tagged(p.uni + (size_t)w * p.us + st, tg, u);
+      // word-major (word m of owner o at m P + o): a poll of all owners' words is
+      // nw2 P / 16 cache lines, not one per owner (20.7 -> 20.4 us, OPT-6.7B shape)
+      st_tagged(p.uni + (size_t)st * P + w, tg, u);
       Lj->union_bits[g] = u;
     }
     for (int i = st; i < rows2 * B; i += kST) {
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
         unsigned long long uv[8];
         const int n = min(8, nw - m0);
         auto valid = [&](int i) { return i < n; };
-        auto addr = [&](int i) { return p.uni + (size_t)o * p.us + m0 + i; };
+        auto addr = [&](int i) { return p.uni + (size_t)(m0 + i) * P + o; };
         poll_tagged_if<8, decltype(valid), decltype(addr), kPS>(uv, valid, addr, tg, p.err);
 #pragma unroll
         for (int i = 0; i < 8; ++i)

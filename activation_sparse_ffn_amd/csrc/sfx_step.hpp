@@ -22,7 +22,7 @@ struct StepParams {
   uint32_t* err;               // nonzero after a wait timed out
   uint32_t* fbar;              // [P] x kFlagStride: layer done (grid barrier); holds layer tags
   unsigned long long* hid;     // [P][16]  {tag, hidden}: rows w + P s, s < nr1, all tokens
-  unsigned long long* uni;     // P us words {tag, union word}: fused step word-major (m P + o), pipeline [P][us]
+  unsigned long long* uni;     // P us words {tag, union word}: word-major: word m of workgroup o at m P + o
   unsigned long long* hact;    // [f][B]   {tag, activation} by active rank
   unsigned long long* ypart;   // [2][P][64 NB] {tag, share of y}: fused step's tile shares
 };
