@@ -85,6 +85,19 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
   int32_t* s_nid = reinterpret_cast<int32_t*>(s_x + kPrefBytes + kUwBytes);
   float* s_hid = reinterpret_cast<float*>(s_x + kXBytes - pipe_hid_bytes(TB, p.h));
   const int nid_cap = (kXBytes - kPrefBytes - kUwBytes - pipe_hid_bytes(TB, p.h)) / 4;
+  // ReGLU up rows read the input from LDS (s_xk, below the stream waves' hidden)
+  // when the layer's list leaves room for it: loaded by waves 0..3 right after the
+  // list is built, waited for before the grid barrier.  Measured, one token: ReGLU
+  // (two weight rows per input read) 24.2 -> 22.7 us per layer-step at the LLaMA2-7B
+  // shape; ReLU 20.4 -> 21.3 at the OPT-6.7B shape (the gather waves then reach
+  // the union poll earlier and their polls meet the stream waves' W2 traffic), so
+  // ReLU keeps reading the input from memory.
+  const long long xk_end = (long long)kXBytes - pipe_hid_bytes(TB, p.h);
+  const long long xk_off = (xk_end - (long long)p.B * p.d * 2) & ~255LL;
+  const int nid_cap_x = xk_off > kPrefBytes + kUwBytes ? (int)((xk_off - kPrefBytes - kUwBytes) / 4) : -1;
+  uint8_t* const s_xk = s_x + (xk_off > 0 ? xk_off : 0);
+  bool x_in_lds = false;
+  constexpr bool kXK = REGLU;
 
   if (threadIdx.x == 0) { s_gsync = 0u; s_ssync = 0u; s_nosplit = 0u; s_hdone = 0u; }
   lds_barrier();
@@ -418,8 +431,20 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
         const int c = min(lane + (u0 + u) * kWave, nch1 - 1);
         wa[u] = load_raw<16>(ra + (size_t)c * 16);
         if (REGLU) wl[u] = load_raw<16>(rl + (size_t)c * 16);
+      }
+      if (x_in_lds) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)c * 16);
+        for (int u = 0; u < kUP; ++u)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            xq[u][b] = *reinterpret_cast<const Raw<16>*>(s_xk + (size_t)min(b, B - 1) * rb1 +
+                                                         (size_t)min(lane + (u0 + u) * kWave, nch1 - 1) * 16);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUP; ++u)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            xq[u][b] = load_raw<16>(x + (size_t)min(b, B - 1) * rb1 + (size_t)min(lane + (u0 + u) * kWave, nch1 - 1) * 16);
       }
 #pragma unroll
       for (int u = 0; u < kUP; ++u) {
@@ -464,6 +489,12 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       if (p.L > 1) prefetch_w2(p, L0 + 1, s_w2);
     } else {
       k = union_scan(L0, tg0);
+      x_in_lds = kXK && k <= nid_cap_x;
+      if (x_in_lds && wave < kAW) {
+        load_x_lds(p, L0, s_xk);
+        wait_memory();
+      }
+      gather_sync();
       if (wave < kAW && p.L > 1) prefetch_w1<kU>(p, L0 + 1, w1r);
     }
   }
@@ -572,11 +603,14 @@ __global__ __launch_bounds__(kNT, 1) void k_pipe(StepParams p) {
       }
       if (has_next) {
         k = union_scan(Ld + 1, tag + 1u);    // its first sync also orders the s_dred reads
+        x_in_lds = kXK && k <= nid_cap_x;
+        if (x_in_lds && wave < kAW) load_x_lds(p, Ld + 1, s_xk);
         if (wave < kAW && l + 2 < p.L) prefetch_w1<kU>(p, Ld + 2, w1r);
       }
     }
     if (has_next) {
       // grid barrier: every workgroup raises its flag once its layer is done
+      if (x_in_lds && wave < kAW) wait_memory();
       lds_barrier();
       if (threadIdx.x == 0) store_through(p.fbar + (size_t)blockIdx.x * kFS, tag);
       if (wave == kCW) wait_flags(p.fbar, gridDim.x, tag, p.err, 1u);
