@@ -30,8 +30,9 @@
  *     of a weight matrix must span a multiple of 16 bytes.
  *   - Workspaces must be 256-byte aligned, at least as large as the matching
  *     *_ws() query, and zero-filled before their first use; each call leaves the
- *     control words it uses at zero again, except the sticky status words named
- *     below, which stay set until the caller clears them.  One workspace must not
+ *     control words it uses at zero again or, where a call says so, in a state the
+ *     next call continues from, except the sticky status words named below, which
+ *     stay set until the caller clears them.  One workspace must not
  *     be used by two calls that may run at the same time.
  *   - Batch B (tokens per step) is 1..SFX_MAX_B.
  *   - The data passed to one call must not change until that call's kernels end.
@@ -154,7 +155,9 @@ int sfx_predict_q4(void* stream, int B, int d, int h, int f, const void* x,
  *   count      device int32 scalar, written.  It stays on the device.
  *   ws         >= sfx_compact_ws(B, f) bytes (256 + 4 per 1024 neurons, rounded
  *              up to 256).  The workgroups hand their counts to each other through
- *              it with bounded waits: a count that does not arrive within the bound
+ *              it, tagged with a 16-bit call counter kept in word 0 (carried from
+ *              call to call, never cleared; zero-filling the whole workspace resets
+ *              it), with bounded waits: a count that does not arrive within the bound
  *              sets word 1 of the workspace nonzero instead of hanging, and the list
  *              of that call is then undefined.  Word 1 is sticky: the library never
  *              clears it; the caller reads it after synchronising (nonzero = some

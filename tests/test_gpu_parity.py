@@ -192,7 +192,7 @@ def test_compact_long_lists(f, B, t):
     cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
     ws = A.workspace(A.sfx_compact_ws(B, f))
     mtok, muni, midx, mcnt = O.gate(s.cpu().double().numpy(), t)
-    for rep in range(2):                       # the control words are clear again after a call
+    for rep in range(2):                       # the second call continues from the first's counter
         say(f"compact long f={f} B={B} t={t} rep {rep}")
         A.sfx_compact(s, t, uni, idx, cnt, ws, tok_bits=tok)
         torch.cuda.synchronize()
@@ -201,7 +201,12 @@ def test_compact_long_lists(f, B, t):
         k = int(cnt.item())
         assert k == mcnt and np.array_equal(idx[:k].cpu().numpy(), midx)
         assert torch.all(idx[k:] == -7)
-        assert int(torch.count_nonzero(ws)) == 0
+        # workspace after the call: error word clear, call counter advanced by one,
+        # every workgroup's count word tagged with this call's counter
+        wsw = ws.view(torch.int32).cpu().numpy().view(np.uint32)
+        assert wsw[1] == 0 and wsw[0] == rep + 1
+        nblk = (f + 1023) // 1024
+        assert np.all((wsw[64:64 + nblk] >> 16) == rep + 1)
 
 
 def test_out_of_range_indices_are_inert():
