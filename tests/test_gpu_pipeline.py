@@ -85,6 +85,15 @@ def test_pipeline_long_list_w2_from_memory(B):
     torch.cuda.empty_cache()
 
 
+def test_pipeline_reglu_list_too_long_for_input_in_lds():
+    """LLaMA2-7B shape at one token with about 30% of the neurons active: the list
+    (k ~ 3.3k) leaves no room for the input below the hidden in LDS, so the ReGLU
+    up rows read it from memory (at the default density they read it from LDS)."""
+    cfg = S.CONFIGS["C3"]
+    _run_and_check(cfg, 2, 1, 2, threshold=S.threshold_for_share(cfg, 0.3), min_k=1848)
+    torch.cuda.empty_cache()
+
+
 def test_pipeline_threshold_extremes():
     cfg = SMALL["C2s"]
     layers = [S.make_layer(cfg, l, device=DEV) for l in range(2)]
