@@ -333,8 +333,11 @@ __device__ __forceinline__ void prefetch_w2_rows(const StepParams& p, CLayer* Ld
     }
   }
 }
+// One eighth late since the hidden is polled after the W2 rows land (one token,
+// us per layer-step, eighths 2 -> 1: OPT-6.7B shape 21.0 -> 20.6, LLaMA2-7B shape
+// 22.95 -> 23.15; 0: 21.5 / 23.9; 4: 21.2 / 22.9).
 #ifndef SFX_W2_LATE
-#define SFX_W2_LATE 2
+#define SFX_W2_LATE 1
 #endif
 // Own W2 rows [w2_split, nr2) that waves 0..kAW-1 load once their W1 rows are done
 // (the last SFX_W2_LATE eighths); waves kAW.. load [0, w2_split) from the start of
