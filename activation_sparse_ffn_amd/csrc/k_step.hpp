@@ -1007,10 +1007,14 @@ __global__ __launch_bounds__(kNT, 1) void k_step(StepParams p) {
       auto load_wd = [&](int qb) {                 // kRD local positions at a time, qb < kl
         // positions past kl are clamped to kl - 1 (loaded, never used), so the
         // loads are issued back to back without branches
+        // rows this wave needs (wave-uniform: its lowest lane group's count); the rest
+        // are not loaded, their neuron set to 0 so every poll address stays valid
+        const int nu = min(kRD, (kl - __builtin_amdgcn_readfirstlane(qb) + d_rs - 1) / d_rs);
 #pragma unroll
-        for (int u = 0; u < kRD; ++u) nid[u] = pos_to_neuron(d_sub + dsplit * min(qb + u * d_rs, kl - 1));
+        for (int u = 0; u < kRD; ++u) nid[u] = u < nu ? pos_to_neuron(d_sub + dsplit * min(qb + u * d_rs, kl - 1)) : 0;
 #pragma unroll
-        for (int u = 0; u < kRD; ++u) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
+        for (int u = 0; u < kRD; ++u)
+          if (u < nu) wdv[u] = load_raw<16>(Wd + (size_t)nid[u] * rb1 + (size_t)d_col * 2);
       };
       // the workers' first batch goes out before anything else is waited for; the
       // outputs in the standard layout are built while it is in flight
