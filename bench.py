@@ -685,8 +685,8 @@ def main():
                 sys.exit(2)
             return "pipeline"
         # the fused step wherever it takes the shape (up to 4 tokens): measured faster
-        # than the separate calls at 1-4 tokens on both 7B shapes (at 3 tokens 41.9
-        # against 52.3 us per layer-step, OPT-6.7B); --separate forces the calls
+        # than the separate calls at 1-4 tokens on both 7B shapes (at 3 tokens 41.7
+        # against 52.4 us per layer-step, OPT-6.7B); --separate forces the calls
         fused = (not args.separate) and not cfg.pred_q4 and \
             StackStep.supported(cfg.d, cfg.f, cfg.h, B, cfg.wdtype, cfg.act)
         return "fused" if fused else "separate"

@@ -421,8 +421,8 @@ int sfx_gather_rows(void* stream, int n_dst, int n_src, size_t row_bytes, const 
  * Returns SFX_E_UNSUPPORTED for shapes the fused kernel is not built for; the
  * separate calls cover those.  Measured on MI355X against the separate calls (which
  * run on the matrix cores from 3 tokens): faster at 1 to 4 tokens on the OPT-6.7B and
- * LLaMA2-7B shapes (3 tokens, OPT-6.7B: 41.9 against 52.3 us per layer-step; 4
- * tokens, LLaMA2-7B: 49.2 against 55.4).
+ * LLaMA2-7B shapes (3 tokens, OPT-6.7B: 41.7 against 52.4 us per layer-step; 4
+ * tokens, LLaMA2-7B: 49.6 against 55.5).
  * ------------------------------------------------------------------------------- */
 typedef struct sfx_layer {
   const void* x;            /* [B][d] */
