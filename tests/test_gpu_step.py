@@ -156,6 +156,17 @@ def test_fused_outputs_inside_down_loop():
     torch.cuda.empty_cache()
 
 
+def test_fused_reglu_input_in_lds_outputs_inside_down_loop():
+    """ReGLU at one token with W2 rows in LDS (h = 256) and every neuron active
+    (f = 32768: 8192 list positions per workgroup, more than the 6144 pairs the LDS
+    save area holds next to the ReGLU up-row slots): the up rows of the own
+    neurons read the input from LDS, the overflow rows read it from memory (the
+    standard-layout outputs were built over it before the down loop)."""
+    cfg = S.scaled(S.CONFIGS["C3"], name="C3w", d=4096, f=32768, h=256)
+    _run_and_check(cfg, 2, 1, 1, threshold=float("-inf"), min_k=NID_CAP)
+    torch.cuda.empty_cache()
+
+
 def test_fused_long_list_w2_in_lds():
     """OPT-6.7B shape (W2 rows in LDS) with every neuron active: 16384 > 4920."""
     cfg = S.CONFIGS["C2"]
