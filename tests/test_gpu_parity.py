@@ -91,8 +91,8 @@ def test_scaled_configs(name, B):
             say("   ", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in r.items()})
 
 
-@pytest.mark.parametrize("name,B", [("C2", 1), ("C3", 1), ("C3", 4), ("C3", 8), ("C4", 1), ("C5", 1), ("C5", 8),
-                                    ("C5", 32)])
+@pytest.mark.parametrize("name,B", [("C2", 1), ("C2", 2), ("C3", 1), ("C3", 4), ("C3", 8), ("C4", 1), ("C4", 2),
+                                    ("C5", 1), ("C5", 8), ("C5", 32)])
 def test_full_size_layer(name, B):
     """One layer at the workload's full shape, in the launch configuration the
     benchmark times, two decode steps, every output compared."""
